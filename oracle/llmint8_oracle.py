@@ -1,0 +1,214 @@
+"""CPU oracle for the LLM.int8() mixed-precision decomposition linear layer.
+
+TEST INFRASTRUCTURE. Only the test-suite, the package's smoke check and the
+benchmark's CPU-baseline leg import this module. The product path never does:
+it shares no code, table or helper with this file, and this file imports
+nothing from the product.
+
+What it computes, stage by stage, in the order the method takes them. Sources
+are cited by page title and section:
+
+* [HFQ-2]  "Hugging Face Quantization with bitsandbytes: 4-bit & 8-bit Models
+           Explained", section 2 "LLM.int8(): Quantizing Without Degrading
+           Large Models": outliers are whole feature dimensions of large
+           magnitude; they are computed in 16-bit while the rest is multiplied
+           in int8 and converted back to 16-bit at the end.
+* [HFQ-3]  same page, section 3 "Configuring 8-Bit Loading": the outlier
+           cutoff ``llm_int8_threshold``, default 6.0, applies to hidden-state
+           (activation) values.
+* [HYS]    "bitsandbytes: GPU-Accelerated Inference and Training at Lower Bit
+           Depths", section "How LLM.int8() quantizes weights and activations":
+           vector-wise quantization; values that fit 8-bit are quantized,
+           outliers go through a separate 16-bit matrix multiplication.
+* [HEAT]   "Shrink LLMs to 4-bit and train them anyway", section "The
+           interesting bit": vector-wise quantization for the bulk, outliers
+           through 16-bit matmul.
+* [DCT]    "bitsandbytes" (mining glossary), sections "What it provides" (the
+           large *activation* values are kept in higher precision) and the
+           introduction (weights are quantized when the model loads).
+
+Readings where the pages leave a step open (each one is also listed, with its
+reason, in the design notes):
+
+* R1  an outlier is a whole *column* (feature dimension) of X, decided over all
+      T rows of the call; the weight has no threshold.
+* R2  a column is an outlier when some |x| *reaches* the threshold (``>=``).
+* R3  the row statistic of X is the absolute maximum over the non-outlier
+      columns only.
+* R4  absmax ("vector-wise") scaling: ``s = fl32(127 / absmax)`` computed once
+      per row, ``q = rne(fl32(v * s))``; symmetric, so -128 never occurs.
+* R5  a row whose absmax is 0 quantizes to all zeros and keeps scale 0.
+* R6  the weight is quantized once per output row over all K.
+* R7  the 16-bit weight operand of the outlier product is the stored int8
+      weight dequantized: ``fp16(fl32(fl32(q * b) / 127))``.
+* R8  the outlier product has fp16 operands; the output is rounded once to fp16.
+* R9  the threshold is compared in fp32; ``+inf`` gives an empty outlier set.
+
+Precision: every quantization step is the fp32 operation named (NumPy float32
+arithmetic is IEEE round-to-nearest-even); ``np.rint`` is round-half-to-even.
+The integer product is a float64 matrix product of the int8 values, which is
+exact because every partial sum is an integer of magnitude below 2**31 < 2**53.
+The output is formed in float64 and rounded once to fp16.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+__all__ = [
+    "quantize_weight", "outlier_columns", "pack_bitmap", "quantize_activations",
+    "int8_matmul", "outlier_operands", "output", "linear", "Stages", "parity_error",
+]
+
+_F32_127 = np.float32(127.0)
+
+
+def _absmax_rows(v32: np.ndarray) -> np.ndarray:
+    if v32.shape[1] == 0:
+        return np.zeros(v32.shape[0], np.float32)
+    return np.abs(v32).max(axis=1).astype(np.float32)
+
+
+def _quantize_rows(v32: np.ndarray, absmax: np.ndarray) -> np.ndarray:
+    """R4/R5: q = rne(fl32(v * fl32(127/absmax))) per row, 0 where absmax == 0."""
+    pos = absmax > 0
+    s = np.zeros_like(absmax)
+    s[pos] = _F32_127 / absmax[pos]                 # fp32 correctly-rounded division
+    prod = v32 * s[:, None]                         # fp32 multiply
+    q = np.rint(prod)                               # round half to even
+    q = np.clip(q, -127, 127)                       # no-op for |v| <= absmax
+    q[~pos, :] = 0
+    return q.astype(np.int8)
+
+
+def quantize_weight(W16: np.ndarray):
+    """Vector-wise weight quantization at load time ([HYS]; [DCT] introduction; R4-R6).
+
+    ``W16`` fp16 [N, K] -> (``Wq`` int8 [N, K], ``sW`` fp32 [N]) with
+    ``sW[n] = max_k |W[n, k]|`` (exact: an fp16 value) and
+    ``Wq[n, k] = rne(fl32(W[n, k] * fl32(127 / sW[n])))``.
+    """
+    W = np.asarray(W16)
+    assert W.dtype == np.float16 and W.ndim == 2
+    W32 = W.astype(np.float32)
+    b = _absmax_rows(W32)
+    return _quantize_rows(W32, b), b
+
+
+def outlier_columns(X16: np.ndarray, threshold: float) -> np.ndarray:
+    """Outlier feature dimensions ([HFQ-2]; [HFQ-3]; R1, R2, R9).
+
+    Returns a bool mask [K]: column h is an outlier when some row has
+    ``|X[t, h]| >= threshold`` (fp32 comparison).
+    """
+    X = np.asarray(X16)
+    assert X.dtype == np.float16 and X.ndim == 2
+    thr = np.float32(threshold)
+    return np.any(np.abs(X.astype(np.float32)) >= thr, axis=0)
+
+
+def pack_bitmap(mask: np.ndarray) -> np.ndarray:
+    """Bitmap form of the outlier set: bit (h % 32) of uint32 word h // 32 is column h."""
+    K = mask.shape[0]
+    words = np.zeros((K + 31) // 32, np.uint32)
+    for h in np.flatnonzero(mask):
+        words[h // 32] |= np.uint32(1) << np.uint32(h % 32)
+    return words
+
+
+def quantize_activations(X16: np.ndarray, outlier_mask: np.ndarray):
+    """Row-wise (vector-wise) quantization of the non-outlier part of X ([HYS]; R3-R5).
+
+    ``a[t] = max over non-outlier columns of |X[t, k]|``;
+    ``Xq[t, k] = 0`` on outlier columns, else ``rne(fl32(X[t, k] * fl32(127 / a[t])))``.
+    """
+    X32 = np.asarray(X16).astype(np.float32)
+    kept = np.where(outlier_mask[None, :], np.float32(0), X32)
+    a = _absmax_rows(kept)
+    return _quantize_rows(kept, a), a
+
+
+def int8_matmul(Xq: np.ndarray, Wq: np.ndarray) -> np.ndarray:
+    """The int8 product with integer accumulation ([HFQ-2]: "multiplied in int8").
+
+    ``C = Xq @ Wq.T`` exactly, returned as int32.
+    """
+    C = Xq.astype(np.float64) @ Wq.astype(np.float64).T
+    Ci = C.astype(np.int64)
+    assert np.all(Ci == C), "float64 product of int8 values must be exact"
+    assert Ci.size == 0 or np.abs(Ci).max() < 2 ** 31
+    return Ci.astype(np.int32)
+
+
+def outlier_operands(X16: np.ndarray, Wq: np.ndarray, sW: np.ndarray, idx: np.ndarray):
+    """16-bit operands of the outlier product ([HYS]; [HFQ-2]; R7, R8).
+
+    ``Xo = X[:, idx]`` (fp16, exact copy);
+    ``Wd[n, j] = fp16(fl32(fl32(Wq[n, idx[j]] * sW[n]) / 127))``.
+    """
+    Xo = np.asarray(X16)[:, idx]
+    q32 = Wq[:, idx].astype(np.float32)
+    Wd = ((q32 * sW[:, None].astype(np.float32)) / _F32_127).astype(np.float16)
+    return Xo, Wd
+
+
+def output(C: np.ndarray, aX: np.ndarray, sW: np.ndarray, Xo: np.ndarray, Wd: np.ndarray):
+    """Recombination, converted back to 16-bit at the end ([HFQ-2]).
+
+    ``Y = fp16( C * a[t] * b[n] / 127**2  +  Xo @ Wd.T )`` evaluated in float64.
+    """
+    Y64 = C.astype(np.float64) * aX.astype(np.float64)[:, None] \
+        * sW.astype(np.float64)[None, :] / 16129.0
+    if Xo.shape[1]:
+        Y64 = Y64 + Xo.astype(np.float64) @ Wd.astype(np.float64).T
+    with np.errstate(over="ignore"):               # beyond fp16 range: +-inf, like any fp16 cast
+        return Y64.astype(np.float16)
+
+
+@dataclasses.dataclass
+class Stages:
+    outlier_mask: np.ndarray   # bool [K]
+    bitmap: np.ndarray         # uint32 [ceil(K/32)]
+    idx: np.ndarray            # int32 [|O|], ascending
+    Xq: np.ndarray             # int8 [T, K]
+    aX: np.ndarray             # fp32 [T]
+    C: np.ndarray | None       # int32 [T, N] (None when rows were restricted)
+    Xo: np.ndarray             # fp16 [T, |O|]
+    Wd: np.ndarray             # fp16 [N, |O|]
+    Y: np.ndarray | None       # fp16 [T, N]
+
+    @property
+    def count(self) -> int:
+        return int(self.idx.shape[0])
+
+
+def linear(X16: np.ndarray, Wq: np.ndarray, sW: np.ndarray, threshold: float,
+           rows: np.ndarray | None = None, with_outputs: bool = True) -> Stages:
+    """The whole forward: outlier set, quantized activations, int8 product, output.
+
+    ``rows`` restricts C and Y to a subset of rows (the outlier set and row
+    statistics are still taken over all of X, as the method defines them).
+    """
+    mask = outlier_columns(X16, threshold)
+    idx = np.flatnonzero(mask).astype(np.int32)
+    Xq, aX = quantize_activations(X16, mask)
+    Xo, Wd = outlier_operands(X16, Wq, sW, idx)
+    C = Y = None
+    if with_outputs:
+        sel = slice(None) if rows is None else rows
+        C = int8_matmul(Xq[sel], Wq)
+        Y = output(C, aX[sel], sW, Xo[sel], Wd)
+    return Stages(mask, pack_bitmap(mask), idx, Xq, aX, C, Xo, Wd, Y)
+
+
+def parity_error(Y_test: np.ndarray, Y_ref: np.ndarray) -> float:
+    """Max-abs error normalised by the reference's max-abs value (floor 2**-14)."""
+    a = Y_test.astype(np.float64)
+    r = Y_ref.astype(np.float64)
+    if r.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(a[np.isfinite(r)])):
+        return float("inf")
+    den = max(float(np.abs(r).max()), 2.0 ** -14)
+    return float(np.abs(a - r).max() / den)

@@ -1,0 +1,118 @@
+"""Independent brute-force twin of the LLM.int8() forward, for tiny inputs.
+
+Pure Python: loops, Python ``int`` for the integer product, ``fractions.Fraction``
+for the exact output value, ``struct`` for IEEE rounding to fp32 / fp16. It uses
+no NumPy and nothing from the oracle, so agreement between the two pins the
+oracle's vectorised arithmetic (indices, operand order, scales, rounding).
+
+Rounding facts it relies on:
+* ``struct.pack('f', x)`` rounds a binary64 value to the nearest fp32 (ties to
+  even); ``struct.pack('e', x)`` does the same to fp16.
+* An fp16 value times an fp32 value, or a 7-bit integer times an fp32 value, is
+  exact in binary64 (at most 35 and 31 significant bits), so one rounding to
+  fp32 afterwards is the IEEE fp32 product.
+* A binary64 quotient of two fp32 values, rounded again to fp32, is the
+  correctly-rounded fp32 quotient (53 >= 2*24 + 2).
+* Python's ``round()`` on a float rounds half to even.
+"""
+from __future__ import annotations
+
+import math
+import struct
+from fractions import Fraction
+
+
+def f32(x: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def f16(x: float) -> float:
+    return struct.unpack("<e", struct.pack("<e", x))[0]
+
+
+def f16_of_fraction(q: Fraction) -> float:
+    """Correct round-half-even of an exact rational to fp16 (finite range only)."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    # fix possible off-by-one of the float log
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -14)                      # subnormal range shares the 2**-24 quantum
+    quantum = Fraction(2) ** (e - 10)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = fl * quantum
+    if val > 65504:
+        return sign * math.inf
+    return sign * float(val)
+
+
+def rne(x: float) -> int:
+    return int(round(x))
+
+
+def quantize_vector(vals):
+    """absmax row quantization; returns (q list, absmax)."""
+    m = 0.0
+    for v in vals:
+        m = max(m, abs(v))
+    if m == 0.0:
+        return [0] * len(vals), 0.0
+    s = f32(127.0 / m)
+    q = []
+    for v in vals:
+        r = rne(f32(v * s))
+        q.append(max(-127, min(127, r)))
+    return q, m
+
+
+def forward(X, W, thr):
+    """X: T x K list of fp16-valued floats; W: N x K; thr: float.
+
+    Returns dict with outlier list, Wq, sW, Xq, aX, C, Y (Y as floats).
+    """
+    T = len(X)
+    N = len(W)
+    K = len(W[0]) if N else (len(X[0]) if T else 0)
+    thr32 = f32(thr) if math.isfinite(thr) else thr
+    outl = []
+    for h in range(K):
+        hit = False
+        for t in range(T):
+            if abs(X[t][h]) >= thr32:
+                hit = True
+        if hit:
+            outl.append(h)
+    oset = set(outl)
+    Wq, sW = [], []
+    for n in range(N):
+        q, b = quantize_vector(W[n])
+        Wq.append(q)
+        sW.append(b)
+    Xq, aX = [], []
+    for t in range(T):
+        kept = [0.0 if h in oset else X[t][h] for h in range(K)]
+        q, a = quantize_vector(kept)
+        Xq.append(q)
+        aX.append(a)
+    C = [[sum(Xq[t][k] * Wq[n][k] for k in range(K)) for n in range(N)] for t in range(T)]
+    Wd = [[f16(f32(f32(Wq[n][h] * sW[n]) / 127.0)) for h in outl] for n in range(N)]
+    Y = []
+    for t in range(T):
+        row = []
+        for n in range(N):
+            exact = Fraction(C[t][n]) * Fraction(aX[t]) * Fraction(sW[n]) / 16129
+            for j, h in enumerate(outl):
+                exact += Fraction(X[t][h]) * Fraction(Wd[n][j])
+            row.append((exact, f16_of_fraction(exact)))
+        Y.append(row)
+    return {"outliers": outl, "Wq": Wq, "sW": sW, "Xq": Xq, "aX": aX, "C": C, "Wd": Wd,
+            "Y": [[y for _, y in r] for r in Y], "Y_exact": [[e for e, _ in r] for r in Y]}

@@ -1,0 +1,155 @@
+/*
+ * llmint8.h - C ABI of an MI355X (gfx950) library for the LLM.int8()
+ * mixed-precision decomposition linear layer (the forward of an int8 linear
+ * layer that replaces a 16-bit one).
+ *
+ * The method, as the sources describe it:
+ *  - "Hugging Face Quantization with bitsandbytes: 4-bit & 8-bit Models
+ *    Explained", section 2 "LLM.int8(): Quantizing Without Degrading Large
+ *    Models": a few feature dimensions carry outliers of large magnitude; those
+ *    are computed in 16-bit, the rest is multiplied in int8 and converted back
+ *    to 16-bit at the end. Section 3: the outlier cutoff (default 6.0) applies
+ *    to hidden-state values.
+ *  - "bitsandbytes: GPU-Accelerated Inference and Training at Lower Bit
+ *    Depths", section "How LLM.int8() quantizes weights and activations":
+ *    vector-wise quantization; outliers go through a separate 16-bit product.
+ *  - "bitsandbytes" (glossary), introduction: weights are quantized when the
+ *    model loads, from the full-precision checkpoint.
+ *
+ * What the library computes (T rows, K input features, N output features):
+ *   O      = { h : some |X[t,h]| >= threshold }            (fp32 compare)
+ *   a[t]   = max_{k not in O} |X[t,k]|
+ *   Xq     = rne(fl32(X * fl32(127/a[t]))), 0 on columns in O or when a[t]=0
+ *   b[n]   = max_k |W[n,k]|,  Wq = rne(fl32(W * fl32(127/b[n])))
+ *   C      = Xq . Wq^T                                      (int32, exact)
+ *   Wd[n,j]= fp16(fl32(fl32(Wq[n,O_j] * b[n]) / 127))
+ *   Y      = fp16( C * a[t] * b[n] / 127^2  +  X[:,O] . Wd^T )  (fp32 sums)
+ * rne is round-half-to-even; fl32 an IEEE fp32 operation.
+ *
+ * Conventions for every entry point:
+ *  - Matrices are dense and row-major (row stride = row length). Device
+ *    pointers must be 16-byte aligned (sW, aX: 4-byte). fp16 data is IEEE
+ *    binary16 passed as void*.
+ *  - The caller owns every buffer. The library never allocates, frees or keeps
+ *    a pointer past the call.
+ *  - stream is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; outputs are valid once the stream has reached the call.
+ *    No call synchronises the host or copies device data to the host.
+ *  - Arguments are validated on the host before anything is enqueued. An
+ *    error return means nothing was enqueued, except LLMINT8_ERR_HIP, which
+ *    reports a failed launch (llmint8_last_hip_error() gives the HIP code).
+ *  - Inputs must be finite. Non-finite inputs give unspecified results.
+ *  - Calls that share a workspace must not run concurrently.
+ */
+#ifndef LLMINT8_H
+#define LLMINT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define LLMINT8_API __attribute__((visibility("default")))
+#else
+#define LLMINT8_API
+#endif
+
+typedef int llmint8_status;
+
+#define LLMINT8_OK               0
+#define LLMINT8_ERR_INVALID_ARG -1 /* null pointer, size <= 0 (T < 0), bad threshold, misaligned */
+#define LLMINT8_ERR_UNSUPPORTED -2 /* K % 16 != 0, K > 65536, N*K or T*K >= 2^31 */
+#define LLMINT8_ERR_WORKSPACE   -3 /* workspace smaller than llmint8_workspace_bytes(T,K,N) */
+#define LLMINT8_ERR_HIP         -4 /* a HIP launch or runtime call failed */
+
+/* Kernel route for llmint8_linear_debug / llmint8_linear_timed. */
+#define LLMINT8_PATH_AUTO 0 /* what llmint8_linear uses */
+#define LLMINT8_PATH_GEMM 1 /* scan + quantize + int8 MFMA GEMM (3 kernels), any T */
+#define LLMINT8_PATH_GEMV 2 /* one fused weight-streaming kernel, small T only */
+
+/*
+ * Vector-wise int8 quantization of a weight, done once when a layer is loaded
+ * ("bitsandbytes" glossary, introduction; "bitsandbytes: GPU-Accelerated
+ * Inference ...", "How LLM.int8() quantizes weights and activations").
+ *   W   [in]  fp16 [N, K], device
+ *   Wq  [out] int8 [N, K], device: rne(fl32(W[n,k] * fl32(127 / sW[n])))
+ *   sW  [out] fp32 [N], device: row absmax max_k |W[n,k]| (0 for a zero row,
+ *             whose codes are then all 0)
+ * Requires N >= 1, 1 <= K, K % 16 == 0, N*K < 2^31.
+ */
+LLMINT8_API llmint8_status llmint8_quantize_weight(const void* W, int64_t N, int64_t K, int8_t* Wq,
+                                       float* sW, void* stream);
+
+/*
+ * Bytes of device workspace llmint8_linear needs for a call with these sizes.
+ * The size covers the worst case of every column being an outlier; it does
+ * not depend on the data. Returns 0 for invalid sizes.
+ */
+LLMINT8_API size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N);
+
+/*
+ * The forward of the LLM.int8() linear layer ("Hugging Face Quantization with
+ * bitsandbytes ...", sections 2 and 3):
+ *   X         [in]  fp16 [T, K], device (activations / hidden states)
+ *   Wq, sW    [in]  from llmint8_quantize_weight (int8 [N, K], fp32 [N])
+ *   threshold [in]  outlier cutoff on |x| (>= counts), > 0; +inf disables the
+ *                   16-bit part; NaN or <= 0 is LLMINT8_ERR_INVALID_ARG
+ *   Y         [out] fp16 [T, N], device
+ *   workspace [tmp] device, >= llmint8_workspace_bytes(T, K, N) bytes,
+ *                   256-byte aligned; contents on entry do not matter
+ * T == 0 is a valid no-op. The outlier set is decided over all T rows of the
+ * call. Every stage runs on the GPU; the host never waits.
+ */
+LLMINT8_API llmint8_status llmint8_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                              const float* sW, int64_t N, float threshold, void* Y,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * llmint8_linear with a chosen kernel route and copies of the intermediate
+ * results, taken from the same kernels llmint8_linear runs. Every output
+ * pointer below may be NULL (not written).
+ *   path            LLMINT8_PATH_AUTO / _GEMM / _GEMV (GEMV needs
+ *                   T <= llmint8_gemv_max_rows(K); else LLMINT8_ERR_UNSUPPORTED)
+ *   outlier_bitmap  uint32 [ceil(K/32)]: bit h%32 of word h/32 set iff h in O
+ *   outlier_idx     int32 [K]: ascending outlier columns in the first |O| slots
+ *   outlier_count   int32 [1]: |O|
+ *   Xq              int8 [T, K]
+ *   aX              fp32 [T]: the row statistic a[t]
+ *   C               int32 [T, N]: the int8 product before dequantization
+ */
+LLMINT8_API llmint8_status llmint8_linear_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                                    const float* sW, int64_t N, float threshold, void* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int path, uint32_t* outlier_bitmap, int32_t* outlier_idx,
+                                    int32_t* outlier_count, int8_t* Xq, float* aX, int32_t* C);
+
+/*
+ * llmint8_linear that also records caller-created HIP events (hipEvent_t
+ * handles, passed as void*) on the stream around each kernel it launches:
+ * events[0] before the first kernel, events[i+1] after kernel i. Needs
+ * n_events >= kernels + 1 (at most 4); *kernels_launched (host int, may be
+ * NULL) receives the kernel count. Used to time each kernel of a call.
+ */
+LLMINT8_API llmint8_status llmint8_linear_timed(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                                    const float* sW, int64_t N, float threshold, void* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int path, void* const* events, int n_events,
+                                    int* kernels_launched);
+
+/* Largest T the fused GEMV route accepts for this K (0 if none). */
+LLMINT8_API int llmint8_gemv_max_rows(int64_t K);
+
+/* Static description of a status code. */
+LLMINT8_API const char* llmint8_status_string(llmint8_status status);
+
+/* HIP error code (hipError_t value) behind the last LLMINT8_ERR_HIP on this thread. */
+LLMINT8_API int llmint8_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLMINT8_H */

@@ -1,0 +1,254 @@
+"""Python binding of libllmint8 (LLM.int8() linear layer on MI355X / gfx950).
+
+Argument marshalling only: every step of the forward runs in the library's HIP
+kernels. Function names are those of the C ABI (include/llmint8.h). PyTorch
+provides device memory and the current stream; nothing here computes on the
+data, and there is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "LLMINT8_PATH_AUTO", "LLMINT8_PATH_GEMM", "LLMINT8_PATH_GEMV", "Llmint8Error",
+    "library_path", "load_library", "llmint8_quantize_weight", "llmint8_workspace_bytes",
+    "llmint8_linear", "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
+    "llmint8_status_string", "Int8Linear", "EXPORTED_SYMBOLS",
+]
+
+LLMINT8_PATH_AUTO = 0
+LLMINT8_PATH_GEMM = 1
+LLMINT8_PATH_GEMV = 2
+
+EXPORTED_SYMBOLS = (
+    "llmint8_quantize_weight", "llmint8_workspace_bytes", "llmint8_linear",
+    "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
+    "llmint8_status_string", "llmint8_last_hip_error",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class Llmint8Error(RuntimeError):
+    def __init__(self, status: int, where: str, hip: int = 0):
+        self.status = status
+        msg = f"{where}: {_status_text(status)} (status {status}"
+        if hip:
+            msg += f", hipError {hip}"
+        super().__init__(msg + ")")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libllmint8.so")
+
+
+def load_library():
+    """Load the built library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with mixed_precision_int8_amd/build.py "
+                           "(or __graft_entry__.build()) before use")
+    lib = ctypes.CDLL(path)
+    lib.llmint8_quantize_weight.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+    lib.llmint8_quantize_weight.restype = ctypes.c_int
+    lib.llmint8_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    lib.llmint8_workspace_bytes.restype = ctypes.c_size_t
+    lin = [_vp, _i64, _i64, _vp, _vp, _i64, ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.llmint8_linear.argtypes = lin
+    lib.llmint8_linear.restype = ctypes.c_int
+    lib.llmint8_linear_debug.argtypes = lin + [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.llmint8_linear_debug.restype = ctypes.c_int
+    lib.llmint8_linear_timed.argtypes = lin + [ctypes.c_int, ctypes.POINTER(_vp), ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int)]
+    lib.llmint8_linear_timed.restype = ctypes.c_int
+    lib.llmint8_gemv_max_rows.argtypes = [_i64]
+    lib.llmint8_gemv_max_rows.restype = ctypes.c_int
+    lib.llmint8_status_string.argtypes = [ctypes.c_int]
+    lib.llmint8_status_string.restype = ctypes.c_char_p
+    lib.llmint8_last_hip_error.argtypes = []
+    lib.llmint8_last_hip_error.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().llmint8_status_string(status).decode()
+    except Exception:  # noqa: BLE001 - message only
+        return "error"
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        hip = load_library().llmint8_last_hip_error() if status == -4 else 0
+        raise Llmint8Error(status, where, hip)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous CUDA {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def llmint8_workspace_bytes(T: int, K: int, N: int) -> int:
+    return int(load_library().llmint8_workspace_bytes(T, K, N))
+
+
+def llmint8_gemv_max_rows(K: int) -> int:
+    return int(load_library().llmint8_gemv_max_rows(K))
+
+
+def llmint8_status_string(status: int) -> str:
+    return _status_text(status)
+
+
+def llmint8_quantize_weight(W, Wq=None, sW=None, stream=None):
+    """W fp16 [N, K] (CUDA) -> (Wq int8 [N, K], sW fp32 [N])."""
+    import torch
+    lib = load_library()
+    N, K = W.shape
+    _need(W, torch.float16, (N, K), "W")
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if sW is None:
+        sW = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(sW, torch.float32, (N,), "sW")
+    _check(lib.llmint8_quantize_weight(_ptr(W), N, K, _ptr(Wq), _ptr(sW), _stream(stream, W.device)),
+           "llmint8_quantize_weight")
+    return Wq, sW
+
+
+def _workspace(T, K, N, device, workspace):
+    import torch
+    need = llmint8_workspace_bytes(T, K, N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _linear_args(X, Wq, sW, threshold, Y, workspace):
+    import torch
+    T, K = X.shape
+    N = Wq.shape[0]
+    _need(X, torch.float16, (T, K), "X")
+    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(sW, torch.float32, (N,), "sW")
+    if Y is None:
+        Y = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    _need(Y, torch.float16, (T, N), "Y")
+    workspace = _workspace(T, K, N, X.device, workspace)
+    thr = float(threshold)
+    if thr == math.inf:
+        thr = math.inf
+    return T, K, N, Y, workspace, thr
+
+
+def llmint8_linear(X, Wq, sW, threshold: float = 6.0, Y=None, workspace=None, stream=None):
+    """Y fp16 [T, N] = LLM.int8() forward of X fp16 [T, K] with (Wq, sW)."""
+    lib = load_library()
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
+    _check(lib.llmint8_linear(_ptr(X), T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(Y), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream, X.device)),
+           "llmint8_linear")
+    return Y
+
+
+def llmint8_linear_debug(X, Wq, sW, threshold: float = 6.0, path: int = LLMINT8_PATH_AUTO,
+                         Y=None, workspace=None, stream=None, want_C: bool = True):
+    """Forward plus the intermediates of the same kernels: dict of tensors."""
+    import torch
+    lib = load_library()
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
+    dev = X.device
+    KW = (K + 31) // 32
+    out = {
+        "bitmap": torch.zeros((KW,), dtype=torch.int32, device=dev),
+        "idx": torch.full((K,), -1, dtype=torch.int32, device=dev),
+        "count": torch.full((1,), -1, dtype=torch.int32, device=dev),
+        "Xq": torch.zeros((T, K), dtype=torch.int8, device=dev),
+        "aX": torch.zeros((T,), dtype=torch.float32, device=dev),
+        "C": torch.zeros((T, N), dtype=torch.int32, device=dev) if want_C else None,
+    }
+    _check(lib.llmint8_linear_debug(_ptr(X), T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(Y), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream, dev), int(path),
+                                    _ptr(out["bitmap"]), _ptr(out["idx"]), _ptr(out["count"]),
+                                    _ptr(out["Xq"]), _ptr(out["aX"]), _ptr(out["C"])),
+           "llmint8_linear_debug")
+    out["Y"] = Y
+    return out
+
+
+def llmint8_linear_timed(X, Wq, sW, threshold, Y, workspace, events, path=LLMINT8_PATH_AUTO,
+                         stream=None):
+    """Forward that records ``events`` (torch.cuda.Event, created) around each kernel.
+
+    Returns the number of kernels launched.
+    """
+    lib = load_library()
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
+    handles = (_vp * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    nk = ctypes.c_int(0)
+    _check(lib.llmint8_linear_timed(_ptr(X), T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(Y), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream, X.device),
+                                    int(path), handles, len(events), ctypes.byref(nk)),
+           "llmint8_linear_timed")
+    return nk.value
+
+
+class Int8Linear:
+    """Drop-in int8 replacement of a bias-free fp16 linear layer.
+
+    The weight is quantized once at construction ("bitsandbytes" glossary,
+    introduction: quantization happens when the model loads); ``forward`` runs
+    the LLM.int8() forward ("Hugging Face Quantization with bitsandbytes",
+    sections 2 and 3).
+    """
+
+    def __init__(self, weight, threshold: float = 6.0):
+        self.threshold = float(threshold)
+        self.out_features, self.in_features = weight.shape
+        self.Wq, self.sW = llmint8_quantize_weight(weight.contiguous())
+        self._ws = None
+
+    def memory_bytes(self) -> int:
+        return self.Wq.numel() + self.sW.numel() * 4
+
+    def _workspace(self, T, device):
+        import torch
+        need = max(llmint8_workspace_bytes(T, self.in_features, self.out_features), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty((need,), dtype=torch.uint8, device=device)
+        return self._ws
+
+    def forward(self, X):
+        shape = X.shape
+        X2 = X.reshape(-1, self.in_features).contiguous()
+        Y = llmint8_linear(X2, self.Wq, self.sW, self.threshold,
+                           workspace=self._workspace(X2.shape[0], X2.device))
+        return Y.reshape(*shape[:-1], self.out_features)
+
+    __call__ = forward

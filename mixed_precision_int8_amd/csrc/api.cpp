@@ -1,0 +1,230 @@
+// Host side of the C ABI declared in include/llmint8.h: argument validation,
+// workspace carving, kernel-route choice and launches on the caller's stream.
+// Nothing here allocates device memory, synchronises the host or copies device
+// data to the host; validation runs before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/llmint8.h"
+#include "internal.h"
+
+using namespace llmint8;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+llmint8_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return LLMINT8_OK;
+  g_last_hip_error = (int)e;
+  return LLMINT8_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr double kTwo31 = 2147483648.0;
+
+llmint8_status check_sizes(int64_t T, int64_t K, int64_t N) {
+  if (T < 0 || K <= 0 || N <= 0) return LLMINT8_ERR_INVALID_ARG;
+  if (K % 16 != 0 || K > kMaxK) return LLMINT8_ERR_UNSUPPORTED;
+  if ((double)N * (double)K >= kTwo31 || (double)T * (double)K >= kTwo31) return LLMINT8_ERR_UNSUPPORTED;
+  if ((double)T * (double)N >= 16.0 * kTwo31) return LLMINT8_ERR_UNSUPPORTED;
+  return LLMINT8_OK;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+llmint8_status validate_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                               const float* sW, int64_t N, float threshold, void* Y,
+                               void* workspace, size_t workspace_bytes) {
+  llmint8_status st = check_sizes(T, K, N);
+  if (st != LLMINT8_OK) return st;
+  if (std::isnan(threshold) || !(threshold > 0.0f)) return LLMINT8_ERR_INVALID_ARG;
+  if (!Wq || !sW) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
+  if (T == 0) return LLMINT8_OK;
+  if (!X || !Y || !workspace) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(workspace, kWsAlign)) return LLMINT8_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_layout(T, K, N).total) return LLMINT8_ERR_WORKSPACE;
+  return LLMINT8_OK;
+}
+
+LinearArgs make_args(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sW,
+                     int64_t N, float threshold, void* Y, void* workspace) {
+  const WsLayout L = ws_layout(T, K, N);
+  char* ws = static_cast<char*>(workspace);
+  LinearArgs a{};
+  a.X = static_cast<const uint16_t*>(X);
+  a.Wq = Wq;
+  a.sW = sW;
+  a.Y = static_cast<uint16_t*>(Y);
+  a.T = (int)T;
+  a.K = (int)K;
+  a.N = (int)N;
+  a.thr = threshold;
+  a.parts = reinterpret_cast<uint32_t*>(ws + L.parts);
+  a.bitmap = reinterpret_cast<uint32_t*>(ws + L.bitmap);
+  a.count = reinterpret_cast<int32_t*>(ws + L.count);
+  a.idx = reinterpret_cast<int32_t*>(ws + L.idx);
+  a.aX = reinterpret_cast<float*>(ws + L.aX);
+  a.Xq = reinterpret_cast<int8_t*>(ws + L.Xq);
+  a.Xo = reinterpret_cast<uint16_t*>(ws + L.Xo);
+  a.Wd = reinterpret_cast<uint16_t*>(ws + L.Wd);
+  return a;
+}
+
+int choose_path(int path, int64_t T, int64_t K) {
+  if (path == LLMINT8_PATH_AUTO) return T <= gemv_max_rows((int)K) ? LLMINT8_PATH_GEMV : LLMINT8_PATH_GEMM;
+  return path;
+}
+
+// The whole forward; `events` (nullable) are recorded around each kernel.
+llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sW,
+                          int64_t N, float threshold, void* Y, void* workspace,
+                          size_t workspace_bytes, void* stream_ptr, int path,
+                          uint32_t* dbg_bitmap, int32_t* dbg_idx, int32_t* dbg_count,
+                          int8_t* dbg_Xq, float* dbg_aX, int32_t* dbg_C,
+                          void* const* events, int n_events, int* kernels_launched) {
+  if (kernels_launched) *kernels_launched = 0;
+  llmint8_status st = validate_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes);
+  if (st != LLMINT8_OK) return st;
+  if (path != LLMINT8_PATH_AUTO && path != LLMINT8_PATH_GEMM && path != LLMINT8_PATH_GEMV)
+    return LLMINT8_ERR_INVALID_ARG;
+  const int route = choose_path(path, T, K);
+  if (route == LLMINT8_PATH_GEMV && T > gemv_max_rows((int)K)) return LLMINT8_ERR_UNSUPPORTED;
+  const int nk = route == LLMINT8_PATH_GEMV ? 1 : 3;
+  if (events && n_events < nk + 1) return LLMINT8_ERR_INVALID_ARG;
+  if (T == 0) return LLMINT8_OK;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  LinearArgs a = make_args(X, T, K, Wq, sW, N, threshold, Y, workspace);
+  a.dbg_C = dbg_C;
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
+  };
+  const int cus = device_cu_count();
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return hip_status(e);
+  if (route == LLMINT8_PATH_GEMV) {
+    a.dbg_bitmap = dbg_bitmap;
+    a.dbg_idx = dbg_idx;
+    a.dbg_count = dbg_count;
+    a.dbg_Xq = dbg_Xq;
+    a.dbg_aX = dbg_aX;
+    e = launch_gemv(a, stream);
+    if (e == hipSuccess) e = mark(1);
+    if (e != hipSuccess) return hip_status(e);
+    if (kernels_launched) *kernels_launched = 1;
+    return LLMINT8_OK;
+  }
+  const int groups = scan_row_groups((int)T, (int)K, cus);
+  e = launch_scan(a, groups, stream);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = launch_prepare(a, groups, cus, stream);
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess) e = launch_gemm(a, cus, stream);
+  if (e == hipSuccess) e = mark(3);
+  if (e != hipSuccess) return hip_status(e);
+  if (kernels_launched) *kernels_launched = 3;
+  // intermediate copies for the debug entry point (device to device, async)
+  const size_t KW = (size_t)ceil_div(K, 32);
+  if (dbg_bitmap) e = hipMemcpyAsync(dbg_bitmap, a.bitmap, KW * 4, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && dbg_idx)
+    e = hipMemcpyAsync(dbg_idx, a.idx, (size_t)K * 4, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && dbg_count)
+    e = hipMemcpyAsync(dbg_count, a.count, 4, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && dbg_Xq)
+    e = hipMemcpyAsync(dbg_Xq, a.Xq, (size_t)T * K, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && dbg_aX)
+    e = hipMemcpyAsync(dbg_aX, a.aX, (size_t)T * 4, hipMemcpyDeviceToDevice, stream);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+llmint8_status llmint8_quantize_weight(const void* W, int64_t N, int64_t K, int8_t* Wq, float* sW,
+                                       void* stream) {
+  llmint8_status st = check_sizes(0, K, N);
+  if (st != LLMINT8_OK) return st;
+  if (!W || !Wq || !sW) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_weight(static_cast<const uint16_t*>(W), (int)N, (int)K, Wq, sW,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+  if (check_sizes(T, K, N) != LLMINT8_OK) return 0;
+  return ws_layout(T, K, N).total;
+}
+
+llmint8_status llmint8_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                              const float* sW, int64_t N, float threshold, void* Y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream,
+                    LLMINT8_PATH_AUTO, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, 0, nullptr);
+}
+
+llmint8_status llmint8_linear_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                                    const float* sW, int64_t N, float threshold, void* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int path, uint32_t* outlier_bitmap, int32_t* outlier_idx,
+                                    int32_t* outlier_count, int8_t* Xq, float* aX, int32_t* C) {
+  if ((outlier_bitmap && !aligned(outlier_bitmap, 4)) || (outlier_idx && !aligned(outlier_idx, 4)) ||
+      (outlier_count && !aligned(outlier_count, 4)) || (Xq && !aligned(Xq, 16)) ||
+      (aX && !aligned(aX, 4)) || (C && !aligned(C, 16)))
+    return LLMINT8_ERR_INVALID_ARG;
+  return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream, path,
+                    outlier_bitmap, outlier_idx, outlier_count, Xq, aX, C, nullptr, 0, nullptr);
+}
+
+llmint8_status llmint8_linear_timed(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                                    const float* sW, int64_t N, float threshold, void* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int path, void* const* events, int n_events,
+                                    int* kernels_launched) {
+  if (!events || n_events < 2) return LLMINT8_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events && i < 4; ++i)
+    if (!events[i]) return LLMINT8_ERR_INVALID_ARG;
+  return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream, path,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, events, n_events,
+                    kernels_launched);
+}
+
+int llmint8_gemv_max_rows(int64_t K) {
+  if (K <= 0 || K % 16 != 0 || K > kMaxK) return 0;
+  return gemv_max_rows((int)K);
+}
+
+const char* llmint8_status_string(llmint8_status status) {
+  switch (status) {
+    case LLMINT8_OK: return "ok";
+    case LLMINT8_ERR_INVALID_ARG: return "invalid argument";
+    case LLMINT8_ERR_UNSUPPORTED: return "unsupported shape";
+    case LLMINT8_ERR_WORKSPACE: return "workspace too small";
+    case LLMINT8_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int llmint8_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

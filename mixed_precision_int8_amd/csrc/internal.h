@@ -1,0 +1,92 @@
+// Internal declarations shared by the host dispatcher and the kernel files.
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace llmint8 {
+
+constexpr int kMaxK = 65536;        // bitmap prefix tables live in LDS
+constexpr int kScanMaxGroups = 8;   // row groups of the column scan (partial bitmaps)
+constexpr int kOutChunk = 32;       // outlier columns per fp16 MFMA k-step
+constexpr size_t kWsAlign = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workspace regions (byte offsets from the workspace base), worst case |O| = K.
+//   parts  uint32 [kScanMaxGroups][KW]      per-row-group column bitmaps
+//   bitmap uint32 [KW]                      final outlier bitmap
+//   count  int32  [1]                       |O|
+//   idx    int32  [K]                       ascending outlier columns
+//   aX     fp32   [T]                       row statistic
+//   Xq     int8   [T, K]                    quantized activations
+//   Xo     fp16   [KC][T][32]               outlier activations, chunk-major, zero padded
+//   Wd     fp16   [KC][N][32]               dequantized outlier weight columns, same layout
+// with KW = ceil(K/32) words and KC = ceil(K/32) chunks of 32 outlier columns.
+struct WsLayout {
+  size_t parts, bitmap, count, idx, aX, Xq, Xo, Wd, total;
+};
+
+inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N) {
+  WsLayout L;
+  const int64_t KW = ceil_div(K, 32);
+  const int64_t KC = ceil_div(K, kOutChunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, kWsAlign);
+    return o;
+  };
+  L.parts = take(sizeof(uint32_t) * kScanMaxGroups * KW);
+  L.bitmap = take(sizeof(uint32_t) * KW);
+  L.count = take(sizeof(int32_t) * 4);
+  L.idx = take(sizeof(int32_t) * K);
+  L.aX = take(sizeof(float) * (T > 0 ? T : 1));
+  L.Xq = take((size_t)T * K);
+  L.Xo = take(sizeof(uint16_t) * KC * kOutChunk * (size_t)T);
+  L.Wd = take(sizeof(uint16_t) * KC * kOutChunk * (size_t)N);
+  L.total = off;
+  return L;
+}
+
+// Pointers into a workspace, plus optional debug destinations.
+struct LinearArgs {
+  const uint16_t* X;
+  const int8_t* Wq;
+  const float* sW;
+  uint16_t* Y;
+  int T, K, N;
+  float thr;
+  // workspace
+  uint32_t* parts;
+  uint32_t* bitmap;
+  int32_t* count;
+  int32_t* idx;
+  float* aX;
+  int8_t* Xq;
+  uint16_t* Xo;
+  uint16_t* Wd;
+  // debug outputs (nullable)
+  uint32_t* dbg_bitmap;
+  int32_t* dbg_idx;
+  int32_t* dbg_count;
+  int8_t* dbg_Xq;
+  float* dbg_aX;
+  int32_t* dbg_C;
+};
+
+// Launchers (each enqueues exactly one kernel on `stream`).
+hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW,
+                                  hipStream_t stream);
+int scan_row_groups(int T, int K, int num_cus);
+uint32_t threshold_code(float thr);  // smallest fp16 |x| code whose value reaches thr
+hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream);
+hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStream_t stream);
+hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream);
+int gemv_max_rows(int K);
+hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
+
+}  // namespace llmint8

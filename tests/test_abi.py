@@ -1,0 +1,133 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import mixed_precision_int8_amd as m8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llmint8.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+# fake, never-dereferenced device addresses (validation only looks at null/alignment)
+P = 0x7f0000000000
+ALIGNED = ctypes.c_void_p(P)
+MISALIGNED = ctypes.c_void_p(P + 2)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m8.library_path()):
+        pytest.skip("libllmint8.so not built")
+    return m8.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LLMINT8_API\s+[\w\s\*]+?\b(llmint8_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_symbols()
+    assert "llmint8_quantize_weight" in names and "llmint8_linear" in names
+    assert set(names) == set(m8.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def _linear(lib, X=ALIGNED, T=16, K=1024, Wq=ALIGNED, sW=ALIGNED, N=1024, thr=6.0, Y=ALIGNED,
+            ws=ALIGNED, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.llmint8_workspace_bytes(max(T, 0), K, N) if T >= 0 else 0
+    return lib.llmint8_linear(X, T, K, Wq, sW, N, thr, Y, ws, ws_bytes, None)
+
+
+def test_linear_argument_errors(lib):
+    assert _linear(lib, X=None) == INVALID
+    assert _linear(lib, Y=None) == INVALID
+    assert _linear(lib, Wq=None) == INVALID
+    assert _linear(lib, sW=None) == INVALID
+    assert _linear(lib, ws=None) == INVALID
+    assert _linear(lib, T=-1) == INVALID
+    assert _linear(lib, K=0) == INVALID
+    assert _linear(lib, N=0) == INVALID
+    assert _linear(lib, thr=float("nan")) == INVALID
+    assert _linear(lib, thr=0.0) == INVALID
+    assert _linear(lib, thr=-6.0) == INVALID
+    assert _linear(lib, X=MISALIGNED) == INVALID
+    assert _linear(lib, Y=MISALIGNED) == INVALID
+    assert _linear(lib, Wq=MISALIGNED) == INVALID
+    assert _linear(lib, ws=ctypes.c_void_p(P + 16)) == INVALID     # workspace needs 256-B alignment
+    assert _linear(lib, K=1000) == UNSUPPORTED                      # K % 16 != 0
+    assert _linear(lib, K=65536 + 16) == UNSUPPORTED
+    assert _linear(lib, N=1 << 20, K=4096) == UNSUPPORTED            # N*K >= 2^31
+    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    assert _linear(lib, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_zero_rows_is_a_noop_without_launch(lib):
+    # T == 0 returns OK before any HIP call, even with no X / Y / workspace
+    assert lib.llmint8_linear(None, 0, 1024, ALIGNED, ALIGNED, 1024, 6.0, None, None, 0, None) == OK
+    assert lib.llmint8_linear(None, 0, 1024, ALIGNED, ALIGNED, 1024, math.inf, None, None, 0, None) == OK
+
+
+def test_quantize_weight_argument_errors(lib):
+    q = lib.llmint8_quantize_weight
+    assert q(None, 16, 64, ALIGNED, ALIGNED, None) == INVALID
+    assert q(ALIGNED, 16, 64, None, ALIGNED, None) == INVALID
+    assert q(ALIGNED, 16, 64, ALIGNED, None, None) == INVALID
+    assert q(ALIGNED, 0, 64, ALIGNED, ALIGNED, None) == INVALID
+    assert q(ALIGNED, 16, 0, ALIGNED, ALIGNED, None) == INVALID
+    assert q(ALIGNED, 16, 72, ALIGNED, ALIGNED, None) == UNSUPPORTED
+    assert q(MISALIGNED, 16, 64, ALIGNED, ALIGNED, None) == INVALID
+
+
+def test_debug_and_timed_argument_errors(lib):
+    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    d = lib.llmint8_linear_debug
+    base = [ALIGNED, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, ALIGNED, ALIGNED, need, None]
+    assert d(*base, 7, None, None, None, None, None, None) == INVALID        # unknown path
+    assert d(*base, m8.LLMINT8_PATH_GEMM, None, None, None, MISALIGNED, None, None) == INVALID
+    big_t = lib.llmint8_gemv_max_rows(1024) + 1
+    need2 = lib.llmint8_workspace_bytes(big_t, 1024, 1024)
+    base2 = [ALIGNED, big_t, 1024, ALIGNED, ALIGNED, 1024, 6.0, ALIGNED, ALIGNED, need2, None]
+    assert d(*base2, m8.LLMINT8_PATH_GEMV, None, None, None, None, None, None) == UNSUPPORTED
+    t = lib.llmint8_linear_timed
+    ev = (ctypes.c_void_p * 4)(P, P, P, P)
+    nk = ctypes.c_int(0)
+    assert t(*base, 0, None, 4, ctypes.byref(nk)) == INVALID
+    assert t(*base, m8.LLMINT8_PATH_GEMM, ev, 2, ctypes.byref(nk)) == INVALID   # 3 kernels need 4 events
+
+
+def test_workspace_size_covers_worst_case(lib):
+    for T, K, N in [(1, 16, 1), (16, 1024, 1024), (2048, 4096, 11008), (4096, 8192, 28672)]:
+        ws = lib.llmint8_workspace_bytes(T, K, N)
+        kpad = (K + 31) // 32 * 32
+        # at least: Xq + aX + idx + outlier activations and weight columns for |O| = K
+        assert ws >= T * K + 4 * T + 4 * K + 2 * kpad * (T + N)
+        assert ws < T * K + 4 * T + 4 * K + 2 * kpad * (T + N) + 64 * 1024
+    assert lib.llmint8_workspace_bytes(16, 1000, 16) == 0
+    assert lib.llmint8_workspace_bytes(-1, 1024, 16) == 0
+
+
+def test_gemv_row_limit(lib):
+    assert lib.llmint8_gemv_max_rows(4096) == 16
+    assert lib.llmint8_gemv_max_rows(14336) >= 8
+    assert lib.llmint8_gemv_max_rows(1000) == 0
+    assert lib.llmint8_gemv_max_rows(65536) < 16
+
+
+def test_status_strings(lib):
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert lib.llmint8_status_string(s)
+    assert m8.llmint8_status_string(-3) == "workspace too small"

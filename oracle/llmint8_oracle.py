@@ -203,12 +203,19 @@ def linear(X16: np.ndarray, Wq: np.ndarray, sW: np.ndarray, threshold: float,
 
 
 def parity_error(Y_test: np.ndarray, Y_ref: np.ndarray) -> float:
-    """Max-abs error normalised by the reference's max-abs value (floor 2**-14)."""
+    """Max-abs error normalised by the reference's max-abs finite value (floor 2**-14).
+
+    Entries where the reference overflowed fp16 (+-inf) must match exactly; any
+    other non-finite test value is an infinite error.
+    """
     a = Y_test.astype(np.float64)
     r = Y_ref.astype(np.float64)
     if r.size == 0:
         return 0.0
-    if not np.all(np.isfinite(a[np.isfinite(r)])):
+    fin = np.isfinite(r)
+    if np.any(a[~fin] != r[~fin]) or not np.all(np.isfinite(a[fin])):
         return float("inf")
-    den = max(float(np.abs(r).max()), 2.0 ** -14)
-    return float(np.abs(a - r).max() / den)
+    if not fin.any():
+        return 0.0
+    den = max(float(np.abs(r[fin]).max()), 2.0 ** -14)
+    return float(np.abs(a[fin] - r[fin]).max() / den)

@@ -368,6 +368,10 @@ def test_parity_error_metric():
     assert oracle.parity_error(np.array([[1.0, -2.002]], np.float16), ref) == pytest.approx(
         abs(float(np.float16(-2.002)) + 2.0) / 2.0)
     assert oracle.parity_error(np.array([[np.inf, -2.0]], np.float16), ref) == math.inf
+    over = np.array([[np.inf, -np.inf, 3.0]], np.float16)      # fp16 overflow on both sides
+    assert oracle.parity_error(over, over) == 0.0
+    assert oracle.parity_error(np.array([[np.inf, np.inf, 3.0]], np.float16), over) == math.inf
+    assert oracle.parity_error(np.array([[65504, -np.inf, 3.0]], np.float16), over) == math.inf
 
 
 # --------------------------------------------------------------------------- planted mistakes

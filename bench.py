@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-copies", type=int, default=24,
                    help="distinct weight copies cycled in the decode timing (> last-level cache)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after the measurement, run 5 plain device copies of MIB MiB (untimed), "
+                        "a known-size reference for HBM byte counters")
     return p.parse_args()
 
 
@@ -231,6 +234,16 @@ def main():
                             "outliers": st.count}
 
     print(json.dumps(result), flush=True)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty((n,), dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

@@ -150,18 +150,23 @@ hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream) {
 
 // ---------------------------------------------------------------------------
 // Prepare. Every block ORs the row-group parts into the outlier bitmap in LDS.
-//   quantization blocks [0, nq): one wavefront per row of X; the row is read
-//     once into registers (up to kRegChunks 16-byte chunks per lane), reduced
-//     to its absmax over the kept columns, quantized and written as int8.
-//   gather blocks [nq, nq + ng): per-word prefix counts of the bitmap, then one
-//     thread per (row, 8 consecutive outliers) fills the chunk-major outlier
-//     activations Xo [KC][T][32] and the dequantized outlier weight columns
-//     Wd [KC][N][32] (zero past |O|), all gathers in flight together. The
-//     first gather block publishes bitmap, idx and count.
+//   gather blocks [0, ng) come first in the grid, so that their small bitmap
+//     reads are issued ahead of the quantization blocks' loads of X on the
+//     same CUs. They build the per-word prefix counts of the bitmap and the
+//     ascending outlier indices in LDS, then one thread per (row, 8
+//     consecutive outliers) fills the chunk-major outlier activations
+//     Xo [KC][T][32] and the dequantized outlier weight columns Wd [KC][N][32]
+//     (zero past |O|), all gathers in flight together. Gather block 0
+//     publishes bitmap, idx and count.
+//   quantization blocks [ng, ng + nq): one wavefront per row of X; the row is
+//     read once into registers (up to kRegChunks 16-byte chunks per lane),
+//     reduced to its absmax over the kept columns, quantized and written as
+//     int8.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 256;
 constexpr int kMaxKW = kMaxK / 32;
 constexpr int kRegChunks = 16;
+constexpr int kIdxCap = 4096;  // outlier indices kept in LDS by the gather blocks
 
 __device__ __forceinline__ uint32_t chunk_skip_mask(const uint32_t* bm, int c) {
   return (bm[c >> 2] >> ((c & 3) * 8)) & 0xffu;
@@ -185,14 +190,16 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   __shared__ uint32_t bm[kMaxKW];
   __shared__ int pre[kMaxKW];
   __shared__ int wave_tot[kPrepThreads / 64];
+  __shared__ uint16_t idx_s[kIdxCap];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, K = a.K, N = a.N;
   const int KW = (K + 31) >> 5;
   const int KC = K >> 3;
-  const bool quant = (int)blockIdx.x < nq;
+  const int ng = gridDim.x - nq;  // gather blocks come first: their bitmap reads then
+  const bool quant = (int)blockIdx.x >= ng;  // queue ahead of the quantization blocks' X loads
 
   // quantization blocks start their first row's loads before anything else
-  const int row0 = blockIdx.x * 4 + wave;
+  const int row0 = (blockIdx.x - ng) * 4 + wave;
   uint4 v[kRegChunks];
   const bool in_regs = KC <= 64 * kRegChunks;
   const int cpl = (KC + 63) >> 6;  // chunks per lane
@@ -266,11 +273,15 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   int run = base + incl - local;
   for (int w = w0; w < w1; ++w) {
     pre[w] = run;
-    run += __popc(bm[w]);
+    uint32_t bits = bm[w];
+    while (bits) {  // ascending outlier columns, as far as the LDS table reaches
+      if (run < kIdxCap) idx_s[run] = (uint16_t)(w * 32 + __builtin_ctz(bits));
+      ++run;
+      bits &= bits - 1u;
+    }
   }
   __syncthreads();
-
-  const int gb = blockIdx.x - nq;
+  const int gb = blockIdx.x;
   if (gb == 0) {
     for (int w = tid; w < KW; w += kPrepThreads) {
       a.bitmap[w] = bm[w];
@@ -288,27 +299,42 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   // one item = (row of Xo or Wd, group of 8 consecutive outliers)
   const int ngrp = (count + kOutChunk - 1) / kOutChunk * (kOutChunk / 8);
   const int items = (T + N) * ngrp;  // < 2^31: T, N < 2^31 / K and ngrp <= K / 8
-  const int ng = gridDim.x - nq;
   for (int it = gb * kPrepThreads + tid; it < items; it += ng * kPrepThreads) {
     const int row = it / ngrp;
     const int jg = it - row * ngrp;
     const int j0 = jg * 8;
-    // column of each outlier j0 .. j0+7: binary search for the word holding
-    // it (last word with pre[w] <= j), then the (j - pre[w])-th set bit of
-    // that word; the 8 searches are independent
+    // column of each outlier j0 .. j0+7 (index 0 past |O|, masked later):
+    // from the LDS table, or beyond it by a binary search for the word holding
+    // it (last word with pre[w] <= j), all 8 searches advancing together,
+    // then the (j - pre[w])-th set bit of that word
     int h[8];
     const int nvalid = min(8, max(0, count - j0));
+    if (j0 + 8 <= kIdxCap) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = min(j0 + e, count - 1);
-      int lo = 0, hi = KW - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= j) lo = mid; else hi = mid - 1;
+      for (int e = 0; e < 8; ++e) h[e] = idx_s[min(j0 + e, count - 1)];
+    } else {
+      int lo[8], hi[8], jj[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        jj[e] = min(j0 + e, count - 1);
+        lo[e] = 0;
+        hi[e] = KW - 1;
       }
-      uint32_t bits = bm[lo];
-      for (int r = j - pre[lo]; r > 0; --r) bits &= bits - 1u;
-      h[e] = lo * 32 + __builtin_ctz(bits);
+      for (int span = KW; span > 1; span = (span + 1) >> 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int mid = (lo[e] + hi[e] + 1) >> 1;
+          if (lo[e] < hi[e]) {
+            if (pre[mid] <= jj[e]) lo[e] = mid; else hi[e] = mid - 1;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t bits = bm[lo[e]];
+        for (int r = jj[e] - pre[lo[e]]; r > 0; --r) bits &= bits - 1u;
+        h[e] = lo[e] * 32 + __builtin_ctz(bits);
+      }
     }
     // all 8 gathers are issued unconditionally (index 0 past |O|, masked
     // afterwards) so that they are in flight together

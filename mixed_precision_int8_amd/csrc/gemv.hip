@@ -13,19 +13,20 @@
 // and splits into two roles:
 //   * 4 stream wavefronts issue the block's weight loads into registers at
 //     once (16 x 16-byte loads per lane). Issuing that much stalls the issuing
-//     wavefront for about a microsecond, so these wavefronts do nothing else
-//     until the int8 rows of X are ready; then each multiplies its quarter of
-//     K on v_mfma_i32_16x16x64_i8 (16 weight rows as A, int8 rows of X as B)
-//     and leaves its int32 partial sums in LDS.
-//   * 4 X wavefronts copy X into LDS (buffer_load ... lds), then a thread owns
-//     8-column chunks across all T rows: it decides their outlier flags on its
-//     own (column absmax >= threshold), takes the rows' maxima over its kept
-//     columns in the same pass (packed u16 arithmetic on fp16 codes), and
-//     after one block-wide reduction quantizes its chunks. X wavefront 0 also
-//     compacts the outlier indices, gathers the weight bytes of the first 32
-//     outlier columns, computes the 16-bit outlier product on
-//     v_mfma_f32_16x16x32_f16 while the stream wavefronts multiply, and
-//     finally dequantizes the exact int32 sums and stores fp16 Y.
+//     wavefront for about a microsecond, which is about when X has landed.
+//   * 4 X wavefronts copy X into LDS (buffer_load ... lds) meanwhile.
+//   * Then all 8 wavefronts work on X: a thread owns 8-column chunks across
+//     all T rows, decides their outlier flags on its own (column absmax >=
+//     threshold), takes the rows' maxima over its kept columns in the same
+//     pass (packed u16 arithmetic on fp16 codes), and after one block-wide
+//     reduction quantizes its chunks into LDS.
+//   * The stream wavefronts then multiply their quarter of K on
+//     v_mfma_i32_16x16x64_i8 (16 weight rows as A, int8 rows of X as B) and
+//     leave int32 partial sums in LDS. Meanwhile X wavefront 0, which has
+//     compacted the outlier indices and gathered the weight bytes of the
+//     first 32 outlier columns, computes the 16-bit outlier product on
+//     v_mfma_f32_16x16x32_f16; it finally sums the partials, dequantizes and
+//     stores fp16 Y.
 // The kernel is instantiated per row capacity TB (1, 2, 4, 8, 16 >= T) so
 // that per-row loops are resolved at compile time.
 #include <atomic>
@@ -61,8 +62,8 @@ __host__ __device__ inline GemvLds gemv_lds(int T, int K) {
   off += 4 * 64 * 16;
   L.arow = off;
   off += kGemvRowsN * 4;
-  L.rowred = off;  // [4 wavefronts][8 row pairs] packed u16 maxima
-  off += 4 * 8 * 4;
+  L.rowred = off;  // [8 wavefronts][8 row pairs] packed u16 maxima
+  off += 8 * 8 * 4;
   L.cnt = off;
   off += 16;
   L.total = off;
@@ -170,15 +171,16 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   lds_barrier();  // A: X is in LDS, the bitmap is clear
 
   uint32_t g[8];
-  if (xwave) {
-    // ---- 3. a thread takes 8-column chunks across all rows: column absmax
+  {
+    // ---- 3. all 8 wavefronts (the stream wavefronts have issued their loads
+    // by now): a thread takes 8-column chunks across all rows: column absmax
     // -> outlier flags -> keep masks -> row maxima over the kept columns. All
     // values are fp16 codes with the sign cleared, compared as packed u16.
     const v2u16 hthr2 = {(uint16_t)hthr, (uint16_t)hthr};
     v2u16 rmax[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) rmax[t] = v2u16{0, 0};
-    for (int c = xt; c < KC; c += 256) {
+    for (int c = tid; c < KC; c += 512) {
       v2u16 ab[TB][4];
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
@@ -225,14 +227,14 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   }
   lds_barrier();  // B: bitmap and partial row maxima complete
 
-  if (xwave) {
-    // ---- 4. row scales: lane t (< T) of every X wavefront combines the 4
+  {
+    // ---- 4. row scales: lane t (< T) of every wavefront combines the 8
     // partial maxima of row t; the scales then go to scalar registers
     float srow = 0.0f;
     if (lane < T) {
       uint32_t m = 0u;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) m = max(m, (rowred[w * 8 + (lane >> 1)] >> ((lane & 1) * 16)) & 0xffffu);
+      for (int w = 0; w < 8; ++w) m = max(m, (rowred[w * 8 + (lane >> 1)] >> ((lane & 1) * 16)) & 0xffffu);
       const float ax = half_bits_to_float(m);
       srow = m ? 127.0f / ax : 0.0f;
       if (wave == 0) arow[lane] = ax;
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     for (int t = 0; t < TB; ++t)
       st[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, srow), t));
     // int8 codes of this thread's chunks
-    for (int c = xt; c < KC; c += 256) {
+    for (int c = tid; c < KC; c += 512) {
       const uint32_t skip = (bm[c >> 2] >> ((c & 3) * 8)) & 0xffu;
       const uint32_t m0 = expand4(~skip & 0xfu), m1 = expand4((~skip >> 4) & 0xfu);
       uint4 v[TB];

@@ -34,8 +34,11 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "kb_gemm_prefill_counters.txt"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10,
+                   help="untimed calls before timing; at least this many, and at least "
+                        "--warmup-ms of back-to-back calls (the clock ramps up under load)")
+    p.add_argument("--warmup-ms", type=float, default=30.0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-copies", type=int, default=24,
@@ -99,8 +102,13 @@ def main():
     def step():
         m8.llmint8_linear(Xd, Wq, sW, thr, Y=Y, workspace=ws)
 
-    for _ in range(args.warmup):
+    warm = 0
+    w0 = time.perf_counter()
+    while warm < args.warmup or (time.perf_counter() - w0) * 1e3 < args.warmup_ms:
         step()
+        warm += 1
+        if warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -138,6 +146,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -87,7 +87,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 template <class G>
 __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tiles_t, int group_n) {
-  __shared__ __attribute__((aligned(1024))) char smem[G::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDS + (G::BN + G::BT) * 4];
+  // the tile's weight and activation scales, read by the epilogue
+  float* sW_l = reinterpret_cast<float*>(smem + G::LDS);
+  float* aX_l = sW_l + G::BN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -221,12 +224,29 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
       order_reads_before_mfma();
     }
     // stage kt+1 must have landed (later stages may still be in flight) and
-    // this wavefront's reads of stage kt must be done before the barrier
+    // this wavefront's reads of stage kt must be done before the barrier.
+    // The scheduling barrier keeps this stage's MFMAs ahead of the waits, so
+    // they run while the copy lands.
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(P - 1) * G::LOADS>();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     barrier_no_fence();
     (void)next_slot;
   };
+  {
+    // scales -> LDS by direct copy (rows past the matrix read as zero). They
+    // are issued before the first K stage, so the stage waits cover them.
+    constexpr int CS = (G::BN + 63) / 64, CX = (G::BT + 63) / 64;
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.sW + n0, (uint32_t)(rows_n * 4));
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.aX + t0, (uint32_t)(rows_t * 4));
+    for (int c = wave; c < CS + CX; c += G::NWAVES) {
+      const bool is_w = c < CS;  // wave-uniform
+      const int cc = is_w ? c : c - CS;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          is_w ? rS : rX, (__attribute__((address_space(3))) void*)((is_w ? sW_l : aX_l) + cc * 64),
+          4, (uint32_t)((cc * 64 + lane) * 4), 0, 0, 0);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < P; ++s) issue(s, s);
   wait_vmcnt<(P - 1) * G::LOADS>();
@@ -246,20 +266,38 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
   const int tl = t0 + wt * G::WT + fi;      // + j*32
   float as[G::FT];
 #pragma unroll
-  for (int j = 0; j < G::FT; ++j) {
-    const int t = tl + j * 32;
-    as[j] = t < T ? a.aX[t] : 0.0f;
-  }
+  for (int j = 0; j < G::FT; ++j) as[j] = aX_l[wt * G::WT + fi + j * 32];
   const bool vec_ok = (N & 3) == 0;
   const int count = *a.count;
   const int nch = (count + kOutChunk - 1) / kOutChunk;
+  // Operands of the first chunk of 32 outlier columns (the common case is a
+  // single chunk), all requested before the first is used so that the
+  // epilogue pays one memory latency rather than one per block.
+  v8h wf0[G::FN][2], xf0[G::FT][2];
+  if (nch > 0) {
+#pragma unroll
+    for (int i = 0; i < G::FN; ++i) {
+      const int nrow = min(n0 + wn * G::WN + i * 32 + fi, N - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wf0[i][h] = *reinterpret_cast<const v8h*>(a.Wd + (size_t)nrow * kOutChunk + h * 16 + fg * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < G::FT; ++j) {
+      const int t = min(tl + j * 32, T - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        xf0[j][h] = *reinterpret_cast<const v8h*>(a.Xo + (size_t)t * kOutChunk + h * 16 + fg * 8);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < G::FN; ++i) {
     float bs[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int n = nl + i * 32 + 8 * (v >> 2) + (v & 3);
-      bs[v] = n < N ? a.sW[n] * (1.0f / 16129.0f) : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const v4f w4 = *reinterpret_cast<const v4f*>(sW_l + wn * G::WN + 4 * fg + i * 32 + 8 * q);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bs[4 * q + r] = w4[r] * (1.0f / 16129.0f);
     }
     if (a.dbg_C) {
 #pragma unroll
@@ -280,8 +318,15 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
       for (int v = 0; v < 16; ++v) y[j][v] = (float)acc[i][j][v] * (as[j] * bs[v]);
     // outlier columns: fp16 operands, fp32 accumulation on top of the int8 part;
     // a chunk of 32 outlier columns is two 32x32x16 steps.
+    if (nch > 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < G::FT; ++j)
+          y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf0[i][h], xf0[j][h], y[j], 0, 0, 0);
+    }
     const int nrow = min(n0 + wn * G::WN + i * 32 + fi, N - 1);
-    for (int c = 0; c < nch; ++c) {
+    for (int c = 1; c < nch; ++c) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const v8h wf = *reinterpret_cast<const v8h*>(

@@ -43,6 +43,24 @@ reason, in the design notes):
       weight dequantized: ``fp16(fl32(fl32(q * b) / 127))``.
 * R8  the outlier product has fp16 operands; the output is rounded once to fp16.
 * R9  the threshold is compared in fp32; ``+inf`` gives an empty outlier set.
+* B1  the input gradient through the frozen layer, used to train an adapter on
+      top of it, treats the layer as the linear map ``X -> X . Wdeq^T`` with the
+      stored weight dequantized per operation, ``Wdeq = fp16(fl32(fl32(q * b) /
+      127))`` for every entry (as in R7); quantizing X has no useful derivative.
+      ``dX = fp16(dY . Wdeq)``: fp16 operands, a wide accumulation, one
+      rounding to fp16.
+
+The backward sources:
+
+* [HFQ-T]  "Hugging Face Quantization with bitsandbytes ...", the quick
+           comparison table before section 1 (an int8 model is not trained
+           directly: it is frozen and an adapter is added) and section 6
+           "Quantization for Inference vs. Quantization for Training (QLoRA)"
+           (the quantized weights stay frozen while gradients still have to
+           flow through them).
+* [DCT-S]  "bitsandbytes" (mining glossary), "Where it fits in the stack":
+           weights are dequantized for each operation instead of being
+           computed on directly.
 
 Precision: every quantization step is the fp32 operation named (NumPy float32
 arithmetic is IEEE round-to-nearest-even); ``np.rint`` is round-half-to-even.
@@ -59,6 +77,7 @@ import numpy as np
 __all__ = [
     "quantize_weight", "outlier_columns", "pack_bitmap", "quantize_activations",
     "int8_matmul", "outlier_operands", "output", "linear", "Stages", "parity_error",
+    "dequantize_weight", "linear_backward_input",
 ]
 
 _F32_127 = np.float32(127.0)
@@ -219,3 +238,26 @@ def parity_error(Y_test: np.ndarray, Y_ref: np.ndarray) -> float:
         return 0.0
     den = max(float(np.abs(r[fin]).max()), 2.0 ** -14)
     return float(np.abs(a[fin] - r[fin]).max() / den)
+
+
+def dequantize_weight(Wq: np.ndarray, sW: np.ndarray) -> np.ndarray:
+    """The stored weight dequantized per operation ([DCT-S]; R7, B1).
+
+    ``Wdeq[n, k] = fp16(fl32(fl32(Wq[n, k] * sW[n]) / 127))`` for every entry;
+    the outlier operand ``Wd`` of the forward is its columns at the outliers.
+    """
+    q32 = np.asarray(Wq).astype(np.float32)
+    return ((q32 * np.asarray(sW, dtype=np.float32)[:, None]) / _F32_127).astype(np.float16)
+
+
+def linear_backward_input(dY16: np.ndarray, Wq: np.ndarray, sW: np.ndarray) -> np.ndarray:
+    """Input gradient of the frozen layer, the step that lets an adapter train on top of it ([HFQ-T]; B1).
+
+    ``dX = fp16( dY @ Wdeq )`` with ``Wdeq = dequantize_weight(Wq, sW)``: the
+    fp16 products are exact in float64, the sum is formed in float64 and the
+    result is rounded once to fp16.
+    """
+    Wd = dequantize_weight(Wq, sW)
+    dX64 = np.asarray(dY16).astype(np.float64) @ Wd.astype(np.float64)
+    with np.errstate(over="ignore"):
+        return dX64.astype(np.float16)

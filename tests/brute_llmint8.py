@@ -116,3 +116,27 @@ def forward(X, W, thr):
         Y.append(row)
     return {"outliers": outl, "Wq": Wq, "sW": sW, "Xq": Xq, "aX": aX, "C": C, "Wd": Wd,
             "Y": [[y for _, y in r] for r in Y], "Y_exact": [[e for e, _ in r] for r in Y]}
+
+
+def backward_input(dY, Wq, sW):
+    """Input gradient through the frozen layer, for tiny inputs.
+
+    dY: T x N list of fp16-valued floats; Wq: N x K list of ints; sW: N floats.
+    Each dequantized entry is fp16(fl32(fl32(q * b) / 127)) (fp32 product and
+    quotient by the rounding facts above); the sum over n of dY * Wdeq is an
+    exact Fraction, rounded once to fp16.
+    """
+    T = len(dY)
+    N = len(Wq)
+    K = len(Wq[0]) if N else 0
+    Wdeq = [[f16(f32(f32(Wq[n][k] * sW[n]) / 127.0)) for k in range(K)] for n in range(N)]
+    dX = []
+    for t in range(T):
+        row = []
+        for k in range(K):
+            acc = Fraction(0)
+            for n in range(N):
+                acc += Fraction(dY[t][n]) * Fraction(Wdeq[n][k])
+            row.append(f16_of_fraction(acc))
+        dX.append(row)
+    return Wdeq, dX

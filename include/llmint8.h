@@ -61,7 +61,7 @@ typedef int llmint8_status;
 
 #define LLMINT8_OK               0
 #define LLMINT8_ERR_INVALID_ARG -1 /* null pointer, size <= 0 (T < 0), bad threshold, misaligned */
-#define LLMINT8_ERR_UNSUPPORTED -2 /* K % 16 != 0, K > 65536, N*K or T*K >= 2^31 */
+#define LLMINT8_ERR_UNSUPPORTED -2 /* K % 16 != 0, K > 65536, N*K or T*K >= 2^31 (backward: N % 8 != 0 or N > 65536) */
 #define LLMINT8_ERR_WORKSPACE   -3 /* workspace smaller than llmint8_workspace_bytes(T,K,N) */
 #define LLMINT8_ERR_HIP         -4 /* a HIP launch or runtime call failed */
 
@@ -138,6 +138,55 @@ LLMINT8_API llmint8_status llmint8_linear_timed(const void* X, int64_t T, int64_
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     int path, void* const* events, int n_events,
                                     int* kernels_launched);
+
+/*
+ * Input gradient of the frozen layer, the step that lets an adapter be
+ * trained on top of it ("Hugging Face Quantization with bitsandbytes ...",
+ * the comparison table before section 1 and section 6: an int8 model is
+ * frozen and an adapter is trained on top, with gradients flowing through the
+ * quantized weights). The layer is taken as the linear map X -> X . Wdeq^T
+ * with the stored weight dequantized for the operation ("bitsandbytes"
+ * glossary, "Where it fits in the stack"):
+ *   Wdeq[n,k] = fp16(fl32(fl32(Wq[n,k] * sW[n]) / 127))
+ *   dX        = fp16( dY . Wdeq )            (fp16 products, fp32 sums)
+ *
+ *   dY        [in]  fp16 [T, N], device (gradient of the layer output)
+ *   Wq, sW    [in]  from llmint8_quantize_weight (int8 [N, K], fp32 [N])
+ *   dX        [out] fp16 [T, K], device
+ *   workspace [tmp] device, >= llmint8_backward_workspace_bytes(T, K, N)
+ *                   bytes, 256-byte aligned; it receives Wdeq transposed
+ * Requires, besides the forward's size limits, N % 8 == 0 and N <= 65536
+ * (LLMINT8_ERR_UNSUPPORTED otherwise). T == 0 is a valid no-op. Results are
+ * exact for the dequantization and within fp32 summation order for dX.
+ */
+LLMINT8_API size_t llmint8_backward_workspace_bytes(int64_t T, int64_t K, int64_t N);
+LLMINT8_API llmint8_status llmint8_linear_backward_input(const void* dY, int64_t T, int64_t K,
+                                                         const int8_t* Wq, const float* sW,
+                                                         int64_t N, void* dX, void* workspace,
+                                                         size_t workspace_bytes, void* stream);
+
+/*
+ * llmint8_linear_backward_input recording caller-created HIP events on the
+ * stream: events[0] before the dequantization kernel, events[1] between the
+ * two kernels, events[2] after the GEMM (n_events >= 3). *kernels_launched
+ * (host int, may be NULL) receives 2.
+ */
+LLMINT8_API llmint8_status llmint8_linear_backward_input_timed(
+    const void* dY, int64_t T, int64_t K, const int8_t* Wq, const float* sW, int64_t N, void* dX,
+    void* workspace, size_t workspace_bytes, void* stream, void* const* events, int n_events,
+    int* kernels_launched);
+
+/*
+ * The stored weight dequantized for an operation, transposed ("bitsandbytes"
+ * glossary, "Where it fits in the stack"):
+ *   WdT[k][n] = fp16(fl32(fl32(Wq[n,k] * sW[n]) / 127))
+ *   Wq, sW [in]  from llmint8_quantize_weight (int8 [N, K], fp32 [N])
+ *   WdT    [out] fp16 [K, N], device
+ * Requires N % 8 == 0, N <= 65536 and the forward's limits on K and N*K. The result is
+ * bit-exact for every sW that llmint8_quantize_weight produces.
+ */
+LLMINT8_API llmint8_status llmint8_dequantize_weight_t(const int8_t* Wq, const float* sW, int64_t N,
+                                                       int64_t K, void* WdT, void* stream);
 
 /* Largest T the fused GEMV route accepts for this K (0 if none). */
 LLMINT8_API int llmint8_gemv_max_rows(int64_t K);

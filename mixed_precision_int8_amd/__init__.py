@@ -15,7 +15,9 @@ __all__ = [
     "LLMINT8_PATH_AUTO", "LLMINT8_PATH_GEMM", "LLMINT8_PATH_GEMV", "Llmint8Error",
     "library_path", "load_library", "llmint8_quantize_weight", "llmint8_workspace_bytes",
     "llmint8_linear", "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
-    "llmint8_status_string", "Int8Linear", "EXPORTED_SYMBOLS",
+    "llmint8_status_string", "llmint8_backward_workspace_bytes", "llmint8_dequantize_weight_t",
+    "llmint8_linear_backward_input", "llmint8_linear_backward_input_timed", "Int8Linear",
+    "EXPORTED_SYMBOLS",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -25,7 +27,9 @@ LLMINT8_PATH_GEMV = 2
 EXPORTED_SYMBOLS = (
     "llmint8_quantize_weight", "llmint8_workspace_bytes", "llmint8_linear",
     "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
-    "llmint8_status_string", "llmint8_last_hip_error",
+    "llmint8_status_string", "llmint8_last_hip_error", "llmint8_backward_workspace_bytes",
+    "llmint8_dequantize_weight_t", "llmint8_linear_backward_input",
+    "llmint8_linear_backward_input_timed",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +74,16 @@ def load_library():
     lib.llmint8_linear_timed.argtypes = lin + [ctypes.c_int, ctypes.POINTER(_vp), ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_int)]
     lib.llmint8_linear_timed.restype = ctypes.c_int
+    lib.llmint8_backward_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    lib.llmint8_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.llmint8_dequantize_weight_t.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+    lib.llmint8_dequantize_weight_t.restype = ctypes.c_int
+    bwd = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.llmint8_linear_backward_input.argtypes = bwd
+    lib.llmint8_linear_backward_input.restype = ctypes.c_int
+    lib.llmint8_linear_backward_input_timed.argtypes = bwd + [ctypes.POINTER(_vp), ctypes.c_int,
+                                                              ctypes.POINTER(ctypes.c_int)]
+    lib.llmint8_linear_backward_input_timed.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
     lib.llmint8_gemv_max_rows.restype = ctypes.c_int
     lib.llmint8_status_string.argtypes = [ctypes.c_int]
@@ -219,13 +233,101 @@ def llmint8_linear_timed(X, Wq, sW, threshold, Y, workspace, events, path=LLMINT
     return nk.value
 
 
+def llmint8_backward_workspace_bytes(T: int, K: int, N: int) -> int:
+    return int(load_library().llmint8_backward_workspace_bytes(T, K, N))
+
+
+def llmint8_dequantize_weight_t(Wq, sW, WdT=None, stream=None):
+    """(Wq int8 [N, K], sW fp32 [N]) -> WdT fp16 [K, N], the weight dequantized and transposed."""
+    import torch
+    lib = load_library()
+    N, K = Wq.shape
+    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(sW, torch.float32, (N,), "sW")
+    if WdT is None:
+        WdT = torch.empty((K, N), dtype=torch.float16, device=Wq.device)
+    _need(WdT, torch.float16, (K, N), "WdT")
+    _check(lib.llmint8_dequantize_weight_t(_ptr(Wq), _ptr(sW), N, K, _ptr(WdT),
+                                           _stream(stream, Wq.device)),
+           "llmint8_dequantize_weight_t")
+    return WdT
+
+
+def _backward_args(dY, Wq, sW, dX, workspace):
+    import torch
+    T, N = dY.shape
+    K = Wq.shape[1]
+    _need(dY, torch.float16, (T, N), "dY")
+    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(sW, torch.float32, (N,), "sW")
+    if dX is None:
+        dX = torch.empty((T, K), dtype=torch.float16, device=dY.device)
+    _need(dX, torch.float16, (T, K), "dX")
+    if workspace is None:
+        need = llmint8_backward_workspace_bytes(T, K, N)
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dY.device)
+    return T, K, N, dX, workspace
+
+
+def llmint8_linear_backward_input(dY, Wq, sW, dX=None, workspace=None, stream=None):
+    """dX fp16 [T, K] = dY fp16 [T, N] . Wdeq, the input gradient of the frozen layer."""
+    lib = load_library()
+    T, K, N, dX, ws = _backward_args(dY, Wq, sW, dX, workspace)
+    _check(lib.llmint8_linear_backward_input(_ptr(dY), T, K, _ptr(Wq), _ptr(sW), N, _ptr(dX),
+                                             _ptr(ws), ws.numel() * ws.element_size(),
+                                             _stream(stream, dY.device)),
+           "llmint8_linear_backward_input")
+    return dX
+
+
+def llmint8_linear_backward_input_timed(dY, Wq, sW, events, dX=None, workspace=None, stream=None):
+    """Input gradient recording ``events`` (3 created torch.cuda.Event) around its two kernels."""
+    lib = load_library()
+    T, K, N, dX, ws = _backward_args(dY, Wq, sW, dX, workspace)
+    handles = (_vp * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    nk = ctypes.c_int(0)
+    _check(lib.llmint8_linear_backward_input_timed(_ptr(dY), T, K, _ptr(Wq), _ptr(sW), N, _ptr(dX),
+                                                   _ptr(ws), ws.numel() * ws.element_size(),
+                                                   _stream(stream, dY.device), handles, len(events),
+                                                   ctypes.byref(nk)),
+           "llmint8_linear_backward_input_timed")
+    return dX
+
+
+def _autograd_function():
+    import torch
+
+    class _Int8LinearFn(torch.autograd.Function):
+        """Forward through llmint8_linear; backward gives the input gradient only
+        (the int8 weight is frozen; an adapter trained on top needs dX)."""
+
+        @staticmethod
+        def forward(ctx, X2, layer):
+            ctx.layer = layer
+            return llmint8_linear(X2, layer.Wq, layer.sW, layer.threshold,
+                                  workspace=layer._workspace(X2.shape[0], X2.device))
+
+        @staticmethod
+        def backward(ctx, dY):
+            layer = ctx.layer
+            dX = llmint8_linear_backward_input(dY.contiguous(), layer.Wq, layer.sW)
+            return dX, None
+
+    return _Int8LinearFn
+
+
+_FN = None
+
+
 class Int8Linear:
     """Drop-in int8 replacement of a bias-free fp16 linear layer.
 
     The weight is quantized once at construction ("bitsandbytes" glossary,
     introduction: quantization happens when the model loads); ``forward`` runs
     the LLM.int8() forward ("Hugging Face Quantization with bitsandbytes",
-    sections 2 and 3).
+    sections 2 and 3) and, for inputs that require a gradient, registers the
+    input-gradient kernels as its backward (same page, section 6: the int8
+    weights stay frozen while an adapter on top is trained).
     """
 
     def __init__(self, weight, threshold: float = 6.0):
@@ -245,10 +347,18 @@ class Int8Linear:
         return self._ws
 
     def forward(self, X):
+        """Y = the LLM.int8() forward of X. When X requires a gradient, the
+        backward pass gives dX = dY . Wdeq (the weight itself stays frozen)."""
+        global _FN
         shape = X.shape
         X2 = X.reshape(-1, self.in_features).contiguous()
-        Y = llmint8_linear(X2, self.Wq, self.sW, self.threshold,
-                           workspace=self._workspace(X2.shape[0], X2.device))
+        if X2.requires_grad:
+            if _FN is None:
+                _FN = _autograd_function()
+            Y = _FN.apply(X2, self)
+        else:
+            Y = llmint8_linear(X2, self.Wq, self.sW, self.threshold,
+                               workspace=self._workspace(X2.shape[0], X2.device))
         return Y.reshape(*shape[:-1], self.out_features)
 
     __call__ = forward

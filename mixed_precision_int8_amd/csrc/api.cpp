@@ -156,6 +156,53 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   return hip_status(e);
 }
 
+llmint8_status check_backward_sizes(int64_t T, int64_t K, int64_t N) {
+  llmint8_status st = check_sizes(T, K, N);
+  if (st != LLMINT8_OK) return st;
+  // WdT and dY rows (2N bytes) are copied in whole 16-byte pieces, and a tile's
+  // rows x 2N bytes must stay within 32-bit buffer offsets
+  if (N % 8 != 0 || N > kMaxK) return LLMINT8_ERR_UNSUPPORTED;
+  return LLMINT8_OK;
+}
+
+size_t backward_workspace(int64_t K, int64_t N) { return align_up((size_t)2 * N * K, kWsAlign); }
+
+// dX = dY . Wdeq: dequantize-transpose into the workspace, then the fp16 GEMM.
+llmint8_status run_backward_input(const void* dY, int64_t T, int64_t K, const int8_t* Wq,
+                                  const float* sW, int64_t N, void* dX, void* workspace,
+                                  size_t workspace_bytes, void* stream_ptr, void* const* events,
+                                  int n_events, int* kernels_launched) {
+  if (kernels_launched) *kernels_launched = 0;
+  llmint8_status st = check_backward_sizes(T, K, N);
+  if (st != LLMINT8_OK) return st;
+  if (!Wq || !sW || !aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
+  if (events && n_events < 3) return LLMINT8_ERR_INVALID_ARG;
+  if (T == 0) return LLMINT8_OK;
+  if (!dY || !dX || !workspace) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(dY, 16) || !aligned(dX, 16) || !aligned(workspace, kWsAlign)) return LLMINT8_ERR_INVALID_ARG;
+  if (workspace_bytes < backward_workspace(K, N)) return LLMINT8_ERR_WORKSPACE;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
+  };
+  BwdArgs a{};
+  a.dY = static_cast<const uint16_t*>(dY);
+  a.WdT = static_cast<uint16_t*>(workspace);
+  a.dX = static_cast<uint16_t*>(dX);
+  a.T = (int)T;
+  a.K = (int)K;
+  a.N = (int)N;
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_dequant_t(Wq, sW, (int)N, (int)K, static_cast<uint16_t*>(workspace), stream);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = launch_gemm_f16(a, device_cu_count(), stream);
+  if (e == hipSuccess) e = mark(2);
+  if (e != hipSuccess) return hip_status(e);
+  if (kernels_launched) *kernels_launched = 2;
+  return LLMINT8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,6 +254,40 @@ llmint8_status llmint8_linear_timed(const void* X, int64_t T, int64_t K, const i
   return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream, path,
                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, events, n_events,
                     kernels_launched);
+}
+
+size_t llmint8_backward_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+  if (check_backward_sizes(T, K, N) != LLMINT8_OK) return 0;
+  return backward_workspace(K, N);
+}
+
+llmint8_status llmint8_dequantize_weight_t(const int8_t* Wq, const float* sW, int64_t N, int64_t K,
+                                           void* WdT, void* stream) {
+  llmint8_status st = check_backward_sizes(0, K, N);
+  if (st != LLMINT8_OK) return st;
+  if (!Wq || !sW || !WdT) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(Wq, 16) || !aligned(sW, 4) || !aligned(WdT, 16)) return LLMINT8_ERR_INVALID_ARG;
+  return hip_status(launch_dequant_t(Wq, sW, (int)N, (int)K, static_cast<uint16_t*>(WdT),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+llmint8_status llmint8_linear_backward_input(const void* dY, int64_t T, int64_t K, const int8_t* Wq,
+                                             const float* sW, int64_t N, void* dX, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return run_backward_input(dY, T, K, Wq, sW, N, dX, workspace, workspace_bytes, stream, nullptr, 0,
+                            nullptr);
+}
+
+llmint8_status llmint8_linear_backward_input_timed(const void* dY, int64_t T, int64_t K,
+                                                   const int8_t* Wq, const float* sW, int64_t N,
+                                                   void* dX, void* workspace, size_t workspace_bytes,
+                                                   void* stream, void* const* events, int n_events,
+                                                   int* kernels_launched) {
+  if (!events || n_events < 3) return LLMINT8_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (!events[i]) return LLMINT8_ERR_INVALID_ARG;
+  return run_backward_input(dY, T, K, Wq, sW, N, dX, workspace, workspace_bytes, stream, events,
+                            n_events, kernels_launched);
 }
 
 int llmint8_gemv_max_rows(int64_t K) {

@@ -78,6 +78,15 @@ struct LinearArgs {
   int32_t* dbg_C;
 };
 
+// Operands of the input gradient dX = dY . Wdeq (WdT: the dequantized weight,
+// transposed, in the workspace).
+struct BwdArgs {
+  const uint16_t* dY;  // fp16 [T, N]
+  const uint16_t* WdT; // fp16 [K, N]
+  uint16_t* dX;        // fp16 [T, K]
+  int T, K, N;
+};
+
 // Launchers (each enqueues exactly one kernel on `stream`).
 hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW,
                                   hipStream_t stream);
@@ -88,5 +97,9 @@ hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStrea
 hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream);
 int gemv_max_rows(int K);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
+hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uint16_t* WdT,
+                            hipStream_t stream);
+hipError_t launch_gemm_f16(const BwdArgs& a, int num_cus, hipStream_t stream);
+hipError_t launch_gemm_f16_variant(const BwdArgs& a, int variant, hipStream_t stream);
 
 }  // namespace llmint8

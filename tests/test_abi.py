@@ -132,3 +132,48 @@ def test_status_strings(lib):
     for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.llmint8_status_string(s)
     assert m8.llmint8_status_string(-3) == "workspace too small"
+
+
+def _backward(lib, dY=ALIGNED, T=16, K=1024, Wq=ALIGNED, sW=ALIGNED, N=1024, dX=ALIGNED,
+              ws=ALIGNED, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.llmint8_backward_workspace_bytes(max(T, 0), K, N) if T >= 0 else 0
+    return lib.llmint8_linear_backward_input(dY, T, K, Wq, sW, N, dX, ws, ws_bytes, None)
+
+
+def test_backward_argument_errors(lib):
+    assert _backward(lib, dY=None) == INVALID
+    assert _backward(lib, dX=None) == INVALID
+    assert _backward(lib, Wq=None) == INVALID
+    assert _backward(lib, sW=None) == INVALID
+    assert _backward(lib, ws=None) == INVALID
+    assert _backward(lib, T=-1) == INVALID
+    assert _backward(lib, dY=MISALIGNED) == INVALID
+    assert _backward(lib, dX=MISALIGNED) == INVALID
+    assert _backward(lib, ws=ctypes.c_void_p(P + 16)) == INVALID
+    assert _backward(lib, N=1020) == UNSUPPORTED                 # N % 8 != 0
+    assert _backward(lib, N=65536 + 8, K=16) == UNSUPPORTED      # N > 65536
+    assert _backward(lib, K=1000) == UNSUPPORTED                 # K % 16 != 0
+    need = lib.llmint8_backward_workspace_bytes(16, 1024, 1024)
+    assert _backward(lib, ws_bytes=need - 1) == WORKSPACE
+    # T == 0 returns OK before any HIP call
+    assert lib.llmint8_linear_backward_input(None, 0, 1024, ALIGNED, ALIGNED, 1024, None, None, 0,
+                                             None) == OK
+    t = lib.llmint8_linear_backward_input_timed
+    ev = (ctypes.c_void_p * 3)(P, P, P)
+    nk = ctypes.c_int(0)
+    args = [ALIGNED, 16, 1024, ALIGNED, ALIGNED, 1024, ALIGNED, ALIGNED, need, None]
+    assert t(*args, None, 3, ctypes.byref(nk)) == INVALID
+    assert t(*args, ev, 2, ctypes.byref(nk)) == INVALID           # two kernels need 3 events
+    d = lib.llmint8_dequantize_weight_t
+    assert d(None, ALIGNED, 64, 128, ALIGNED, None) == INVALID
+    assert d(ALIGNED, ALIGNED, 64, 128, None, None) == INVALID
+    assert d(ALIGNED, ALIGNED, 60, 128, ALIGNED, None) == UNSUPPORTED
+    assert d(ALIGNED, ALIGNED, 64, 128, MISALIGNED, None) == INVALID
+
+
+def test_backward_workspace_holds_the_transposed_weight(lib):
+    for T, K, N in [(1, 16, 8), (2048, 4096, 11008), (4096, 8192, 28672)]:
+        ws = lib.llmint8_backward_workspace_bytes(T, K, N)
+        assert 2 * N * K <= ws < 2 * N * K + 256
+    assert lib.llmint8_backward_workspace_bytes(16, 1024, 1020) == 0

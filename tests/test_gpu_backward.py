@@ -1,0 +1,141 @@
+"""GPU parity of the input gradient through the frozen int8 layer.
+
+Called through the C ABI and compared with the CPU oracle on the same seeded
+inputs: the dequantized, transposed weight bit-exact; dX within
+max-abs-relative 1e-3 (fp32 summation order is not pinned). Small and ragged
+shapes compare every element; the prefill-sized backward compares a seeded
+sample of rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+import mixed_precision_int8_amd as m8  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DX_TOL = 1e-3
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m8.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _weights(seed, N, K, sigma=0.02):
+    W = workloads.make_weight(workloads.rng_for(seed, 0), N, K, sigma)
+    Wq_ref, sW_ref = oracle.quantize_weight(W)
+    return _dev(Wq_ref), _dev(sW_ref), Wq_ref, sW_ref
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (200, 336), (8, 16), (1000, 1040)])
+def test_dequantize_transposed_bit_exact(N, K):
+    _say(f"dequantize_weight_t N={N} K={K}")
+    Wq, sW, Wq_ref, sW_ref = _weights(21, N, K)
+    WdT = _host(m8.llmint8_dequantize_weight_t(Wq, sW))
+    ref = oracle.dequantize_weight(Wq_ref, sW_ref).T
+    assert np.array_equal(WdT.view(np.uint16), ref.view(np.uint16))
+
+
+def test_dequantize_transposed_prefill_weight_bit_exact():
+    w = workloads.CONFIGS["prefill"]
+    _say(f"dequantize_weight_t N={w.N} K={w.K}")
+    W = workloads.make_weight(workloads.rng_for(w.seed, 0), w.N, w.K, w.sigma)
+    Wq_ref, sW_ref = oracle.quantize_weight(W)
+    WdT = _host(m8.llmint8_dequantize_weight_t(_dev(Wq_ref), _dev(sW_ref)))
+    ref = oracle.dequantize_weight(Wq_ref, sW_ref).T
+    assert np.array_equal(WdT.view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("T,K,N", [(16, 1024, 1024), (37, 336, 200), (300, 512, 264),
+                                   (1, 4096, 4096), (257, 144, 520), (5, 16, 8)])
+def test_backward_input_parity(T, K, N):
+    _say(f"backward_input T={T} K={K} N={N}")
+    Wq, sW, Wq_ref, sW_ref = _weights(22, N, K)
+    dY = workloads.make_output_grad(22, T, N)
+    dX = _host(m8.llmint8_linear_backward_input(_dev(dY), Wq, sW))
+    ref = oracle.linear_backward_input(dY, Wq_ref, sW_ref)
+    assert np.all(np.isfinite(dX.astype(np.float32)))
+    err = oracle.parity_error(dX, ref)
+    assert err <= DX_TOL, err
+
+
+@pytest.mark.parametrize("cfg", ["prefill", "large"])
+def test_backward_input_full_size_sampled_rows(cfg):
+    """Backward of the workload's layer at full size (the launch the benchmark
+    times); a seeded sample of 24 rows of dX is checked against the oracle."""
+    w = workloads.CONFIGS[cfg]
+    _say(f"backward_input {cfg} T={w.T} K={w.K} N={w.N}")
+    W = workloads.make_weight(workloads.rng_for(w.seed, 0), w.N, w.K, w.sigma)
+    Wq_ref, sW_ref = oracle.quantize_weight(W)
+    del W
+    dY = workloads.make_output_grad(w.seed, w.T, w.N)
+    dX = _host(m8.llmint8_linear_backward_input(_dev(dY), _dev(Wq_ref), _dev(sW_ref)))
+    rows = np.sort(np.random.default_rng(w.seed).choice(w.T, size=24, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, w.T - 1]]))
+    ref = oracle.linear_backward_input(dY[rows], Wq_ref, sW_ref)
+    assert np.all(np.isfinite(dX.astype(np.float32)))
+    err = oracle.parity_error(dX[rows], ref)
+    assert err <= DX_TOL, err
+
+
+def test_backward_input_edge_cases():
+    _say("backward_input edge cases")
+    Wq, sW, _, _ = _weights(23, 64, 128)
+    empty = m8.llmint8_linear_backward_input(_dev(np.zeros((0, 64), np.float16)), Wq, sW)
+    assert tuple(empty.shape) == (0, 128)
+    # N % 8 != 0 is rejected before anything runs
+    Wq2, sW2, _, _ = _weights(23, 60, 128)
+    with pytest.raises(m8.Llmint8Error) as e:
+        m8.llmint8_linear_backward_input(_dev(np.zeros((4, 60), np.float16)), Wq2, sW2)
+    assert e.value.status == -2
+    # a workspace smaller than required
+    small = torch.empty((256,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(m8.Llmint8Error) as e:
+        m8.llmint8_linear_backward_input(_dev(np.zeros((4, 64), np.float16)), Wq, sW,
+                                         workspace=small)
+    assert e.value.status == -3
+    # a zero gradient gives an exact zero
+    dX = _host(m8.llmint8_linear_backward_input(_dev(np.zeros((3, 64), np.float16)), Wq, sW))
+    assert not np.any(dX.astype(np.float32))
+
+
+def test_int8linear_autograd_uses_the_kernels():
+    """Int8Linear in autograd: X.grad is the library's input gradient, bit for bit."""
+    _say("Int8Linear autograd T=33 K=256 N=128")
+    rng = np.random.default_rng(24)
+    W = _dev((rng.standard_normal((128, 256)) * 0.05).astype(np.float16))
+    layer = m8.Int8Linear(W)
+    X = _dev(rng.standard_normal((33, 256)).astype(np.float16)).requires_grad_(True)
+    Y = layer(X)
+    dY = _dev(rng.standard_normal((33, 128)).astype(np.float16))
+    Y.backward(dY)
+    ref = m8.llmint8_linear_backward_input(dY, layer.Wq, layer.sW)
+    assert torch.equal(X.grad.view(torch.int16), ref.view(torch.int16))
+    Y2 = m8.llmint8_linear(X.detach(), layer.Wq, layer.sW, 6.0)
+    assert torch.equal(Y.detach().view(torch.int16), Y2.view(torch.int16))

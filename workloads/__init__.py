@@ -23,6 +23,10 @@ the draw order below, so either can be drawn without the other:
 4. (only when ``zero_rows > 0``) ``rows = sort(choice(T, zero_rows,
    replace=False))``; ``X[rows[:, None], cols[None, :]] = 0``.
 
+5. (input-gradient checks only) the output gradient comes from
+   ``Generator(PCG64(SeedSequence([seed, 2])))``:
+   ``dY = fp16(standard_normal((T, N), float32))``.
+
 Natural N(0,1) entries can still cross the threshold on their own; the set of
 outlier columns is always whatever the method computes, not ``cols``.
 """
@@ -33,7 +37,7 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "make_weight", "make_activations", "make"]
+__all__ = ["Workload", "CONFIGS", "make_weight", "make_activations", "make", "make_output_grad"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -106,8 +110,14 @@ def make_activations(rng: np.random.Generator, T: int, K: int, n_out: int, lo: f
     return x, cols, rows
 
 
+def make_output_grad(seed: int, T: int, N: int) -> np.ndarray:
+    """Step 5 of the recipe: fp16 output gradient [T, N] for the input-gradient checks."""
+    g = rng_for(seed, 2).standard_normal((T, N), dtype=np.float32)
+    return g.astype(np.float16)
+
+
 def rng_for(seed: int, stream: int) -> np.random.Generator:
-    """Stream 0 draws the weight, stream 1 the activations."""
+    """Stream 0 draws the weight, stream 1 the activations, stream 2 output gradients."""
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
 
 

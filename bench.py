@@ -9,8 +9,9 @@ and already resident in HBM when the timed region starts.
 
 Prints one JSON line. Besides the headline TOPS it carries the roofline of the
 dominant kernel (the int8 GEMM, timed with HIP events on the launch stream),
-the decode-shaped workload (T=8, K=N=4096) as GB/s against HBM bandwidth, and
-the CPU oracle timed on this host.
+the decode-shaped workload (T=8, K=N=4096) as GB/s against HBM bandwidth, the
+input gradient through the frozen layer at the prefill shape (fp16 TFLOP/s
+against the fp16 MFMA peak), and the CPU oracle timed on this host.
 """
 from __future__ import annotations
 
@@ -28,7 +29,10 @@ sys.path.insert(0, ROOT)
 METRIC = "LLM.int8() linear TOPS + % int8 MFMA peak (T=2048) / % HBM BW (T<=8)"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, tera-ops/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "kb_gemm_prefill_counters.txt")
+PROFILE_BWD_COUNTERS = os.path.join(ROOT, "profiles", "kg_backward_prefill_counters.txt")
+BWD_SOURCES = ("bwd.hip", "gemm_common.h", "device_util.h", "internal.h")
 
 
 def parse():
@@ -41,6 +45,7 @@ def parse():
     p.add_argument("--warmup-ms", type=float, default=30.0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-backward", action="store_true", help="skip the input-gradient workload")
     p.add_argument("--decode-copies", type=int, default=24,
                    help="distinct weight copies cycled in the decode timing (> last-level cache)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -49,24 +54,25 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=None) -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "device_util.h", "internal.h"):
+    for f in files or ("gemm.hip", "gemm_common.h", "device_util.h", "internal.h"):
         with open(os.path.join(ROOT, "mixed_precision_int8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(units_per_launch_bytes):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, or
-    None when absent or taken on different kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
+def committed_traffic(path=None, files=None, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when absent or taken on different kernel source."""
+    path = path or PROFILE_COUNTERS
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_COUNTERS).read()
+    text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m or m.group(1) != kernel_source_hash():
+    if not m or m.group(1) != kernel_source_hash(files):
         return None
-    m = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m = re.search(key + r":\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
 
 
@@ -137,7 +143,7 @@ def main():
     names = ["ka_scan", "ka_prepare", "kb_gemm"] if nk == 3 else ["kd_gemv"]
     gemm_ms = per_kernel[-1]
     achieved = ops / (gemm_ms * 1e-3) / 1e12
-    traffic = committed_traffic(None)
+    traffic = committed_traffic()
 
     result = {
         "metric": METRIC,
@@ -219,6 +225,69 @@ def main():
                             "weight_copies_cycled": len(copies), **dec}
         del copies
 
+    # ---- input gradient through the frozen layer, at the prefill layer's shape
+    if not args.no_backward:
+        dY_np = workloads.make_output_grad(w.seed, T, N)
+        dY = torch.from_numpy(dY_np).to(dev)
+        dX = torch.empty((T, K), dtype=torch.float16, device=dev)
+        wsb = torch.empty((m8.llmint8_backward_workspace_bytes(T, K, N),), dtype=torch.uint8,
+                          device=dev)
+
+        def bstep():
+            m8.llmint8_linear_backward_input(dY, Wq, sW, dX=dX, workspace=wsb)
+
+        bw = 0
+        w0 = time.perf_counter()
+        while bw < args.warmup or (time.perf_counter() - w0) * 1e3 < args.warmup_ms:
+            bstep()
+            bw += 1
+            if bw % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.steps):
+            bstep()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / args.steps
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for row in bev:          # torch creates the HIP event on its first record
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for row in bev:
+            m8.llmint8_linear_backward_input_timed(dY, Wq, sW, row, dX=dX, workspace=wsb)
+        torch.cuda.synchronize()
+        dq_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in bev]))
+        gf_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in bev]))
+        flops = 2.0 * T * N * K
+        dq_bytes = N * K + 4 * N + 2 * N * K
+        result["backward_input"] = {
+            "workload": "input gradient of the prefill layer: dY fp16 [2048, 11008] -> dX [2048, 4096]",
+            "T": T, "K": K, "N": N, "dtype": "f16 operands, f32 accumulation",
+            "warmup_steps_run": bw, "ms_per_call": round(bms, 5),
+            "TFLOPS": round(flops / (bms * 1e-3) / 1e12, 2),
+            "pct_fp16_peak": round(100.0 * flops / (bms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 2),
+            "kernels_ms": {"kg_dequant_t": round(dq_ms, 5), "kg_gemm_f16": round(gf_ms, 5)},
+            "roofline": {"bound": "mfma", "kernel": "kg_gemm_f16",
+                         "achieved": round(flops / (gf_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (gf_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+                         "traffic": committed_traffic(PROFILE_BWD_COUNTERS, BWD_SOURCES,
+                                                      "gemm_hbm_bytes_per_launch"),
+                         "algorithmic_ops_per_launch": flops,
+                         "avg_launch_ms": round(gf_ms, 5)},
+            "dequant_roofline": {"bound": "hbm", "kernel": "kg_dequant_t",
+                                 "achieved": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(dq_bytes / (dq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                 "bytes_per_launch": dq_bytes,
+                                 "traffic": committed_traffic(PROFILE_BWD_COUNTERS, BWD_SOURCES,
+                                                              "dequant_hbm_bytes_per_launch")},
+        }
+
     # ---- CPU oracle baseline on this host (bounded: the full prefill call once)
     if not args.no_cpu:
         import oracle
@@ -241,6 +310,19 @@ def main():
                                             f"{c1 - c0:.2f} s not counted"}
         result["parity"] = {"Y_max_abs_rel_err": oracle.parity_error(Yg, st.Y),
                             "outliers": st.count}
+        if "backward_input" in result:
+            # oracle input gradient on a seeded sample of rows: parity, and its CPU rate
+            rows = np.sort(np.random.default_rng(w.seed).choice(T, size=64, replace=False))
+            c3 = time.perf_counter()
+            dX_ref = oracle.linear_backward_input(dY_np[rows], Wq_ref, sW_ref)
+            c4 = time.perf_counter()
+            dXg = dX.cpu().numpy()[rows]
+            result["backward_input"]["parity"] = {
+                "dX_max_abs_rel_err_sampled_rows": oracle.parity_error(dXg, dX_ref), "rows": len(rows)}
+            result["backward_input"]["cpu_oracle"] = {
+                "value": round(2.0 * len(rows) * N * K / (c4 - c3) / 1e12, 5), "unit": "TFLOPS",
+                "cores": threads, "sample": f"{len(rows)} rows of dX, {c4 - c3:.2f} s "
+                                            "(weight dequantization included)"}
 
     print(json.dumps(result), flush=True)
 

@@ -50,6 +50,15 @@ reason, in the design notes):
       ``dX = fp16(dY . Wdeq)``: fp16 operands, a wide accumulation, one
       rounding to fp16.
 
+* Q1  blockwise 8-bit codec: a flat tensor is cut into blocks of ``block``
+      consecutive elements (the last one may be shorter); each block keeps its
+      absolute maximum ``a`` (fp32) and codes ``q = rne(fl32(x * fl32(127 / a)))``
+      (the R4 rule per block; a zero block gives codes 0 and a = 0).
+      Dequantization is ``fl32(fl32(q * a) / 127)`` (the R7 form), returned in
+      the input's dtype (fp16 rounds once more). The pages give neither the
+      block size nor a code table: the block size is the caller's, and the
+      code is the same symmetric linear one as the rest of the method.
+
 The backward sources:
 
 * [HFQ-T]  "Hugging Face Quantization with bitsandbytes ...", the quick
@@ -61,6 +70,15 @@ The backward sources:
 * [DCT-S]  "bitsandbytes" (mining glossary), "Where it fits in the stack":
            weights are dequantized for each operation instead of being
            computed on directly.
+
+The blockwise codec sources:
+
+* [DCT-P]  "bitsandbytes" (mining glossary), "What it provides": weights are
+           quantized in blocks, each with its own scaling factor, so that one
+           outlier only affects its own block.
+* [HYS-O]  "bitsandbytes: GPU-Accelerated Inference and Training at Lower Bit
+           Depths", the 8-bit optimizers: block-wise quantization shrinks the
+           optimizer states.
 
 Precision: every quantization step is the fp32 operation named (NumPy float32
 arithmetic is IEEE round-to-nearest-even); ``np.rint`` is round-half-to-even.
@@ -77,7 +95,7 @@ import numpy as np
 __all__ = [
     "quantize_weight", "outlier_columns", "pack_bitmap", "quantize_activations",
     "int8_matmul", "outlier_operands", "output", "linear", "Stages", "parity_error",
-    "dequantize_weight", "linear_backward_input",
+    "dequantize_weight", "linear_backward_input", "quantize_blockwise", "dequantize_blockwise",
 ]
 
 _F32_127 = np.float32(127.0)
@@ -261,3 +279,31 @@ def linear_backward_input(dY16: np.ndarray, Wq: np.ndarray, sW: np.ndarray) -> n
     dX64 = np.asarray(dY16).astype(np.float64) @ Wd.astype(np.float64)
     with np.errstate(over="ignore"):
         return dX64.astype(np.float16)
+
+
+def quantize_blockwise(x: np.ndarray, block: int):
+    """Blockwise absmax int8 quantization of a flat tensor ([DCT-P], [HYS-O]; Q1).
+
+    ``x`` is fp16 or fp32 (any shape, taken flat). Returns ``(q int8[n],
+    absmax fp32[ceil(n / block)])``; block ``b`` covers elements
+    ``[b * block, min((b + 1) * block, n))``.
+    """
+    flat = np.asarray(x).reshape(-1)
+    n = flat.shape[0]
+    nb = -(-n // block)
+    v32 = flat.astype(np.float32)
+    pad = nb * block - n
+    blocks = np.concatenate([v32, np.zeros(pad, np.float32)]).reshape(nb, block)
+    a = _absmax_rows(blocks)
+    q = _quantize_rows(blocks, a).reshape(-1)[:n]
+    return q.astype(np.int8), a
+
+
+def dequantize_blockwise(q: np.ndarray, absmax: np.ndarray, block: int, dtype=np.float16):
+    """Inverse of ``quantize_blockwise`` (Q1): ``fl32(fl32(q * a) / 127)``, then
+    rounded to ``dtype`` (fp16 or fp32)."""
+    q32 = np.asarray(q).reshape(-1).astype(np.float32)
+    n = q32.shape[0]
+    a = np.repeat(np.asarray(absmax, dtype=np.float32), block)[:n]
+    v = (q32 * a) / _F32_127
+    return v.astype(dtype)

@@ -140,3 +140,21 @@ def backward_input(dY, Wq, sW):
             row.append(f16_of_fraction(acc))
         dX.append(row)
     return Wdeq, dX
+
+
+def quantize_blockwise(vals, block):
+    """Blockwise absmax codes of a flat list of fp16- or fp32-valued floats."""
+    q, absmax = [], []
+    for b0 in range(0, len(vals), block):
+        codes, m = quantize_vector(vals[b0:b0 + block])
+        q.extend(codes)
+        absmax.append(m)
+    return q, absmax
+
+
+def dequantize_blockwise(q, absmax, block, to_fp16):
+    out = []
+    for i, c in enumerate(q):
+        v = f32(f32(c * absmax[i // block]) / 127.0)
+        out.append(f16(v) if to_fp16 else v)
+    return out

@@ -188,6 +188,34 @@ LLMINT8_API llmint8_status llmint8_linear_backward_input_timed(
 LLMINT8_API llmint8_status llmint8_dequantize_weight_t(const int8_t* Wq, const float* sW, int64_t N,
                                                        int64_t K, void* WdT, void* stream);
 
+/* Element types of the blockwise codec. */
+#define LLMINT8_DTYPE_F16 0 /* IEEE binary16 */
+#define LLMINT8_DTYPE_F32 1 /* IEEE binary32 */
+
+/*
+ * Blockwise 8-bit codec ("bitsandbytes" glossary, "What it provides": a
+ * tensor is quantized in blocks that each carry their own scaling factor, so
+ * an outlier only affects its own block; "bitsandbytes: GPU-Accelerated
+ * Inference and Training at Lower Bit Depths", 8-bit optimizers: block-wise
+ * quantization of optimizer states). The flat tensor x of n elements is cut
+ * into blocks of `block` consecutive elements (the last may be shorter):
+ *   absmax[b] = max |x| over block b                       (fp32, exact)
+ *   q[i]      = rne(fl32(x[i] * fl32(127 / absmax[b])))    (0 for a zero block)
+ *   x'[i]     = fl32(fl32(q[i] * absmax[b]) / 127), rounded to dtype
+ *   x, out  device, dtype LLMINT8_DTYPE_F16 or _F32, n elements, 16-byte aligned
+ *   q       device int8 [n], 16-byte aligned
+ *   absmax  device fp32 [ceil(n / block)]
+ * Requires block a power of two in [64, 4096], n % 16 == 0 and n <= 2^30
+ * (LLMINT8_ERR_UNSUPPORTED otherwise); n == 0 is a valid no-op. Inputs must be
+ * finite. Results are bit-exact.
+ */
+LLMINT8_API llmint8_status llmint8_quantize_blockwise(const void* x, int dtype, int64_t n,
+                                                      int64_t block, int8_t* q, float* absmax,
+                                                      void* stream);
+LLMINT8_API llmint8_status llmint8_dequantize_blockwise(const int8_t* q, const float* absmax,
+                                                        int64_t n, int64_t block, void* out,
+                                                        int dtype, void* stream);
+
 /* Largest T the fused GEMV route accepts for this K (0 if none). */
 LLMINT8_API int llmint8_gemv_max_rows(int64_t K);
 

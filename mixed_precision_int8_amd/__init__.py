@@ -17,19 +17,23 @@ __all__ = [
     "llmint8_linear", "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
     "llmint8_status_string", "llmint8_backward_workspace_bytes", "llmint8_dequantize_weight_t",
     "llmint8_linear_backward_input", "llmint8_linear_backward_input_timed", "Int8Linear",
-    "EXPORTED_SYMBOLS",
+    "LLMINT8_DTYPE_F16", "LLMINT8_DTYPE_F32", "llmint8_quantize_blockwise",
+    "llmint8_dequantize_blockwise", "EXPORTED_SYMBOLS",
 ]
 
 LLMINT8_PATH_AUTO = 0
 LLMINT8_PATH_GEMM = 1
 LLMINT8_PATH_GEMV = 2
+LLMINT8_DTYPE_F16 = 0
+LLMINT8_DTYPE_F32 = 1
 
 EXPORTED_SYMBOLS = (
     "llmint8_quantize_weight", "llmint8_workspace_bytes", "llmint8_linear",
     "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
     "llmint8_status_string", "llmint8_last_hip_error", "llmint8_backward_workspace_bytes",
     "llmint8_dequantize_weight_t", "llmint8_linear_backward_input",
-    "llmint8_linear_backward_input_timed",
+    "llmint8_linear_backward_input_timed", "llmint8_quantize_blockwise",
+    "llmint8_dequantize_blockwise",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +88,10 @@ def load_library():
     lib.llmint8_linear_backward_input_timed.argtypes = bwd + [ctypes.POINTER(_vp), ctypes.c_int,
                                                               ctypes.POINTER(ctypes.c_int)]
     lib.llmint8_linear_backward_input_timed.restype = ctypes.c_int
+    lib.llmint8_quantize_blockwise.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _vp]
+    lib.llmint8_quantize_blockwise.restype = ctypes.c_int
+    lib.llmint8_dequantize_blockwise.argtypes = [_vp, _vp, _i64, _i64, _vp, ctypes.c_int, _vp]
+    lib.llmint8_dequantize_blockwise.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
     lib.llmint8_gemv_max_rows.restype = ctypes.c_int
     lib.llmint8_status_string.argtypes = [ctypes.c_int]
@@ -292,6 +300,54 @@ def llmint8_linear_backward_input_timed(dY, Wq, sW, events, dX=None, workspace=N
                                                    ctypes.byref(nk)),
            "llmint8_linear_backward_input_timed")
     return dX
+
+
+def _codec_dtype(dtype):
+    import torch
+    if dtype == torch.float16:
+        return LLMINT8_DTYPE_F16
+    if dtype == torch.float32:
+        return LLMINT8_DTYPE_F32
+    raise ValueError(f"blockwise codec: fp16 or fp32 only, got {dtype}")
+
+
+def llmint8_quantize_blockwise(x, block: int = 4096, q=None, absmax=None, stream=None):
+    """Blockwise int8 codes of a contiguous fp16/fp32 tensor (taken flat):
+    (q int8 [n], absmax fp32 [ceil(n / block)])."""
+    import torch
+    lib = load_library()
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.is_contiguous()):
+        raise ValueError("x: expected a contiguous CUDA tensor")
+    n = x.numel()
+    nb = -(-n // block)
+    if q is None:
+        q = torch.empty((n,), dtype=torch.int8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty((nb,), dtype=torch.float32, device=x.device)
+    _need(q, torch.int8, (n,), "q")
+    _need(absmax, torch.float32, (nb,), "absmax")
+    _check(lib.llmint8_quantize_blockwise(_ptr(x), _codec_dtype(x.dtype), n, block, _ptr(q),
+                                          _ptr(absmax), _stream(stream, x.device)),
+           "llmint8_quantize_blockwise")
+    return q, absmax
+
+
+def llmint8_dequantize_blockwise(q, absmax, block: int = 4096, dtype=None, out=None, stream=None):
+    """Inverse of llmint8_quantize_blockwise: fp16 (default) or fp32 [n]."""
+    import torch
+    lib = load_library()
+    n = q.numel()
+    nb = -(-n // block)
+    _need(q, torch.int8, (n,), "q")
+    _need(absmax, torch.float32, (nb,), "absmax")
+    if out is None:
+        out = torch.empty((n,), dtype=dtype or torch.float16, device=q.device)
+    if not (out.is_cuda and out.is_contiguous() and out.numel() == n):
+        raise ValueError("out: expected a contiguous CUDA tensor of n elements")
+    _check(lib.llmint8_dequantize_blockwise(_ptr(q), _ptr(absmax), n, block, _ptr(out),
+                                            _codec_dtype(out.dtype), _stream(stream, q.device)),
+           "llmint8_dequantize_blockwise")
+    return out
 
 
 def _autograd_function():

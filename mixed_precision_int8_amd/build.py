@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libllmint8.so")
 
-SOURCES = ["prep.hip", "gemm.hip", "gemv.hip", "bwd.hip", "api.cpp"]
+SOURCES = ["prep.hip", "gemm.hip", "gemv.hip", "bwd.hip", "blockwise.hip", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -290,6 +290,38 @@ llmint8_status llmint8_linear_backward_input_timed(const void* dY, int64_t T, in
                             n_events, kernels_launched);
 }
 
+static llmint8_status check_blockwise(int dtype, int64_t n, int64_t block) {
+  if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_F32) return LLMINT8_ERR_INVALID_ARG;
+  if (n < 0 || block <= 0) return LLMINT8_ERR_INVALID_ARG;
+  if (block > 4096 || !blockwise_supported((int)block) || n % 16 != 0 || n > (int64_t)1 << 30)
+    return LLMINT8_ERR_UNSUPPORTED;
+  return LLMINT8_OK;
+}
+
+llmint8_status llmint8_quantize_blockwise(const void* x, int dtype, int64_t n, int64_t block,
+                                          int8_t* q, float* absmax, void* stream) {
+  llmint8_status st = check_blockwise(dtype, n, block);
+  if (st != LLMINT8_OK) return st;
+  if (n == 0) return LLMINT8_OK;
+  if (!x || !q || !absmax) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(absmax, 4)) return LLMINT8_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_blockwise(x, dtype == LLMINT8_DTYPE_F32, (int)n, (int)block, q,
+                                              absmax, device_cu_count(),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+llmint8_status llmint8_dequantize_blockwise(const int8_t* q, const float* absmax, int64_t n,
+                                            int64_t block, void* out, int dtype, void* stream) {
+  llmint8_status st = check_blockwise(dtype, n, block);
+  if (st != LLMINT8_OK) return st;
+  if (n == 0) return LLMINT8_OK;
+  if (!q || !absmax || !out) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(absmax, 4)) return LLMINT8_ERR_INVALID_ARG;
+  return hip_status(launch_dequantize_blockwise(q, absmax, (int)n, (int)block, out,
+                                                dtype == LLMINT8_DTYPE_F32, device_cu_count(),
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int llmint8_gemv_max_rows(int64_t K) {
   if (K <= 0 || K % 16 != 0 || K > kMaxK) return 0;
   return gemv_max_rows((int)K);

@@ -101,5 +101,10 @@ hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uin
                             hipStream_t stream);
 hipError_t launch_gemm_f16(const BwdArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_f16_variant(const BwdArgs& a, int variant, hipStream_t stream);
+bool blockwise_supported(int block);  // a power of two in [64, 4096]
+hipError_t launch_quantize_blockwise(const void* x, bool f32, int n, int block, int8_t* q,
+                                     float* absmax, int num_cus, hipStream_t stream);
+hipError_t launch_dequantize_blockwise(const int8_t* q, const float* absmax, int n, int block,
+                                       void* out, bool f32, int num_cus, hipStream_t stream);
 
 }  // namespace llmint8

@@ -177,3 +177,21 @@ def test_backward_workspace_holds_the_transposed_weight(lib):
         ws = lib.llmint8_backward_workspace_bytes(T, K, N)
         assert 2 * N * K <= ws < 2 * N * K + 256
     assert lib.llmint8_backward_workspace_bytes(16, 1024, 1020) == 0
+
+
+def test_blockwise_argument_errors(lib):
+    qb, dq = lib.llmint8_quantize_blockwise, lib.llmint8_dequantize_blockwise
+    F16, F32 = m8.LLMINT8_DTYPE_F16, m8.LLMINT8_DTYPE_F32
+    assert qb(ALIGNED, 7, 4096, 64, ALIGNED, ALIGNED, None) == INVALID         # unknown dtype
+    assert qb(None, F16, 4096, 64, ALIGNED, ALIGNED, None) == INVALID
+    assert qb(ALIGNED, F16, 4096, 64, None, ALIGNED, None) == INVALID
+    assert qb(ALIGNED, F32, 4096, 64, ALIGNED, None, None) == INVALID
+    assert qb(ALIGNED, F16, -16, 64, ALIGNED, ALIGNED, None) == INVALID
+    assert qb(MISALIGNED, F16, 4096, 64, ALIGNED, ALIGNED, None) == INVALID
+    assert qb(ALIGNED, F16, 4104, 64, ALIGNED, ALIGNED, None) == UNSUPPORTED    # n % 16 != 0
+    assert qb(ALIGNED, F16, 4096, 96, ALIGNED, ALIGNED, None) == UNSUPPORTED    # not a power of two
+    assert qb(ALIGNED, F16, 4096, 8192, ALIGNED, ALIGNED, None) == UNSUPPORTED  # block > 4096
+    assert qb(None, F16, 0, 64, None, None, None) == OK                         # empty: no-op
+    assert dq(None, ALIGNED, 4096, 64, ALIGNED, F16, None) == INVALID
+    assert dq(ALIGNED, ALIGNED, 4096, 64, MISALIGNED, F32, None) == INVALID
+    assert dq(ALIGNED, ALIGNED, 4096, 32, ALIGNED, F32, None) == UNSUPPORTED

@@ -27,6 +27,11 @@ the draw order below, so either can be drawn without the other:
    ``Generator(PCG64(SeedSequence([seed, 2])))``:
    ``dY = fp16(standard_normal((T, N), float32))``.
 
+6. (blockwise codec only) an fp32 tensor shaped like an optimizer state comes
+   from ``Generator(PCG64(SeedSequence([seed, 3])))``:
+   ``s = float32(1e-3 * standard_normal(n))``, then every 1000th element times
+   50 (isolated large values, one per few blocks).
+
 Natural N(0,1) entries can still cross the threshold on their own; the set of
 outlier columns is always whatever the method computes, not ``cols``.
 """
@@ -37,7 +42,8 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "make_weight", "make_activations", "make", "make_output_grad"]
+__all__ = ["Workload", "CONFIGS", "make_weight", "make_activations", "make", "make_output_grad",
+           "make_state"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -116,8 +122,15 @@ def make_output_grad(seed: int, T: int, N: int) -> np.ndarray:
     return g.astype(np.float16)
 
 
+def make_state(seed: int, n: int) -> np.ndarray:
+    """Step 6 of the recipe: an fp32 optimizer-state-like tensor of n elements."""
+    s = rng_for(seed, 3).standard_normal(n, dtype=np.float32) * np.float32(1e-3)
+    s[::1000] *= np.float32(50.0)
+    return s
+
+
 def rng_for(seed: int, stream: int) -> np.random.Generator:
-    """Stream 0 draws the weight, stream 1 the activations, stream 2 output gradients."""
+    """Stream 0 draws the weight, 1 the activations, 2 output gradients, 3 codec states."""
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
 
 

@@ -11,7 +11,8 @@ Prints one JSON line. Besides the headline TOPS it carries the roofline of the
 dominant kernel (the int8 GEMM, timed with HIP events on the launch stream),
 the decode-shaped workload (T=8, K=N=4096) as GB/s against HBM bandwidth, the
 input gradient through the frozen layer at the prefill shape (fp16 TFLOP/s
-against the fp16 MFMA peak), and the CPU oracle timed on this host.
+against the fp16 MFMA peak), the blockwise 8-bit codec (GB/s against HBM
+bandwidth) and the CPU oracle timed on this host.
 """
 from __future__ import annotations
 
@@ -46,6 +47,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-backward", action="store_true", help="skip the input-gradient workload")
+    p.add_argument("--no-codec", action="store_true", help="skip the blockwise codec workload")
     p.add_argument("--decode-copies", type=int, default=24,
                    help="distinct weight copies cycled in the decode timing (> last-level cache)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -287,6 +289,50 @@ def main():
                                  "traffic": committed_traffic(PROFILE_BWD_COUNTERS, BWD_SOURCES,
                                                               "dequant_hbm_bytes_per_launch")},
         }
+
+    # ---- blockwise 8-bit codec: the prefill weight (fp16) and an optimizer-state
+    # sized fp32 tensor, at the smallest and largest supported block
+    if not args.no_codec:
+        codec = {}
+        tensors = {"f16_weight": Wd.reshape(-1),
+                   "f32_state": torch.from_numpy(workloads.make_state(w.seed, N * K)).to(dev)}
+        copies = 3   # three of everything: the working set exceeds the 256 MB MALL
+        for name, t in tensors.items():
+            n = t.numel()
+            el = t.element_size()
+            ins = [t.clone() for _ in range(copies)]
+            for block in (64, 4096):
+                nb = -(-n // block)
+                qs = [torch.empty((n,), dtype=torch.int8, device=dev) for _ in range(copies)]
+                ams = [torch.empty((nb,), dtype=torch.float32, device=dev) for _ in range(copies)]
+                outs = [torch.empty_like(t) for _ in range(copies)]
+                fns = {"quantize": lambda i: m8.llmint8_quantize_blockwise(ins[i], block, q=qs[i],
+                                                                            absmax=ams[i]),
+                       "dequantize": lambda i: m8.llmint8_dequantize_blockwise(qs[i], ams[i], block,
+                                                                              out=outs[i])}
+                nbytes = {"quantize": n * el + n + 4 * nb, "dequantize": n + 4 * nb + n * el}
+                for op, fn in fns.items():
+                    for i in range(max(args.warmup, 10)):
+                        fn(i % copies)
+                    torch.cuda.synchronize()
+                    c0e = torch.cuda.Event(enable_timing=True)
+                    c1e = torch.cuda.Event(enable_timing=True)
+                    reps = max(args.steps // 2, 10) // copies * copies
+                    c0e.record(stream)
+                    for i in range(reps):
+                        fn(i % copies)
+                    c1e.record(stream)
+                    torch.cuda.synchronize()
+                    us = c0e.elapsed_time(c1e) / reps * 1e3
+                    gbs = nbytes[op] / (us * 1e-6) / 1e9
+                    codec[f"{name}_block{block}_{op}"] = {
+                        "us_per_call": round(us, 2), "GB_per_s": round(gbs, 1),
+                        "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2), "bytes": nbytes[op]}
+            del ins, qs, ams, outs
+        result["blockwise_codec"] = {"workload": f"{N * K} elements (the prefill weight, and an fp32 "
+                                                 "state of the same size)", "bound": "hbm",
+                                     "copies_cycled": copies, "peak_GB_per_s": PEAK_HBM_GBS, **codec}
+        del tensors
 
     # ---- CPU oracle baseline on this host (bounded: the full prefill call once)
     if not args.no_cpu:

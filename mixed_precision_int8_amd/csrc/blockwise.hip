@@ -8,11 +8,12 @@
 //   q     = rne(fl32(x * fl32(127 / a[b])))           (0 for a zero block)
 //   x'    = fl32(fl32(q * a[b]) / 127), rounded to the input dtype
 //
-// HBM-bound. A wavefront covers 64 / LPB blocks at a time with LPB lanes per
-// block and VPL 16-byte vectors per lane kept in registers: one pass over the
-// data, a segmented lane reduction of the block maximum, the codes written as
-// 8- or 4-byte pieces. Reads use buffer loads, so a ragged last block reads
-// zeros past the end without a branch.
+// HBM-bound. Quantization: a wavefront covers 64 / LPB blocks at a time with
+// LPB lanes per block and VPL 16-byte vectors per lane kept in registers: one
+// pass over the data, a segmented lane reduction of the block maximum, the
+// codes written as 8- or 4-byte pieces. Reads use buffer loads, so a ragged
+// last block reads zeros past the end without a branch. Dequantization is a
+// flat grid-stride loop over output vectors.
 #include "device_util.h"
 #include "internal.h"
 
@@ -97,52 +98,42 @@ __global__ __launch_bounds__(256) void kq_blockwise(const void* __restrict__ x, 
   }
 }
 
-template <bool F32, int LPB, int VPL>
+// Dequantization needs no reduction, so it runs flat: a grid-stride loop over
+// 16-byte output vectors, each reading its codes (8 or 4 bytes) and its
+// block's maximum.
+template <bool F32>
 __global__ __launch_bounds__(256) void kdq_blockwise(const int8_t* __restrict__ q,
-                                                     const float* __restrict__ absmax, int n, int nb,
-                                                     void* __restrict__ out) {
+                                                     const float* __restrict__ absmax, int n,
+                                                     int block_shift, void* __restrict__ out) {
   constexpr int E = F32 ? 4 : 8;
-  constexpr int VPB = LPB * VPL;
-  constexpr int BPI = 64 / LPB;
-  const int lane = threadIdx.x & 63;
-  const int sub = lane / LPB, li = lane % LPB;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
   const int nvec = n / E;
-  for (int b0 = wave * BPI; b0 < nb; b0 += nwaves * BPI) {
-    const int b = b0 + sub;
-    if (b >= nb) continue;
-    const float a = absmax[b];
+  for (int vi = blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += gridDim.x * 256) {
+    const float a = absmax[(vi * E) >> block_shift];
+    if (F32) {
+      const uint32_t c = reinterpret_cast<const uint32_t*>(q)[vi];
+      uint4 o;
+      uint32_t* po = &o.x;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int vi = b * VPB + i * LPB + li;
-      if (vi >= nvec) continue;
-      if (F32) {
-        const uint32_t c = reinterpret_cast<const uint32_t*>(q)[vi];
-        uint4 o;
-        uint32_t* po = &o.x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = (float)(int)(int8_t)((c >> (8 * j)) & 0xffu) * a;
-          po[j] = __builtin_bit_cast(uint32_t, div127(p));
-        }
-        reinterpret_cast<uint4*>(out)[vi] = o;
-      } else {
-        const uint2 c = reinterpret_cast<const uint2*>(q)[vi];
-        const uint32_t w[2] = {c.x, c.y};
-        uint32_t h[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = (float)(int)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xffu) * a;
-          h[j] = float_to_half_bits(div127(p));
-        }
-        uint4 o;
-        o.x = h[0] | (h[1] << 16);
-        o.y = h[2] | (h[3] << 16);
-        o.z = h[4] | (h[5] << 16);
-        o.w = h[6] | (h[7] << 16);
-        reinterpret_cast<uint4*>(out)[vi] = o;
+      for (int j = 0; j < 4; ++j) {
+        const float p = (float)(int)(int8_t)((c >> (8 * j)) & 0xffu) * a;
+        po[j] = __builtin_bit_cast(uint32_t, div127(p));
       }
+      reinterpret_cast<uint4*>(out)[vi] = o;
+    } else {
+      const uint2 c = reinterpret_cast<const uint2*>(q)[vi];
+      const uint32_t w[2] = {c.x, c.y};
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = (float)(int)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xffu) * a;
+        h[j] = float_to_half_bits(div127(p));
+      }
+      uint4 o;
+      o.x = h[0] | (h[1] << 16);
+      o.y = h[2] | (h[3] << 16);
+      o.z = h[4] | (h[5] << 16);
+      o.w = h[6] | (h[7] << 16);
+      reinterpret_cast<uint4*>(out)[vi] = o;
     }
   }
 }
@@ -191,19 +182,19 @@ hipError_t launch_quantize_blockwise(const void* x, bool f32, int n, int block, 
 #undef L
   return hipGetLastError();
 }
+#undef LLMINT8_BW_CASES
 
 hipError_t launch_dequantize_blockwise(const int8_t* q, const float* absmax, int n, int block,
                                        void* out, bool f32, int num_cus, hipStream_t stream) {
-  const int nb = (n + block - 1) / block;
-#define L(F, LPB, VPL)                                                                        \
-  hipLaunchKernelGGL((kdq_blockwise<F, (LPB), (VPL)>), dim3(codec_grid(nb, 64 / (LPB), num_cus)), \
-                     dim3(256), 0, stream, q, absmax, n, nb, out)
+  const int shift = log2_exact(block);
+  if (shift < 0) return hipErrorInvalidValue;
+  const int nvec = n / (f32 ? 4 : 8);
+  const int grid = max(1, min((nvec + 255) / 256, num_cus * 32));
   if (f32) {
-    LLMINT8_BW_CASES(true, 4)
+    hipLaunchKernelGGL(kdq_blockwise<true>, dim3(grid), dim3(256), 0, stream, q, absmax, n, shift, out);
   } else {
-    LLMINT8_BW_CASES(false, 8)
+    hipLaunchKernelGGL(kdq_blockwise<false>, dim3(grid), dim3(256), 0, stream, q, absmax, n, shift, out);
   }
-#undef L
   return hipGetLastError();
 }
 

@@ -50,6 +50,14 @@ reason, in the design notes):
       ``dX = fp16(dY . Wdeq)``: fp16 operands, a wide accumulation, one
       rounding to fp16.
 
+* B2  bf16 activations: with ``dtype="bf16"`` X, the bias and Y are bfloat16
+      (carried here as uint16 bit patterns). Every bf16 value is exact in
+      fp32, so the outlier test and the quantization are the same fp32
+      operations as for fp16; the outlier operand ``Wd`` is rounded to bf16
+      and the 16-bit product takes bf16 operands; Y is rounded once to bf16
+      (round to nearest even).
+* B3  bias: an optional vector [N] in the activation dtype, added to the sum
+      before the single final rounding.
 * Q1  blockwise 8-bit codec: a flat tensor is cut into blocks of ``block``
       consecutive elements (the last one may be shorter); each block keeps its
       absolute maximum ``a`` (fp32) and codes ``q = rne(fl32(x * fl32(127 / a)))``
@@ -58,6 +66,16 @@ reason, in the design notes):
       the input's dtype (fp16 rounds once more). The pages give neither the
       block size nor a code table: the block size is the caller's, and the
       code is the same symmetric linear one as the rest of the method.
+
+The bf16 and bias sources:
+
+* [HFQ-5]  "Hugging Face Quantization with bitsandbytes ...", section 5
+           "Storage Precision vs. Compute Precision": the storage type of the
+           weights and the compute type (bfloat16 preferred where the hardware
+           has it, else float16) are separate choices.
+* [HYS-L]  "bitsandbytes: GPU-Accelerated Inference and Training at Lower Bit
+           Depths": ``Linear8bitLt`` is a drop-in replacement for a linear
+           layer (which carries a bias).
 
 The backward sources:
 
@@ -96,9 +114,50 @@ __all__ = [
     "quantize_weight", "outlier_columns", "pack_bitmap", "quantize_activations",
     "int8_matmul", "outlier_operands", "output", "linear", "Stages", "parity_error",
     "dequantize_weight", "linear_backward_input", "quantize_blockwise", "dequantize_blockwise",
+    "bf16_bits_to_f32", "f32_to_bf16_bits", "f64_to_bf16_bits",
 ]
 
 _F32_127 = np.float32(127.0)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> fp32 values (exact: bf16 is the top half of fp32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    b = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    return ((b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+
+
+def f64_to_bf16_bits(x64: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns with one rounding to 8 significant bits,
+    nearest even (finite inputs; beyond the bf16 range gives +-inf)."""
+    x = np.asarray(x64, dtype=np.float64)
+    m, e = np.frexp(x)                               # x = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                          # bf16 subnormals share the 2**-133 quantum
+    r = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)  # 8 significant bits, half to even
+    with np.errstate(over="ignore"):
+        r32 = r.astype(np.float32)                   # exact unless beyond fp32 range (-> inf)
+    big = np.abs(r) > float(np.float32(3.3895313892515355e38))
+    r32 = np.where(big, np.copysign(np.float32(np.inf), r32), r32)
+    return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _to_f32(A, dtype: str) -> np.ndarray:
+    """Activation-dtype array (fp16 values, or bf16 bit patterns) -> exact fp32."""
+    A = np.asarray(A)
+    if dtype == "bf16":
+        assert A.dtype == np.uint16
+        return bf16_bits_to_f32(A)
+    assert dtype == "f16" and A.dtype == np.float16
+    return A.astype(np.float32)
+
+
+def _to_f64(A, dtype: str) -> np.ndarray:
+    return _to_f32(A, dtype).astype(np.float64)
 
 
 def _absmax_rows(v32: np.ndarray) -> np.ndarray:
@@ -119,30 +178,30 @@ def _quantize_rows(v32: np.ndarray, absmax: np.ndarray) -> np.ndarray:
     return q.astype(np.int8)
 
 
-def quantize_weight(W16: np.ndarray):
+def quantize_weight(W16: np.ndarray, dtype: str = "f16"):
     """Vector-wise weight quantization at load time ([HYS]; [DCT] introduction; R4-R6).
 
-    ``W16`` fp16 [N, K] -> (``Wq`` int8 [N, K], ``sW`` fp32 [N]) with
-    ``sW[n] = max_k |W[n, k]|`` (exact: an fp16 value) and
-    ``Wq[n, k] = rne(fl32(W[n, k] * fl32(127 / sW[n])))``.
+    ``W16`` fp16 [N, K] (or bf16 bit patterns with ``dtype="bf16"``) ->
+    (``Wq`` int8 [N, K], ``sW`` fp32 [N]) with ``sW[n] = max_k |W[n, k]|``
+    (exact: a 16-bit value) and ``Wq[n, k] = rne(fl32(W[n, k] * fl32(127 / sW[n])))``.
     """
     W = np.asarray(W16)
-    assert W.dtype == np.float16 and W.ndim == 2
-    W32 = W.astype(np.float32)
+    assert W.ndim == 2
+    W32 = _to_f32(W, dtype)
     b = _absmax_rows(W32)
     return _quantize_rows(W32, b), b
 
 
-def outlier_columns(X16: np.ndarray, threshold: float) -> np.ndarray:
+def outlier_columns(X16: np.ndarray, threshold: float, dtype: str = "f16") -> np.ndarray:
     """Outlier feature dimensions ([HFQ-2]; [HFQ-3]; R1, R2, R9).
 
     Returns a bool mask [K]: column h is an outlier when some row has
     ``|X[t, h]| >= threshold`` (fp32 comparison).
     """
     X = np.asarray(X16)
-    assert X.dtype == np.float16 and X.ndim == 2
+    assert X.ndim == 2
     thr = np.float32(threshold)
-    return np.any(np.abs(X.astype(np.float32)) >= thr, axis=0)
+    return np.any(np.abs(_to_f32(X, dtype)) >= thr, axis=0)
 
 
 def pack_bitmap(mask: np.ndarray) -> np.ndarray:
@@ -154,13 +213,13 @@ def pack_bitmap(mask: np.ndarray) -> np.ndarray:
     return words
 
 
-def quantize_activations(X16: np.ndarray, outlier_mask: np.ndarray):
+def quantize_activations(X16: np.ndarray, outlier_mask: np.ndarray, dtype: str = "f16"):
     """Row-wise (vector-wise) quantization of the non-outlier part of X ([HYS]; R3-R5).
 
     ``a[t] = max over non-outlier columns of |X[t, k]|``;
     ``Xq[t, k] = 0`` on outlier columns, else ``rne(fl32(X[t, k] * fl32(127 / a[t])))``.
     """
-    X32 = np.asarray(X16).astype(np.float32)
+    X32 = _to_f32(X16, dtype)
     kept = np.where(outlier_mask[None, :], np.float32(0), X32)
     a = _absmax_rows(kept)
     return _quantize_rows(kept, a), a
@@ -178,27 +237,36 @@ def int8_matmul(Xq: np.ndarray, Wq: np.ndarray) -> np.ndarray:
     return Ci.astype(np.int32)
 
 
-def outlier_operands(X16: np.ndarray, Wq: np.ndarray, sW: np.ndarray, idx: np.ndarray):
-    """16-bit operands of the outlier product ([HYS]; [HFQ-2]; R7, R8).
+def outlier_operands(X16: np.ndarray, Wq: np.ndarray, sW: np.ndarray, idx: np.ndarray,
+                     dtype: str = "f16"):
+    """16-bit operands of the outlier product ([HYS]; [HFQ-2]; R7, R8, B2).
 
-    ``Xo = X[:, idx]`` (fp16, exact copy);
-    ``Wd[n, j] = fp16(fl32(fl32(Wq[n, idx[j]] * sW[n]) / 127))``.
+    ``Xo = X[:, idx]`` (exact copy, activation dtype);
+    ``Wd[n, j] = r16(fl32(fl32(Wq[n, idx[j]] * sW[n]) / 127))`` with r16 the
+    rounding to the activation dtype.
     """
     Xo = np.asarray(X16)[:, idx]
     q32 = Wq[:, idx].astype(np.float32)
-    Wd = ((q32 * sW[:, None].astype(np.float32)) / _F32_127).astype(np.float16)
+    d32 = (q32 * sW[:, None].astype(np.float32)) / _F32_127
+    Wd = f32_to_bf16_bits(d32) if dtype == "bf16" else d32.astype(np.float16)
     return Xo, Wd
 
 
-def output(C: np.ndarray, aX: np.ndarray, sW: np.ndarray, Xo: np.ndarray, Wd: np.ndarray):
-    """Recombination, converted back to 16-bit at the end ([HFQ-2]).
+def output(C: np.ndarray, aX: np.ndarray, sW: np.ndarray, Xo: np.ndarray, Wd: np.ndarray,
+           dtype: str = "f16", bias: np.ndarray | None = None):
+    """Recombination, converted back to 16-bit at the end ([HFQ-2]; B2, B3).
 
-    ``Y = fp16( C * a[t] * b[n] / 127**2  +  Xo @ Wd.T )`` evaluated in float64.
+    ``Y = r16( C * a[t] * b[n] / 127**2  +  Xo @ Wd.T  +  bias[n] )`` evaluated
+    in float64 and rounded once to the activation dtype.
     """
     Y64 = C.astype(np.float64) * aX.astype(np.float64)[:, None] \
         * sW.astype(np.float64)[None, :] / 16129.0
     if Xo.shape[1]:
-        Y64 = Y64 + Xo.astype(np.float64) @ Wd.astype(np.float64).T
+        Y64 = Y64 + _to_f64(Xo, dtype) @ _to_f64(Wd, dtype).T
+    if bias is not None:
+        Y64 = Y64 + _to_f64(bias, dtype)[None, :]
+    if dtype == "bf16":
+        return f64_to_bf16_bits(Y64)
     with np.errstate(over="ignore"):               # beyond fp16 range: +-inf, like any fp16 cast
         return Y64.astype(np.float16)
 
@@ -221,21 +289,24 @@ class Stages:
 
 
 def linear(X16: np.ndarray, Wq: np.ndarray, sW: np.ndarray, threshold: float,
-           rows: np.ndarray | None = None, with_outputs: bool = True) -> Stages:
+           rows: np.ndarray | None = None, with_outputs: bool = True, dtype: str = "f16",
+           bias: np.ndarray | None = None) -> Stages:
     """The whole forward: outlier set, quantized activations, int8 product, output.
 
     ``rows`` restricts C and Y to a subset of rows (the outlier set and row
     statistics are still taken over all of X, as the method defines them).
+    ``dtype`` is the activation type ("f16", or "bf16" with X, bias and Y as
+    bf16 bit patterns); ``bias`` an optional [N] vector of that type.
     """
-    mask = outlier_columns(X16, threshold)
+    mask = outlier_columns(X16, threshold, dtype)
     idx = np.flatnonzero(mask).astype(np.int32)
-    Xq, aX = quantize_activations(X16, mask)
-    Xo, Wd = outlier_operands(X16, Wq, sW, idx)
+    Xq, aX = quantize_activations(X16, mask, dtype)
+    Xo, Wd = outlier_operands(X16, Wq, sW, idx, dtype)
     C = Y = None
     if with_outputs:
         sel = slice(None) if rows is None else rows
         C = int8_matmul(Xq[sel], Wq)
-        Y = output(C, aX[sel], sW, Xo[sel], Wd)
+        Y = output(C, aX[sel], sW, Xo[sel], Wd, dtype, bias)
     return Stages(mask, pack_bitmap(mask), idx, Xq, aX, C, Xo, Wd, Y)
 
 

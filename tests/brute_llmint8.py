@@ -55,6 +55,32 @@ def f16_of_fraction(q: Fraction) -> float:
     return sign * float(val)
 
 
+def bf16_of_fraction(q: Fraction) -> float:
+    """Correct round-half-even of an exact rational to bfloat16 (8 significant
+    bits, the fp32 exponent range; finite results only)."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                     # subnormals share the 2**-133 quantum
+    quantum = Fraction(2) ** (e - 7)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * float(fl * quantum)
+
+
+def bf16(x: float) -> float:
+    return bf16_of_fraction(Fraction(x))
+
+
 def rne(x: float) -> int:
     return int(round(x))
 
@@ -74,11 +100,14 @@ def quantize_vector(vals):
     return q, m
 
 
-def forward(X, W, thr):
-    """X: T x K list of fp16-valued floats; W: N x K; thr: float.
+def forward(X, W, thr, bf16_io=False, bias=None):
+    """X: T x K list of fp16-valued floats (bf16-valued with ``bf16_io``);
+    W: N x K; thr: float; bias: optional list of N 16-bit values.
 
     Returns dict with outlier list, Wq, sW, Xq, aX, C, Y (Y as floats).
     """
+    r16 = bf16 if bf16_io else f16
+    r16_exact = bf16_of_fraction if bf16_io else f16_of_fraction
     T = len(X)
     N = len(W)
     K = len(W[0]) if N else (len(X[0]) if T else 0)
@@ -104,7 +133,7 @@ def forward(X, W, thr):
         Xq.append(q)
         aX.append(a)
     C = [[sum(Xq[t][k] * Wq[n][k] for k in range(K)) for n in range(N)] for t in range(T)]
-    Wd = [[f16(f32(f32(Wq[n][h] * sW[n]) / 127.0)) for h in outl] for n in range(N)]
+    Wd = [[r16(f32(f32(Wq[n][h] * sW[n]) / 127.0)) for h in outl] for n in range(N)]
     Y = []
     for t in range(T):
         row = []
@@ -112,7 +141,9 @@ def forward(X, W, thr):
             exact = Fraction(C[t][n]) * Fraction(aX[t]) * Fraction(sW[n]) / 16129
             for j, h in enumerate(outl):
                 exact += Fraction(X[t][h]) * Fraction(Wd[n][j])
-            row.append((exact, f16_of_fraction(exact)))
+            if bias is not None:
+                exact += Fraction(bias[n])
+            row.append((exact, r16_exact(exact)))
         Y.append(row)
     return {"outliers": outl, "Wq": Wq, "sW": sW, "Xq": Xq, "aX": aX, "C": C, "Wd": Wd,
             "Y": [[y for _, y in r] for r in Y], "Y_exact": [[e for e, _ in r] for r in Y]}

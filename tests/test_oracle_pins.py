@@ -411,20 +411,20 @@ def test_planted_mistakes_are_caught(monkeypatch):
 
     mutants = {
         "strict threshold": ("outlier_columns",
-                             lambda X, thr: np.any(np.abs(X.astype(np.float32)) > np.float32(thr), axis=0)),
+                             lambda X, thr, *_: np.any(np.abs(X.astype(np.float32)) > np.float32(thr), axis=0)),
         "half away from zero": ("_quantize_rows", lambda v, a: (
             lambda s: np.where((a > 0)[:, None],
                                np.clip(np.sign(v * s[:, None]) * np.floor(np.abs(v * s[:, None]) + 0.5), -127, 127),
                                0).astype(np.int8))(np.where(a > 0, np.float32(127) / np.where(a > 0, a, 1), 0).astype(np.float32))),
-        "outlier term dropped": ("output", lambda C, aX, sW, Xo, Wd: orig["output"](C, aX, sW, Xo[:, :0], Wd[:, :0])),
-        "outliers kept in absmax": ("quantize_activations", lambda X, m: (
+        "outlier term dropped": ("output", lambda C, aX, sW, Xo, Wd, *r: orig["output"](C, aX, sW, Xo[:, :0], Wd[:, :0], *r)),
+        "outliers kept in absmax": ("quantize_activations", lambda X, m, *_: (
             lambda q_a: (np.where(m[None, :], 0, q_a[0]).astype(np.int8), q_a[1]))(
                 orig["_quantize_rows"](X.astype(np.float32), np.abs(X.astype(np.float32)).max(axis=1).astype(np.float32)))),
-        "row scale ignored": ("output", lambda C, aX, sW, Xo, Wd: orig["output"](
-            C, np.full_like(aX, 127), sW, Xo, Wd)),
-        "column scale squared": ("output", lambda C, aX, sW, Xo, Wd: orig["output"](
-            C, aX, sW * sW, Xo, Wd)),
-        "dequant without /127": ("outlier_operands", lambda X, Wq, sW, idx: (
+        "row scale ignored": ("output", lambda C, aX, sW, Xo, Wd, *r: orig["output"](
+            C, np.full_like(aX, 127), sW, Xo, Wd, *r)),
+        "column scale squared": ("output", lambda C, aX, sW, Xo, Wd, *r: orig["output"](
+            C, aX, sW * sW, Xo, Wd, *r)),
+        "dequant without /127": ("outlier_operands", lambda X, Wq, sW, idx, *_: (
             np.asarray(X)[:, idx], (Wq[:, idx].astype(np.float32) * sW[:, None]).astype(np.float16))),
         "sign flipped in product": ("int8_matmul", lambda Xq, Wq: -orig["int8_matmul"](Xq, Wq)),
     }

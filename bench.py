@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-backward", action="store_true", help="skip the input-gradient workload")
     p.add_argument("--no-codec", action="store_true", help="skip the blockwise codec workload")
+    p.add_argument("--no-bf16", action="store_true", help="skip the bf16 + bias workload")
     p.add_argument("--decode-copies", type=int, default=24,
                    help="distinct weight copies cycled in the decode timing (> last-level cache)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -227,6 +228,69 @@ def main():
                             "weight_copies_cycled": len(copies), **dec}
         del copies
 
+    # ---- bf16 activations with a fused bias: the prefill and decode shapes again
+    if not args.no_bf16:
+        Wb_np = workloads.as_bf16_input(W)
+        Xb_np = workloads.as_bf16_input(X)
+        bias_np = workloads.make_bias(w.seed, N, bf16=True)
+
+        def _bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        Wqb, sWb = m8.llmint8_quantize_weight_ex(_bf(Wb_np))
+        Xb, biasb = _bf(Xb_np), _bf(bias_np)
+        Yb = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+
+        def timed_calls(fn, reps, warm):
+            # warm by count and by time, as for the headline: clocks ramp up
+            i = 0
+            t_w = time.perf_counter()
+            while i < warm or (time.perf_counter() - t_w) * 1e3 < args.warmup_ms:
+                fn(i)
+                i += 1
+                if i % 16 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            q0 = torch.cuda.Event(enable_timing=True)
+            q1 = torch.cuda.Event(enable_timing=True)
+            q0.record(stream)
+            for i in range(reps):
+                fn(i)
+            q1.record(stream)
+            torch.cuda.synchronize()
+            return q0.elapsed_time(q1) / reps
+
+        pms = timed_calls(lambda i: m8.llmint8_linear_ex(Xb, Wqb, sWb, thr, bias=biasb, Y=Yb,
+                                                         workspace=ws),
+                          args.steps, max(args.warmup, 20))
+        bf = {"prefill": {"T": T, "K": K, "N": N, "ms_per_call": round(pms, 5),
+                          "TOPS": round(ops / (pms * 1e-3) / 1e12, 2),
+                          "pct_int8_peak": round(100.0 * ops / (pms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+                          "fp16_no_bias_ms_per_call": round(ms_per_step, 5)}}
+        if not args.no_decode:
+            wd = workloads.CONFIGS["decode"]
+            Wd3, X3, _, _ = workloads.make(wd, T=1)
+            Wq3, sW3 = m8.llmint8_quantize_weight_ex(_bf(workloads.as_bf16_input(Wd3)))
+            cps = [(Wq3.clone(), sW3.clone()) for _ in range(args.decode_copies)]
+            X3b = _bf(workloads.as_bf16_input(X3))
+            b3 = _bf(workloads.make_bias(wd.seed, wd.N, bf16=True))
+            Y3 = torch.empty((1, wd.N), dtype=torch.bfloat16, device=dev)
+            ws3 = torch.empty((m8.llmint8_workspace_bytes(1, wd.K, wd.N),), dtype=torch.uint8,
+                              device=dev)
+            reps = max(args.steps, 2 * len(cps))
+            dms = timed_calls(lambda i: m8.llmint8_linear_ex(X3b, cps[i % len(cps)][0],
+                                                             cps[i % len(cps)][1], wd.threshold,
+                                                             bias=b3, Y=Y3, workspace=ws3),
+                              reps, args.warmup)
+            nbytes = wd.N * wd.K + 4 * wd.N + 2 * wd.K + 2 * wd.N + 2 * wd.N
+            bf["decode_T1"] = {"K": wd.K, "N": wd.N, "us_per_call": round(dms * 1e3, 3),
+                               "GB_per_s": round(nbytes / (dms * 1e-3) / 1e9, 1),
+                               "pct_hbm": round(100.0 * nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                               "algorithmic_bytes": nbytes, "weight_copies_cycled": len(cps)}
+            del cps
+        result["bf16_bias"] = {"workload": "bf16 X, bias and Y; the prefill and decode layers",
+                               "timing": "whole calls between two events", **bf}
+
     # ---- input gradient through the frozen layer, at the prefill layer's shape
     if not args.no_backward:
         dY_np = workloads.make_output_grad(w.seed, T, N)
@@ -356,6 +420,16 @@ def main():
                                             f"{c1 - c0:.2f} s not counted"}
         result["parity"] = {"Y_max_abs_rel_err": oracle.parity_error(Yg, st.Y),
                             "outliers": st.count}
+        if "bf16_bias" in result:
+            rows = np.sort(np.random.default_rng(w.seed + 1).choice(T, size=16, replace=False))
+            Wqb_ref, sWb_ref = oracle.quantize_weight(Wb_np, "bf16")
+            stb = oracle.linear(Xb_np, Wqb_ref, sWb_ref, thr, rows=rows, dtype="bf16", bias=bias_np)
+            Ybg = Yb.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+            result["bf16_bias"]["parity"] = {
+                "Y_max_abs_rel_err_sampled_rows": oracle.parity_error(
+                    oracle.bf16_bits_to_f32(Ybg), oracle.bf16_bits_to_f32(stb.Y)),
+                "Y_bit_identical_fraction": float(np.mean(Ybg == stb.Y)), "rows": len(rows),
+                "weight_codes_identical": bool(np.array_equal(Wqb.cpu().numpy(), Wqb_ref))}
         if "backward_input" in result:
             # oracle input gradient on a seeded sample of rows: parity, and its CPU rate
             rows = np.sort(np.random.default_rng(w.seed).choice(T, size=64, replace=False))

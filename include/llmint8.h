@@ -188,9 +188,11 @@ LLMINT8_API llmint8_status llmint8_linear_backward_input_timed(
 LLMINT8_API llmint8_status llmint8_dequantize_weight_t(const int8_t* Wq, const float* sW, int64_t N,
                                                        int64_t K, void* WdT, void* stream);
 
-/* Element types of the blockwise codec. */
-#define LLMINT8_DTYPE_F16 0 /* IEEE binary16 */
-#define LLMINT8_DTYPE_F32 1 /* IEEE binary32 */
+/* Element types: activations (the _ex entry points: F16 or BF16) and the
+ * blockwise codec (F16 or F32). */
+#define LLMINT8_DTYPE_F16  0 /* IEEE binary16 */
+#define LLMINT8_DTYPE_F32  1 /* IEEE binary32 */
+#define LLMINT8_DTYPE_BF16 2 /* bfloat16: the top 16 bits of an IEEE binary32 */
 
 /*
  * Blockwise 8-bit codec ("bitsandbytes" glossary, "What it provides": a
@@ -215,6 +217,38 @@ LLMINT8_API llmint8_status llmint8_quantize_blockwise(const void* x, int dtype, 
 LLMINT8_API llmint8_status llmint8_dequantize_blockwise(const int8_t* q, const float* absmax,
                                                         int64_t n, int64_t block, void* out,
                                                         int dtype, void* stream);
+
+/*
+ * The entry points above for a chosen activation type and an optional bias
+ * ("Hugging Face Quantization with bitsandbytes ...", section 5: storage type
+ * and compute type are separate choices, bfloat16 preferred where the hardware
+ * has it; "bitsandbytes: GPU-Accelerated Inference ...": Linear8bitLt replaces
+ * a linear layer, which carries a bias).
+ *   dtype  LLMINT8_DTYPE_F16 or LLMINT8_DTYPE_BF16: the type of W (for
+ *          quantize_weight_ex), of X, bias and Y (for linear_ex). Every bf16
+ *          value is exact in fp32, so the outlier test and the quantization
+ *          are the same fp32 operations; with bf16 the outlier operand Wd is
+ *          rounded to bf16, the 16-bit product takes bf16 operands and Y is
+ *          rounded once to bf16 (nearest even).
+ *   bias   device [N] in the activation type (2-byte aligned), or NULL; it is
+ *          added to the fp32 sum before the single rounding of Y:
+ *          Y = r16( C * a[t] * b[n] / 127^2 + X[:,O] . Wd^T + bias[n] )
+ * Other arguments and rules as for llmint8_quantize_weight / llmint8_linear /
+ * llmint8_linear_debug; an unknown dtype is LLMINT8_ERR_INVALID_ARG.
+ */
+LLMINT8_API llmint8_status llmint8_quantize_weight_ex(const void* W, int dtype, int64_t N, int64_t K,
+                                                      int8_t* Wq, float* sW, void* stream);
+LLMINT8_API llmint8_status llmint8_linear_ex(const void* X, int dtype, int64_t T, int64_t K,
+                                             const int8_t* Wq, const float* sW, int64_t N,
+                                             float threshold, const void* bias, void* Y,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+LLMINT8_API llmint8_status llmint8_linear_debug_ex(const void* X, int dtype, int64_t T, int64_t K,
+                                                   const int8_t* Wq, const float* sW, int64_t N,
+                                                   float threshold, const void* bias, void* Y,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   void* stream, int path, uint32_t* outlier_bitmap,
+                                                   int32_t* outlier_idx, int32_t* outlier_count,
+                                                   int8_t* Xq, float* aX, int32_t* C);
 
 /* Largest T the fused GEMV route accepts for this K (0 if none). */
 LLMINT8_API int llmint8_gemv_max_rows(int64_t K);

@@ -18,7 +18,8 @@ __all__ = [
     "llmint8_status_string", "llmint8_backward_workspace_bytes", "llmint8_dequantize_weight_t",
     "llmint8_linear_backward_input", "llmint8_linear_backward_input_timed", "Int8Linear",
     "LLMINT8_DTYPE_F16", "LLMINT8_DTYPE_F32", "llmint8_quantize_blockwise",
-    "llmint8_dequantize_blockwise", "EXPORTED_SYMBOLS",
+    "llmint8_dequantize_blockwise", "EXPORTED_SYMBOLS", "LLMINT8_DTYPE_BF16",
+    "llmint8_quantize_weight_ex", "llmint8_linear_ex", "llmint8_linear_debug_ex",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -26,6 +27,7 @@ LLMINT8_PATH_GEMM = 1
 LLMINT8_PATH_GEMV = 2
 LLMINT8_DTYPE_F16 = 0
 LLMINT8_DTYPE_F32 = 1
+LLMINT8_DTYPE_BF16 = 2
 
 EXPORTED_SYMBOLS = (
     "llmint8_quantize_weight", "llmint8_workspace_bytes", "llmint8_linear",
@@ -33,7 +35,8 @@ EXPORTED_SYMBOLS = (
     "llmint8_status_string", "llmint8_last_hip_error", "llmint8_backward_workspace_bytes",
     "llmint8_dequantize_weight_t", "llmint8_linear_backward_input",
     "llmint8_linear_backward_input_timed", "llmint8_quantize_blockwise",
-    "llmint8_dequantize_blockwise",
+    "llmint8_dequantize_blockwise", "llmint8_quantize_weight_ex", "llmint8_linear_ex",
+    "llmint8_linear_debug_ex",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +95,14 @@ def load_library():
     lib.llmint8_quantize_blockwise.restype = ctypes.c_int
     lib.llmint8_dequantize_blockwise.argtypes = [_vp, _vp, _i64, _i64, _vp, ctypes.c_int, _vp]
     lib.llmint8_dequantize_blockwise.restype = ctypes.c_int
+    lib.llmint8_quantize_weight_ex.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _vp]
+    lib.llmint8_quantize_weight_ex.restype = ctypes.c_int
+    lin_ex = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64, ctypes.c_float, _vp, _vp, _vp,
+              ctypes.c_size_t, _vp]
+    lib.llmint8_linear_ex.argtypes = lin_ex
+    lib.llmint8_linear_ex.restype = ctypes.c_int
+    lib.llmint8_linear_debug_ex.argtypes = lin_ex + [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.llmint8_linear_debug_ex.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
     lib.llmint8_gemv_max_rows.restype = ctypes.c_int
     lib.llmint8_status_string.argtypes = [ctypes.c_int]
@@ -164,6 +175,34 @@ def llmint8_quantize_weight(W, Wq=None, sW=None, stream=None):
     return Wq, sW
 
 
+def _act_dtype(dtype):
+    import torch
+    if dtype == torch.float16:
+        return LLMINT8_DTYPE_F16
+    if dtype == torch.bfloat16:
+        return LLMINT8_DTYPE_BF16
+    raise ValueError(f"activations: fp16 or bf16 only, got {dtype}")
+
+
+def llmint8_quantize_weight_ex(W, Wq=None, sW=None, stream=None):
+    """W fp16 or bf16 [N, K] (CUDA) -> (Wq int8 [N, K], sW fp32 [N])."""
+    import torch
+    lib = load_library()
+    N, K = W.shape
+    code = _act_dtype(W.dtype)
+    _need(W, W.dtype, (N, K), "W")
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if sW is None:
+        sW = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(sW, torch.float32, (N,), "sW")
+    _check(lib.llmint8_quantize_weight_ex(_ptr(W), code, N, K, _ptr(Wq), _ptr(sW),
+                                          _stream(stream, W.device)),
+           "llmint8_quantize_weight_ex")
+    return Wq, sW
+
+
 def _workspace(T, K, N, device, workspace):
     import torch
     need = llmint8_workspace_bytes(T, K, N)
@@ -172,16 +211,19 @@ def _workspace(T, K, N, device, workspace):
     return workspace
 
 
-def _linear_args(X, Wq, sW, threshold, Y, workspace):
+def _linear_args(X, Wq, sW, threshold, Y, workspace, dtype=None, bias=None):
     import torch
     T, K = X.shape
     N = Wq.shape[0]
-    _need(X, torch.float16, (T, K), "X")
+    dtype = dtype or torch.float16
+    _need(X, dtype, (T, K), "X")
     _need(Wq, torch.int8, (N, K), "Wq")
     _need(sW, torch.float32, (N,), "sW")
+    if bias is not None:
+        _need(bias, dtype, (N,), "bias")
     if Y is None:
-        Y = torch.empty((T, N), dtype=torch.float16, device=X.device)
-    _need(Y, torch.float16, (T, N), "Y")
+        Y = torch.empty((T, N), dtype=dtype, device=X.device)
+    _need(Y, dtype, (T, N), "Y")
     workspace = _workspace(T, K, N, X.device, workspace)
     thr = float(threshold)
     if thr == math.inf:
@@ -199,15 +241,24 @@ def llmint8_linear(X, Wq, sW, threshold: float = 6.0, Y=None, workspace=None, st
     return Y
 
 
-def llmint8_linear_debug(X, Wq, sW, threshold: float = 6.0, path: int = LLMINT8_PATH_AUTO,
-                         Y=None, workspace=None, stream=None, want_C: bool = True):
-    """Forward plus the intermediates of the same kernels: dict of tensors."""
-    import torch
+def llmint8_linear_ex(X, Wq, sW, threshold: float = 6.0, bias=None, Y=None, workspace=None,
+                      stream=None):
+    """Y [T, N] = LLM.int8() forward of X [T, K] (fp16 or bf16; Y and the optional
+    bias [N] take the type of X) with (Wq, sW)."""
     lib = load_library()
-    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
-    dev = X.device
+    code = _act_dtype(X.dtype)
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias)
+    _check(lib.llmint8_linear_ex(_ptr(X), code, T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(bias),
+                                 _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream, X.device)),
+           "llmint8_linear_ex")
+    return Y
+
+
+def _debug_outputs(T, K, N, dev, want_C):
+    import torch
     KW = (K + 31) // 32
-    out = {
+    return {
         "bitmap": torch.zeros((KW,), dtype=torch.int32, device=dev),
         "idx": torch.full((K,), -1, dtype=torch.int32, device=dev),
         "count": torch.full((1,), -1, dtype=torch.int32, device=dev),
@@ -215,6 +266,34 @@ def llmint8_linear_debug(X, Wq, sW, threshold: float = 6.0, path: int = LLMINT8_
         "aX": torch.zeros((T,), dtype=torch.float32, device=dev),
         "C": torch.zeros((T, N), dtype=torch.int32, device=dev) if want_C else None,
     }
+
+
+def llmint8_linear_debug_ex(X, Wq, sW, threshold: float = 6.0, bias=None,
+                            path: int = LLMINT8_PATH_AUTO, Y=None, workspace=None, stream=None,
+                            want_C: bool = True):
+    """llmint8_linear_ex plus the intermediates of the same kernels: dict of tensors."""
+    lib = load_library()
+    code = _act_dtype(X.dtype)
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias)
+    dev = X.device
+    out = _debug_outputs(T, K, N, dev, want_C)
+    _check(lib.llmint8_linear_debug_ex(_ptr(X), code, T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(bias),
+                                       _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream, dev), int(path), _ptr(out["bitmap"]),
+                                       _ptr(out["idx"]), _ptr(out["count"]), _ptr(out["Xq"]),
+                                       _ptr(out["aX"]), _ptr(out["C"])),
+           "llmint8_linear_debug_ex")
+    out["Y"] = Y
+    return out
+
+
+def llmint8_linear_debug(X, Wq, sW, threshold: float = 6.0, path: int = LLMINT8_PATH_AUTO,
+                         Y=None, workspace=None, stream=None, want_C: bool = True):
+    """Forward plus the intermediates of the same kernels: dict of tensors."""
+    lib = load_library()
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
+    dev = X.device
+    out = _debug_outputs(T, K, N, dev, want_C)
     _check(lib.llmint8_linear_debug(_ptr(X), T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(Y), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream, dev), int(path),
                                     _ptr(out["bitmap"]), _ptr(out["idx"]), _ptr(out["count"]),
@@ -360,12 +439,13 @@ def _autograd_function():
         @staticmethod
         def forward(ctx, X2, layer):
             ctx.layer = layer
-            return llmint8_linear(X2, layer.Wq, layer.sW, layer.threshold,
-                                  workspace=layer._workspace(X2.shape[0], X2.device))
+            return layer._forward(X2)
 
         @staticmethod
         def backward(ctx, dY):
             layer = ctx.layer
+            if dY.dtype != torch.float16:
+                raise NotImplementedError("Int8Linear backward: fp16 gradients only")
             dX = llmint8_linear_backward_input(dY.contiguous(), layer.Wq, layer.sW)
             return dX, None
 
@@ -375,25 +455,42 @@ def _autograd_function():
 _FN = None
 
 
+def _fp16():
+    import torch
+    return torch.float16
+
+
 class Int8Linear:
-    """Drop-in int8 replacement of a bias-free fp16 linear layer.
+    """Drop-in int8 replacement of an fp16 or bf16 linear layer, with or without bias.
 
     The weight is quantized once at construction ("bitsandbytes" glossary,
     introduction: quantization happens when the model loads); ``forward`` runs
     the LLM.int8() forward ("Hugging Face Quantization with bitsandbytes",
-    sections 2 and 3) and, for inputs that require a gradient, registers the
-    input-gradient kernels as its backward (same page, section 6: the int8
-    weights stay frozen while an adapter on top is trained).
+    sections 2 and 3; section 5 for bf16 as the compute type) with the bias
+    added before the output's rounding, and, for fp16 inputs that require a
+    gradient, registers the input-gradient kernels as its backward (same page,
+    section 6: the int8 weights stay frozen while an adapter on top is trained).
+    Activations, bias and output take the weight's type.
     """
 
-    def __init__(self, weight, threshold: float = 6.0):
+    def __init__(self, weight, threshold: float = 6.0, bias=None):
         self.threshold = float(threshold)
         self.out_features, self.in_features = weight.shape
-        self.Wq, self.sW = llmint8_quantize_weight(weight.contiguous())
+        self.dtype = weight.dtype
+        self.Wq, self.sW = llmint8_quantize_weight_ex(weight.contiguous())
+        self.bias = None if bias is None else bias.detach().to(weight.dtype).contiguous()
         self._ws = None
 
     def memory_bytes(self) -> int:
-        return self.Wq.numel() + self.sW.numel() * 4
+        extra = 0 if self.bias is None else self.bias.numel() * 2
+        return self.Wq.numel() + self.sW.numel() * 4 + extra
+
+    def _forward(self, X2):
+        ws = self._workspace(X2.shape[0], X2.device)
+        if self.dtype == _fp16() and self.bias is None:
+            return llmint8_linear(X2, self.Wq, self.sW, self.threshold, workspace=ws)
+        return llmint8_linear_ex(X2, self.Wq, self.sW, self.threshold, bias=self.bias,
+                                 workspace=ws)
 
     def _workspace(self, T, device):
         import torch
@@ -413,8 +510,7 @@ class Int8Linear:
                 _FN = _autograd_function()
             Y = _FN.apply(X2, self)
         else:
-            Y = llmint8_linear(X2, self.Wq, self.sW, self.threshold,
-                               workspace=self._workspace(X2.shape[0], X2.device))
+            Y = self._forward(X2)
         return Y.reshape(*shape[:-1], self.out_features)
 
     __call__ = forward

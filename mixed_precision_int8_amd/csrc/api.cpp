@@ -52,9 +52,12 @@ int device_cu_count() {
 
 llmint8_status validate_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
                                const float* sW, int64_t N, float threshold, void* Y,
-                               void* workspace, size_t workspace_bytes) {
+                               void* workspace, size_t workspace_bytes, int dtype,
+                               const void* bias) {
   llmint8_status st = check_sizes(T, K, N);
   if (st != LLMINT8_OK) return st;
+  if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_BF16) return LLMINT8_ERR_INVALID_ARG;
+  if (bias && !aligned(bias, 2)) return LLMINT8_ERR_INVALID_ARG;
   if (std::isnan(threshold) || !(threshold > 0.0f)) return LLMINT8_ERR_INVALID_ARG;
   if (!Wq || !sW) return LLMINT8_ERR_INVALID_ARG;
   if (!aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
@@ -66,7 +69,8 @@ llmint8_status validate_linear(const void* X, int64_t T, int64_t K, const int8_t
 }
 
 LinearArgs make_args(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sW,
-                     int64_t N, float threshold, void* Y, void* workspace) {
+                     int64_t N, float threshold, void* Y, void* workspace, int dtype,
+                     const void* bias) {
   const WsLayout L = ws_layout(T, K, N);
   char* ws = static_cast<char*>(workspace);
   LinearArgs a{};
@@ -78,6 +82,8 @@ LinearArgs make_args(const void* X, int64_t T, int64_t K, const int8_t* Wq, cons
   a.K = (int)K;
   a.N = (int)N;
   a.thr = threshold;
+  a.bf16 = dtype == LLMINT8_DTYPE_BF16 ? 1 : 0;
+  a.bias = static_cast<const uint16_t*>(bias);
   a.parts = reinterpret_cast<uint32_t*>(ws + L.parts);
   a.bitmap = reinterpret_cast<uint32_t*>(ws + L.bitmap);
   a.count = reinterpret_cast<int32_t*>(ws + L.count);
@@ -100,9 +106,11 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
                           size_t workspace_bytes, void* stream_ptr, int path,
                           uint32_t* dbg_bitmap, int32_t* dbg_idx, int32_t* dbg_count,
                           int8_t* dbg_Xq, float* dbg_aX, int32_t* dbg_C,
-                          void* const* events, int n_events, int* kernels_launched) {
+                          void* const* events, int n_events, int* kernels_launched,
+                          int dtype = LLMINT8_DTYPE_F16, const void* bias = nullptr) {
   if (kernels_launched) *kernels_launched = 0;
-  llmint8_status st = validate_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes);
+  llmint8_status st = validate_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes,
+                                      dtype, bias);
   if (st != LLMINT8_OK) return st;
   if (path != LLMINT8_PATH_AUTO && path != LLMINT8_PATH_GEMM && path != LLMINT8_PATH_GEMV)
     return LLMINT8_ERR_INVALID_ARG;
@@ -113,7 +121,7 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   if (T == 0) return LLMINT8_OK;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  LinearArgs a = make_args(X, T, K, Wq, sW, N, threshold, Y, workspace);
+  LinearArgs a = make_args(X, T, K, Wq, sW, N, threshold, Y, workspace, dtype, bias);
   a.dbg_C = dbg_C;
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
@@ -207,14 +215,20 @@ llmint8_status run_backward_input(const void* dY, int64_t T, int64_t K, const in
 
 extern "C" {
 
-llmint8_status llmint8_quantize_weight(const void* W, int64_t N, int64_t K, int8_t* Wq, float* sW,
-                                       void* stream) {
+llmint8_status llmint8_quantize_weight_ex(const void* W, int dtype, int64_t N, int64_t K, int8_t* Wq,
+                                          float* sW, void* stream) {
   llmint8_status st = check_sizes(0, K, N);
   if (st != LLMINT8_OK) return st;
+  if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_BF16) return LLMINT8_ERR_INVALID_ARG;
   if (!W || !Wq || !sW) return LLMINT8_ERR_INVALID_ARG;
   if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
   return hip_status(launch_quantize_weight(static_cast<const uint16_t*>(W), (int)N, (int)K, Wq, sW,
-                                           static_cast<hipStream_t>(stream)));
+                                           dtype == LLMINT8_DTYPE_BF16, static_cast<hipStream_t>(stream)));
+}
+
+llmint8_status llmint8_quantize_weight(const void* W, int64_t N, int64_t K, int8_t* Wq, float* sW,
+                                       void* stream) {
+  return llmint8_quantize_weight_ex(W, LLMINT8_DTYPE_F16, N, K, Wq, sW, stream);
 }
 
 size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N) {
@@ -228,6 +242,29 @@ llmint8_status llmint8_linear(const void* X, int64_t T, int64_t K, const int8_t*
   return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream,
                     LLMINT8_PATH_AUTO, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                     nullptr, 0, nullptr);
+}
+
+llmint8_status llmint8_linear_ex(const void* X, int dtype, int64_t T, int64_t K, const int8_t* Wq,
+                                 const float* sW, int64_t N, float threshold, const void* bias,
+                                 void* Y, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream,
+                    LLMINT8_PATH_AUTO, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, 0, nullptr, dtype, bias);
+}
+
+llmint8_status llmint8_linear_debug_ex(const void* X, int dtype, int64_t T, int64_t K,
+                                       const int8_t* Wq, const float* sW, int64_t N, float threshold,
+                                       const void* bias, void* Y, void* workspace,
+                                       size_t workspace_bytes, void* stream, int path,
+                                       uint32_t* outlier_bitmap, int32_t* outlier_idx,
+                                       int32_t* outlier_count, int8_t* Xq, float* aX, int32_t* C) {
+  if ((outlier_bitmap && !aligned(outlier_bitmap, 4)) || (outlier_idx && !aligned(outlier_idx, 4)) ||
+      (outlier_count && !aligned(outlier_count, 4)) || (Xq && !aligned(Xq, 16)) ||
+      (aX && !aligned(aX, 4)) || (C && !aligned(C, 16)))
+    return LLMINT8_ERR_INVALID_ARG;
+  return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream, path,
+                    outlier_bitmap, outlier_idx, outlier_count, Xq, aX, C, nullptr, 0, nullptr,
+                    dtype, bias);
 }
 
 llmint8_status llmint8_linear_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
@@ -291,6 +328,7 @@ llmint8_status llmint8_linear_backward_input_timed(const void* dY, int64_t T, in
 }
 
 static llmint8_status check_blockwise(int dtype, int64_t n, int64_t block) {
+  // the codec takes fp16 or fp32 tensors
   if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_F32) return LLMINT8_ERR_INVALID_ARG;
   if (n < 0 || block <= 0) return LLMINT8_ERR_INVALID_ARG;
   if (block > 4096 || !blockwise_supported((int)block) || n % 16 != 0 || n > (int64_t)1 << 30)

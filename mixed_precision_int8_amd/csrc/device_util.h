@@ -9,10 +9,9 @@ namespace llmint8 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-
-// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 only.
-constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 
 // Buffer resource word 3 for raw (untyped) buffers on gfx9-family parts.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -33,19 +32,22 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);  // exact: bf16 is the top half of fp32
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  // v_cvt_pk_bf16_f32 rounds to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
   return v;
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// |x| codes of 8 fp16 values packed in a uint4, as 4 packed u16 pairs.
+// |x| codes of 8 16-bit values packed in a uint4, as 4 packed u16 pairs.
 __device__ __forceinline__ void abs_codes(const uint4& v, v2u16 out[4]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -58,26 +60,6 @@ __device__ __forceinline__ void abs_codes(const uint4& v, v2u16 out[4]) {
 // 4-bit mask -> 4 bytes of 0xff where the bit is set.
 __device__ __forceinline__ uint32_t expand4(uint32_t b4) {
   return ((b4 * 0x00204081u) & 0x01010101u) * 0xffu;
-}
-
-// Quantize 8 fp16 values (uint4) with scale s: rne(fl32(x * s)); values whose
-// bit in `skip` is set give 0. Returns the 8 int8 codes packed in a uint2.
-// fl32(x * s) is computed as fma(x, s, +0), the same single rounding of the
-// exact product (v_fma_mix_f32 takes the fp16 operand directly). The rounded
-// value q in [-127, 127] is stored as the byte (q + 128) ^ 0x80, which is the
-// two's-complement byte of q (v_cvt_pk_u8_f32 converts the exact integer).
-__device__ __forceinline__ uint2 quantize8(const uint4& v, float s, uint32_t skip) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t out[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint16_t h = (uint16_t)((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-    const float p = __builtin_fmaf((float)__builtin_bit_cast(_Float16, h), s, 0.0f);
-    const float r = __builtin_rintf(p) + 128.0f;
-    out[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r, (uint32_t)(i & 3), out[i >> 2]);
-  }
-  const uint32_t keep0 = expand4(~skip & 0xfu), keep1 = expand4((~skip >> 4) & 0xfu);
-  return make_uint2((out[0] ^ 0x80808080u) & keep0, (out[1] ^ 0x80808080u) & keep1);
 }
 
 // Quantize 8 fp16 values (uint4) with scale s: rne(fl32(x * s)), ANDed with
@@ -103,6 +85,60 @@ __device__ __forceinline__ uint2 quantize8_masked(const uint4& v, float s, uint3
   return make_uint2(__builtin_amdgcn_perm(b23, b01, 0x05040100u) & m0,
                     __builtin_amdgcn_perm(b67, b45, 0x05040100u) & m1);
 }
+
+// quantize8_masked for 8 bf16 values: each value is exact in fp32 (a shift),
+// fl32(x * s) is one fp32 multiply, then the same rounding and byte gathering.
+__device__ __forceinline__ uint2 quantize8_masked_bf16(const uint4& v, float s, uint32_t m0,
+                                                       uint32_t m1) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t bits = (i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16);
+    const float p = __builtin_bit_cast(float, bits) * s;
+    r[i] = __builtin_bit_cast(uint32_t, p + 12582912.0f);
+  }
+  const uint32_t b01 = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
+  const uint32_t b23 = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
+  const uint32_t b45 = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
+  const uint32_t b67 = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
+  return make_uint2(__builtin_amdgcn_perm(b23, b01, 0x05040100u) & m0,
+                    __builtin_amdgcn_perm(b67, b45, 0x05040100u) & m1);
+}
+
+// The 16-bit activation type: fp16 or bf16. Magnitude codes (value & 0x7fff)
+// order like the values for both, so outlier tests and maxima run on codes
+// unchanged; only the conversions, the quantizer's operand form and the MFMA
+// flavour of the 16-bit outlier product differ.
+template <bool BF16>
+struct Act16 {
+  static __device__ __forceinline__ float to_f32(uint32_t h) {
+    if constexpr (BF16) return bf16_bits_to_float(h);
+    else return half_bits_to_float(h);
+  }
+  static __device__ __forceinline__ uint16_t from_f32(float f) {
+    if constexpr (BF16) return float_to_bf16_bits(f);
+    else return float_to_half_bits(f);
+  }
+  static __device__ __forceinline__ uint2 quantize8(const uint4& v, float s, uint32_t m0, uint32_t m1) {
+    if constexpr (BF16) return quantize8_masked_bf16(v, s, m0, m1);
+    else return quantize8_masked(v, s, m0, m1);
+  }
+  // 32x32 output block, k = 16 (8 values per lane of a and b)
+  static __device__ __forceinline__ v16f_t mma32(const uint4& a, const uint4& b, v16f_t c) {
+    if constexpr (BF16)
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+  // 16x16 output block, k = 32 (8 values per lane of a and b)
+  static __device__ __forceinline__ v4f mma16(const uint4& a, const uint4& b, v4f c) {
+    if constexpr (BF16)
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+};
 
 // Maximum over the 64 lanes of two packed u16 values, result in every lane
 // (DPP row reductions, then the row broadcasts, then lane 63).

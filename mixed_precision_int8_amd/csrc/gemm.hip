@@ -2,8 +2,10 @@
 // 16-bit outlier product fused into its epilogue.
 //
 //   C[t,n]  = sum_k Xq[t,k] * Wq[n,k]                 (v_mfma_i32_32x32x32_i8)
-//   Y[t,n]  = fp16( C[t,n] * a[t] * b[n] / 127^2
-//                   + sum_j Xo[t,j] * Wd[n,j] )       (v_mfma_f32_32x32x16_f16)
+//   Y[t,n]  = r16( C[t,n] * a[t] * b[n] / 127^2
+//                  + sum_j Xo[t,j] * Wd[n,j] + bias[n] )
+//             (v_mfma_f32_32x32x16_f16 / _bf16; r16 rounds to the activation
+//              type, fp16 or bf16, and the bias is optional)
 //
 // "Hugging Face Quantization with bitsandbytes: 4-bit & 8-bit Models
 // Explained", section 2: the non-outlier part is multiplied in int8 and
@@ -23,12 +25,14 @@
 
 namespace llmint8 {
 
-template <class G>
+template <class G, bool BF16>
 __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tiles_t, int group_n) {
-  __shared__ __attribute__((aligned(1024))) char smem[G::LDS + (G::BN + G::BT) * 4];
-  // the tile's weight and activation scales, read by the epilogue
+  using A16 = Act16<BF16>;
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDS + (G::BN + G::BT) * 4 + G::BN * 2];
+  // the tile's weight and activation scales and bias, read by the epilogue
   float* sW_l = reinterpret_cast<float*>(smem + G::LDS);
   float* aX_l = sW_l + G::BN;
+  uint16_t* bias_l = reinterpret_cast<uint16_t*>(aX_l + G::BT);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -41,7 +45,9 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.Wq + (size_t)n0 * K, (uint32_t)(rows_n * K));
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.Xq + (size_t)t0 * K, (uint32_t)(rows_t * K));
 
+  uint16_t bias_v = 0;  // requested before the K loop, written to LDS after it
   auto scales_to_lds = [&]() {
+    if (a.bias && tid < G::BN && n0 + tid < N) bias_v = a.bias[n0 + tid];
     // scales -> LDS by direct copy (rows past the matrix read as zero). They
     // are issued before the first K stage, so the stage waits cover them.
     constexpr int CS = (G::BN + 63) / 64, CX = (G::BT + 63) / 64;
@@ -58,6 +64,10 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
   v16i acc[G::FN][G::FT];
   gemm_kloop<G, MmaI8>(smem, rA, rB, K, wave, lane, acc, scales_to_lds);
   const int fi = lane & 31, fg = lane >> 5;
+  if (a.bias) {  // uniform
+    if (tid < G::BN) bias_l[tid] = bias_v;
+    __syncthreads();
+  }
 
   // ---- epilogue, one 32-row block of n at a time. Output layout of a 32x32
   // block: lane holds, for column (t) lane&31, rows (n) 8*q + 4*(lane>>5) + r
@@ -73,21 +83,21 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
   // Operands of the first chunk of 32 outlier columns (the common case is a
   // single chunk), all requested before the first is used so that the
   // epilogue pays one memory latency rather than one per block.
-  v8h wf0[G::FN][2], xf0[G::FT][2];
+  uint4 wf0[G::FN][2], xf0[G::FT][2];
   if (nch > 0) {
 #pragma unroll
     for (int i = 0; i < G::FN; ++i) {
       const int nrow = min(n0 + wn * G::WN + i * 32 + fi, N - 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        wf0[i][h] = *reinterpret_cast<const v8h*>(a.Wd + (size_t)nrow * kOutChunk + h * 16 + fg * 8);
+        wf0[i][h] = *reinterpret_cast<const uint4*>(a.Wd + (size_t)nrow * kOutChunk + h * 16 + fg * 8);
     }
 #pragma unroll
     for (int j = 0; j < G::FT; ++j) {
       const int t = min(tl + j * 32, T - 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        xf0[j][h] = *reinterpret_cast<const v8h*>(a.Xo + (size_t)t * kOutChunk + h * 16 + fg * 8);
+        xf0[j][h] = *reinterpret_cast<const uint4*>(a.Xo + (size_t)t * kOutChunk + h * 16 + fg * 8);
     }
   }
 #pragma unroll
@@ -116,28 +126,35 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
     for (int j = 0; j < G::FT; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) y[j][v] = (float)acc[i][j][v] * (as[j] * bs[v]);
-    // outlier columns: fp16 operands, fp32 accumulation on top of the int8 part;
-    // a chunk of 32 outlier columns is two 32x32x16 steps.
+    // outlier columns: 16-bit operands (the activation type), fp32 accumulation
+    // on top of the int8 part; a chunk of 32 outlier columns is two 32x32x16 steps.
     if (nch > 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < G::FT; ++j)
-          y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf0[i][h], xf0[j][h], y[j], 0, 0, 0);
+        for (int j = 0; j < G::FT; ++j) y[j] = A16::mma32(wf0[i][h], xf0[j][h], y[j]);
     }
     const int nrow = min(n0 + wn * G::WN + i * 32 + fi, N - 1);
     for (int c = 1; c < nch; ++c) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const v8h wf = *reinterpret_cast<const v8h*>(
+        const uint4 wf = *reinterpret_cast<const uint4*>(
             a.Wd + ((size_t)c * N + nrow) * kOutChunk + h * 16 + fg * 8);
 #pragma unroll
         for (int j = 0; j < G::FT; ++j) {
           const int t = min(tl + j * 32, T - 1);
-          const v8h xf = *reinterpret_cast<const v8h*>(
+          const uint4 xf = *reinterpret_cast<const uint4*>(
               a.Xo + ((size_t)c * T + t) * kOutChunk + h * 16 + fg * 8);
-          y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, xf, y[j], 0, 0, 0);
+          y[j] = A16::mma32(wf, xf, y[j]);
         }
+      }
+    }
+    if (a.bias) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float bv = A16::to_f32(bias_l[wn * G::WN + 4 * fg + i * 32 + 8 * (v >> 2) + (v & 3)]);
+#pragma unroll
+        for (int j = 0; j < G::FT; ++j) y[j][v] += bv;
       }
     }
 #pragma unroll
@@ -150,14 +167,12 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
         uint16_t* dst = a.Y + (size_t)t * N + n;
         if (vec_ok && n + 3 < N) {
           uint2 p;
-          p.x = (uint32_t)float_to_half_bits(y[j][4 * q]) |
-                ((uint32_t)float_to_half_bits(y[j][4 * q + 1]) << 16);
-          p.y = (uint32_t)float_to_half_bits(y[j][4 * q + 2]) |
-                ((uint32_t)float_to_half_bits(y[j][4 * q + 3]) << 16);
+          p.x = (uint32_t)A16::from_f32(y[j][4 * q]) | ((uint32_t)A16::from_f32(y[j][4 * q + 1]) << 16);
+          p.y = (uint32_t)A16::from_f32(y[j][4 * q + 2]) | ((uint32_t)A16::from_f32(y[j][4 * q + 3]) << 16);
           *reinterpret_cast<uint2*>(dst) = p;
         } else {
           for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = float_to_half_bits(y[j][4 * q + r]);
+            if (n + r < N) dst[r] = A16::from_f32(y[j][4 * q + r]);
         }
       }
     }
@@ -168,7 +183,10 @@ template <class G>
 hipError_t launch_gemm_tile(const LinearArgs& a, hipStream_t stream, int group_n) {
   const int tn = (a.N + G::BN - 1) / G::BN, tt = (a.T + G::BT - 1) / G::BT;
   if (group_n < 1) group_n = 1;
-  hipLaunchKernelGGL(kb_gemm<G>, dim3(tn * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
+  if (a.bf16)
+    hipLaunchKernelGGL((kb_gemm<G, true>), dim3(tn * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
+  else
+    hipLaunchKernelGGL((kb_gemm<G, false>), dim3(tn * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@
 //   * Then all 8 wavefronts work on X: a thread owns 8-column chunks across
 //     all T rows, decides their outlier flags on its own (column absmax >=
 //     threshold), takes the rows' maxima over its kept columns in the same
-//     pass (packed u16 arithmetic on fp16 codes), and after one block-wide
+//     pass (packed u16 arithmetic on 16-bit magnitude codes), and after one block-wide
 //     reduction quantizes its chunks into LDS.
 //   * The stream wavefronts then multiply their quarter of K on
 //     v_mfma_i32_16x16x64_i8 (16 weight rows as A, int8 rows of X as B) and
@@ -26,7 +26,7 @@
 //     compacted the outlier indices and gathered the weight bytes of the
 //     first 32 outlier columns, computes the 16-bit outlier product on
 //     v_mfma_f32_16x16x32_f16; it finally sums the partials, dequantizes and
-//     stores fp16 Y.
+//     stores Y in the activation type (fp16 or bf16).
 // The kernel is instantiated per row capacity TB (1, 2, 4, 8, 16 >= T) so
 // that per-row loops are resolved at compile time.
 #include <atomic>
@@ -50,7 +50,7 @@ __host__ __device__ inline GemvLds gemv_lds(int T, int K) {
   auto al = [](int v, int a) { return (v + a - 1) / a * a; };
   L.kp = K + 16;  // row pitch of the int8 rows: shifts banks between rows
   int off = 0;
-  L.xs = off;  // fp16 X, copied in 1 KB pieces
+  L.xs = off;  // X (fp16 or bf16), copied in 1 KB pieces
   off += al(T * K * 2, 1024);
   L.xq = off;
   off += al(T * L.kp, 16);
@@ -104,8 +104,9 @@ __device__ __forceinline__ v2u16 pk_max(v2u16 a, v2u16 b) { return __builtin_ele
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
 __device__ __forceinline__ uint32_t as_u32(v2u16 x) { return __builtin_bit_cast(uint32_t, x); }
 
-template <int TB>
+template <int TB, bool BF16>
 __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, int kq) {
+  using A16 = Act16<BF16>;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int T = a.T, K = a.K, N = a.N;
   const GemvLds L = gemv_lds(T, K);
@@ -147,6 +148,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   };
   v4i w0[kGemvBatch], w1[kGemvBatch];
   float bs4[4] = {0.f, 0.f, 0.f, 0.f}, brow = 0.f;
+  uint16_t bias4[4] = {0, 0, 0, 0};
   if (xwave) {
     // ---- 1. X -> LDS (1 KB per wavefront issue); wavefront 0 also fetches
     // the scales of the 16 weight rows (rows past N read as zero)
@@ -160,6 +162,12 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         bs4[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)((4 * fg + v) * 4), 0, 0));
+      if (a.bias) {  // the bias of this lane's 4 output rows, for the epilogue
+        const __amdgpu_buffer_rsrc_t rBias = make_rsrc(a.bias + n0, (uint32_t)(rows_n * 2));
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          bias4[v] = __builtin_amdgcn_raw_buffer_load_b16(rBias, (uint32_t)((4 * fg + v) * 2), 0, 0);
+      }
     }
     for (int w = xt; w < KW; w += 256) bm[w] = 0u;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's part of X has landed
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     // ---- 3. all 8 wavefronts (the stream wavefronts have issued their loads
     // by now): a thread takes 8-column chunks across all rows: column absmax
     // -> outlier flags -> keep masks -> row maxima over the kept columns. All
-    // values are fp16 codes with the sign cleared, compared as packed u16.
+    // values are 16-bit codes with the sign cleared, compared as packed u16.
     const v2u16 hthr2 = {(uint16_t)hthr, (uint16_t)hthr};
     v2u16 rmax[TB];
 #pragma unroll
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       uint32_t m = 0u;
 #pragma unroll
       for (int w = 0; w < 8; ++w) m = max(m, (rowred[w * 8 + (lane >> 1)] >> ((lane & 1) * 16)) & 0xffffu);
-      const float ax = half_bits_to_float(m);
+      const float ax = A16::to_f32(m);
       srow = m ? 127.0f / ax : 0.0f;
       if (wave == 0) arow[lane] = ax;
     }
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
         if (t < T) v[t] = *reinterpret_cast<const uint4*>(xs + t * K + c * 8);
 #pragma unroll
       for (int t = 0; t < TB; ++t)
-        if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = quantize8_masked(v[t], st[t], m0, m1);
+        if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(v[t], st[t], m0, m1);
     }
     // wavefront 0: compact the outlier indices (ascending), then gather the
     // weight bytes of the first 32 outlier columns for the epilogue
@@ -329,21 +337,25 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       const uint4 iv = *reinterpret_cast<const uint4*>(idxl + c + fg * 8);
       const uint32_t iw[4] = {iv.x, iv.y, iv.z, iv.w};
       int h[8];
-      _Float16 xv[8];
+      uint16_t xv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         h[e] = c + fg * 8 + e < count ? (int)((iw[e >> 1] >> ((e & 1) * 16)) & 0xffffu) : 0;
-        xv[e] = __builtin_bit_cast(_Float16, xr[h[e]]);
+        xv[e] = xr[h[e]];
       }
-      v8h wf, xf;
+      uint16_t wf[8], xf[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool ok = c + fg * 8 + e < count;
         const uint32_t word = c == 0 ? g[e] : load_word_of(rW, ok ? rowoff + (uint32_t)h[e] : kOobOffset);
-        wf[e] = (_Float16)(((float)byte_of(word, h[e]) * brow) / 127.0f);
-        xf[e] = (ok && t < T) ? xv[e] : (_Float16)0.0f;
+        wf[e] = A16::from_f32(((float)byte_of(word, h[e]) * brow) / 127.0f);
+        xf[e] = (ok && t < T) ? xv[e] : (uint16_t)0;
       }
-      yo = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf, yo, 0, 0, 0);
+      const uint4 wf4 = make_uint4(wf[0] | ((uint32_t)wf[1] << 16), wf[2] | ((uint32_t)wf[3] << 16),
+                                   wf[4] | ((uint32_t)wf[5] << 16), wf[6] | ((uint32_t)wf[7] << 16));
+      const uint4 xf4 = make_uint4(xf[0] | ((uint32_t)xf[1] << 16), xf[2] | ((uint32_t)xf[3] << 16),
+                                   xf[4] | ((uint32_t)xf[5] << 16), xf[6] | ((uint32_t)xf[7] << 16));
+      yo = A16::mma16(wf4, xf4, yo);
     }
   }
   lds_barrier();  // D: the 4 partial products are in LDS
@@ -369,7 +381,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
 #pragma unroll
   for (int w = 1; w < 4; ++w) acc += red[w * 64 + lane];
 
-  // ---- 6. dequantize, add the outlier product, fp16 store
+  // ---- 6. dequantize, add the outlier product and the bias, round and store
   const int n = n0 + 4 * fg;
   if (a.dbg_C && t < T) {
     for (int v = 0; v < 4; ++v)
@@ -379,26 +391,30 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   v4f y;
 #pragma unroll
   for (int v = 0; v < 4; ++v) y[v] = (float)acc[v] * (at * (bs4[v] * (1.0f / 16129.0f))) + yo[v];
+  if (a.bias) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) y[v] += A16::to_f32(bias4[v]);
+  }
   if (t < T) {
     uint16_t* dst = a.Y + (size_t)t * N + n;
     if ((N & 3) == 0 && n + 3 < N) {
       uint2 p;
-      p.x = (uint32_t)float_to_half_bits(y[0]) | ((uint32_t)float_to_half_bits(y[1]) << 16);
-      p.y = (uint32_t)float_to_half_bits(y[2]) | ((uint32_t)float_to_half_bits(y[3]) << 16);
+      p.x = (uint32_t)A16::from_f32(y[0]) | ((uint32_t)A16::from_f32(y[1]) << 16);
+      p.y = (uint32_t)A16::from_f32(y[2]) | ((uint32_t)A16::from_f32(y[3]) << 16);
       *reinterpret_cast<uint2*>(dst) = p;
     } else {
       for (int v = 0; v < 4; ++v)
-        if (n + v < N) dst[v] = float_to_half_bits(y[v]);
+        if (n + v < N) dst[v] = A16::from_f32(y[v]);
     }
   }
 }
 
-template <int TB>
+template <int TB, bool BF16>
 static hipError_t launch_gemv_tb(const LinearArgs& a, hipStream_t stream) {
   const GemvLds L = gemv_lds(a.T, a.K);
   static std::atomic<int> attr_max{64 * 1024};  // dynamic LDS this instance is allowed so far
   if (L.total > attr_max.load()) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kd_gemv<TB>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kd_gemv<TB, BF16>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     int cur = attr_max.load();
@@ -407,16 +423,22 @@ static hipError_t launch_gemv_tb(const LinearArgs& a, hipStream_t stream) {
   }
   const int kq = (int)(ceil_div(ceil_div(a.K, 4), 64) * 64);
   const int blocks = (int)ceil_div(a.N, kGemvRowsN);
-  hipLaunchKernelGGL(kd_gemv<TB>, dim3(blocks), dim3(512), L.total, stream, a, threshold_code(a.thr), kq);
+  hipLaunchKernelGGL((kd_gemv<TB, BF16>), dim3(blocks), dim3(512), L.total, stream, a,
+                     threshold_code(a.thr, BF16), kq);
   return hipGetLastError();
 }
 
+template <bool BF16>
+static hipError_t launch_gemv_dt(const LinearArgs& a, hipStream_t stream) {
+  if (a.T <= 1) return launch_gemv_tb<1, BF16>(a, stream);
+  if (a.T <= 2) return launch_gemv_tb<2, BF16>(a, stream);
+  if (a.T <= 4) return launch_gemv_tb<4, BF16>(a, stream);
+  if (a.T <= 8) return launch_gemv_tb<8, BF16>(a, stream);
+  return launch_gemv_tb<16, BF16>(a, stream);
+}
+
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream) {
-  if (a.T <= 1) return launch_gemv_tb<1>(a, stream);
-  if (a.T <= 2) return launch_gemv_tb<2>(a, stream);
-  if (a.T <= 4) return launch_gemv_tb<4>(a, stream);
-  if (a.T <= 8) return launch_gemv_tb<8>(a, stream);
-  return launch_gemv_tb<16>(a, stream);
+  return a.bf16 ? launch_gemv_dt<true>(a, stream) : launch_gemv_dt<false>(a, stream);
 }
 
 }  // namespace llmint8

@@ -23,8 +23,9 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   idx    int32  [K]                       ascending outlier columns
 //   aX     fp32   [T]                       row statistic
 //   Xq     int8   [T, K]                    quantized activations
-//   Xo     fp16   [KC][T][32]               outlier activations, chunk-major, zero padded
-//   Wd     fp16   [KC][N][32]               dequantized outlier weight columns, same layout
+//   Xo     16-bit [KC][T][32]               outlier activations, chunk-major, zero padded
+//   Wd     16-bit [KC][N][32]               dequantized outlier weight columns, same layout
+// (16-bit: the activation type, fp16 or bf16)
 // with KW = ceil(K/32) words and KC = ceil(K/32) chunks of 32 outlier columns.
 struct WsLayout {
   size_t parts, bitmap, count, idx, aX, Xq, Xo, Wd, total;
@@ -60,6 +61,8 @@ struct LinearArgs {
   uint16_t* Y;
   int T, K, N;
   float thr;
+  int bf16;              // activation type: 0 fp16, 1 bf16 (X, bias, Y, Xo, Wd)
+  const uint16_t* bias;  // [N] in the activation type, or null
   // workspace
   uint32_t* parts;
   uint32_t* bitmap;
@@ -88,10 +91,10 @@ struct BwdArgs {
 };
 
 // Launchers (each enqueues exactly one kernel on `stream`).
-hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW,
+hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW, bool bf16,
                                   hipStream_t stream);
 int scan_row_groups(int T, int K, int num_cus);
-uint32_t threshold_code(float thr);  // smallest fp16 |x| code whose value reaches thr
+uint32_t threshold_code(float thr, bool bf16);  // smallest 16-bit |x| code whose value reaches thr
 hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream);
 hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStream_t stream);
 hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream);

@@ -23,6 +23,7 @@ namespace llmint8 {
 // Weight quantization: one wavefront per output row.
 //   sW[n] = max_k |W[n,k]|,  Wq[n,k] = rne(fl32(W[n,k] * fl32(127 / sW[n])))
 // ---------------------------------------------------------------------------
+template <bool BF16>
 __global__ __launch_bounds__(256) void kw_quantize_rows(const uint16_t* __restrict__ W, int N,
                                                         int K, int8_t* __restrict__ Wq,
                                                         float* __restrict__ sW) {
@@ -40,17 +41,20 @@ __global__ __launch_bounds__(256) void kw_quantize_rows(const uint16_t* __restri
                                            __builtin_elementwise_max(a[2], a[3])));
   }
   const int m = wave_max_i(max((int)m2.x, (int)m2.y));
-  const float b = half_bits_to_float((uint32_t)m);
+  const float b = Act16<BF16>::to_f32((uint32_t)m);
   const float s = m > 0 ? 127.0f / b : 0.0f;
   uint2* out = reinterpret_cast<uint2*>(Wq + (size_t)n * K);
-  for (int c = lane; c < chunks; c += 64) out[c] = quantize8(row[c], s, 0u);
+  for (int c = lane; c < chunks; c += 64) out[c] = Act16<BF16>::quantize8(row[c], s, ~0u, ~0u);
   if (lane == 0) sW[n] = b;
 }
 
-hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW,
+hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW, bool bf16,
                                   hipStream_t stream) {
   const int blocks = (N + 3) / 4;
-  hipLaunchKernelGGL(kw_quantize_rows, dim3(blocks), dim3(256), 0, stream, W, N, K, Wq, sW);
+  if (bf16)
+    hipLaunchKernelGGL(kw_quantize_rows<true>, dim3(blocks), dim3(256), 0, stream, W, N, K, Wq, sW);
+  else
+    hipLaunchKernelGGL(kw_quantize_rows<false>, dim3(blocks), dim3(256), 0, stream, W, N, K, Wq, sW);
   return hipGetLastError();
 }
 
@@ -59,9 +63,9 @@ hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, f
 // of row group g; 8 lanes span one 128-byte row segment and 64 rows are read
 // per load, kScanLoads loads in flight per thread. The per-column maximum |x|
 // code is kept with packed u16 max and compared with the threshold once at
-// the end: |x| >= thr  <=>  code(|x|) >= hthr, where hthr is the smallest fp16
-// magnitude code whose value reaches thr (computed on the host), so the
-// decision is the fp32 comparison, taken exactly.
+// the end: |x| >= thr  <=>  code(|x|) >= hthr, where hthr is the smallest
+// 16-bit (fp16 or bf16) magnitude code whose value reaches thr (computed on
+// the host), so the decision is the fp32 comparison, taken exactly.
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 512;
 constexpr int kScanLoads = 8;
@@ -122,16 +126,23 @@ int scan_row_groups(int T, int K, int num_cus) {
   return g < 1 ? 1 : (g > kScanMaxGroups ? kScanMaxGroups : g);
 }
 
-uint32_t threshold_code(float thr) {
-  // smallest fp16 magnitude code h (0..0x7c00) with value(h) >= thr; 0x7c00 (inf)
-  // when no finite fp16 reaches thr. Codes are ordered like their values.
-  auto value = [](uint32_t h) -> double {
+uint32_t threshold_code(float thr, bool bf16) {
+  // smallest 16-bit magnitude code h with value(h) >= thr; the infinity code
+  // (0x7c00 fp16, 0x7f80 bf16) when no finite value reaches thr. Codes are
+  // ordered like their values.
+  auto value = [bf16](uint32_t h) -> double {
+    if (bf16) {
+      const uint32_t e = (h >> 7) & 255u, f = h & 127u;
+      if (e == 255) return INFINITY;
+      if (e == 0) return std::ldexp((double)f, -133);
+      return std::ldexp((double)(128 + f), (int)e - 134);
+    }
     const uint32_t e = (h >> 10) & 31u, f = h & 1023u;
     if (e == 31) return INFINITY;
     if (e == 0) return std::ldexp((double)f, -24);
     return std::ldexp((double)(1024 + f), (int)e - 25);
   };
-  uint32_t lo = 0, hi = 0x7c00;  // invariant: value(hi) >= thr (inf >= anything)
+  uint32_t lo = 0, hi = bf16 ? 0x7f80u : 0x7c00u;  // invariant: value(hi) >= thr (inf >= anything)
   if (value(lo) >= thr) return 0;
   while (hi - lo > 1) {
     const uint32_t mid = (lo + hi) / 2;
@@ -144,7 +155,7 @@ hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream) {
   const int KW = (a.K + 31) / 32;
   dim3 grid((a.K + 63) / 64, groups);
   hipLaunchKernelGGL(ka_scan, grid, dim3(kScanThreads), 0, stream, a.X, a.T, a.K,
-                     threshold_code(a.thr), a.parts, KW);
+                     threshold_code(a.thr, a.bf16 != 0), a.parts, KW);
   return hipGetLastError();
 }
 
@@ -186,6 +197,7 @@ __device__ __forceinline__ uint32_t chunk_kept_max(const uint4& v, uint32_t skip
   return max((uint32_t)mx.x, (uint32_t)mx.y);
 }
 
+template <bool BF16>
 __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int groups, int nq) {
   __shared__ uint32_t bm[kMaxKW];
   __shared__ int pre[kMaxKW];
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
         for (int c = lane; c < KC; c += 64) m = max(m, chunk_kept_max(row[c], chunk_skip_mask(bm, c)));
       }
       m = wave_max_u16x2(m) & 0xffffu;
-      const float ax = half_bits_to_float(m);
+      const float ax = Act16<BF16>::to_f32(m);
       const float s = m ? 127.0f / ax : 0.0f;
       if (in_regs) {
 #pragma unroll
@@ -242,13 +254,13 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
           const int c = lane + 64 * u;
           if (u < cpl && c < KC) {
             const uint32_t skip = chunk_skip_mask(bm, c);
-            out[c] = quantize8_masked(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+            out[c] = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
           }
         }
       } else {
         for (int c = lane; c < KC; c += 64) {
           const uint32_t skip = chunk_skip_mask(bm, c);
-          out[c] = quantize8_masked(row[c], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+          out[c] = Act16<BF16>::quantize8(row[c], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
         }
       }
       if (lane == 0) a.aX[t] = ax;
@@ -350,7 +362,7 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
       *reinterpret_cast<uint4*>(a.Xo + dst) = make_uint4(val[0] | ((uint32_t)val[1] << 16), val[2] | ((uint32_t)val[3] << 16),
                                                            val[4] | ((uint32_t)val[5] << 16), val[6] | ((uint32_t)val[7] << 16));
     } else {
-      // Wd[n,j] = fp16(fl32(fl32(Wq[n,idx_j] * sW[n]) / 127))
+      // Wd[n,j] = r16(fl32(fl32(Wq[n,idx_j] * sW[n]) / 127)), r16 the activation type's rounding
       const int n = row - T;
       const float b = a.sW[n];
       const int8_t* wr = a.Wq + (size_t)n * K;
@@ -359,7 +371,7 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
       for (int e = 0; e < 8; ++e) g[e] = wr[h[e]];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        val[e] = e < nvalid ? float_to_half_bits(((float)g[e] * b) / 127.0f) : (uint16_t)0;
+        val[e] = e < nvalid ? Act16<BF16>::from_f32(((float)g[e] * b) / 127.0f) : (uint16_t)0;
       const size_t dst = ((size_t)(j0 / kOutChunk) * N + n) * kOutChunk + (j0 % kOutChunk);
       *reinterpret_cast<uint4*>(a.Wd + dst) = make_uint4(val[0] | ((uint32_t)val[1] << 16), val[2] | ((uint32_t)val[3] << 16),
                                                            val[4] | ((uint32_t)val[5] << 16), val[6] | ((uint32_t)val[7] << 16));
@@ -375,7 +387,10 @@ hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStrea
   int ng = (int)ceil_div((int64_t)(a.T + a.N) * (kOutChunk / 8), kPrepThreads);
   if (ng > 2 * num_cus) ng = 2 * num_cus;
   if (ng < 1) ng = 1;
-  hipLaunchKernelGGL(ka_prepare, dim3(nq + ng), dim3(kPrepThreads), 0, stream, a, groups, nq);
+  if (a.bf16)
+    hipLaunchKernelGGL(ka_prepare<true>, dim3(nq + ng), dim3(kPrepThreads), 0, stream, a, groups, nq);
+  else
+    hipLaunchKernelGGL(ka_prepare<false>, dim3(nq + ng), dim3(kPrepThreads), 0, stream, a, groups, nq);
   return hipGetLastError();
 }
 

@@ -195,3 +195,31 @@ def test_blockwise_argument_errors(lib):
     assert dq(None, ALIGNED, 4096, 64, ALIGNED, F16, None) == INVALID
     assert dq(ALIGNED, ALIGNED, 4096, 64, MISALIGNED, F32, None) == INVALID
     assert dq(ALIGNED, ALIGNED, 4096, 32, ALIGNED, F32, None) == UNSUPPORTED
+
+
+def test_ex_entry_points_argument_errors(lib):
+    F16, BF16, F32 = m8.LLMINT8_DTYPE_F16, m8.LLMINT8_DTYPE_BF16, m8.LLMINT8_DTYPE_F32
+    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    lx = lib.llmint8_linear_ex
+
+    def call(dtype=BF16, bias=None, X=ALIGNED, ws_bytes=need):
+        return lx(X, dtype, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, bias, ALIGNED, ALIGNED,
+                  ws_bytes, None)
+    assert call(dtype=F32) == INVALID                  # fp32 activations are not a forward type
+    assert call(dtype=7) == INVALID
+    assert call(bias=ctypes.c_void_p(P + 1)) == INVALID  # bias needs 2-byte alignment
+    assert call(X=None) == INVALID
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert lx(None, F16, 0, 1024, ALIGNED, ALIGNED, 1024, 6.0, None, None, None, 0, None) == OK
+    d = lib.llmint8_linear_debug_ex
+    base = [ALIGNED, BF16, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, ALIGNED, ALIGNED, ALIGNED, need,
+            None]
+    assert d(*base, 7, None, None, None, None, None, None) == INVALID
+    assert d(*base, m8.LLMINT8_PATH_GEMM, None, None, None, MISALIGNED, None, None) == INVALID
+    q = lib.llmint8_quantize_weight_ex
+    assert q(ALIGNED, F32, 16, 64, ALIGNED, ALIGNED, None) == INVALID
+    assert q(None, BF16, 16, 64, ALIGNED, ALIGNED, None) == INVALID
+    assert q(ALIGNED, BF16, 16, 72, ALIGNED, ALIGNED, None) == UNSUPPORTED
+    assert q(MISALIGNED, BF16, 16, 64, ALIGNED, ALIGNED, None) == INVALID
+    # the codec takes fp16 or fp32, not bf16
+    assert lib.llmint8_quantize_blockwise(ALIGNED, BF16, 4096, 64, ALIGNED, ALIGNED, None) == INVALID

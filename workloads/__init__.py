@@ -32,6 +32,15 @@ the draw order below, so either can be drawn without the other:
    ``s = float32(1e-3 * standard_normal(n))``, then every 1000th element times
    50 (isolated large values, one per few blocks).
 
+7. (bf16 checks only) bf16 inputs are the fp16 draws above widened to float32
+   and cut to their upper 16 bits (truncation toward zero, so every value is
+   an exact bf16 and the injected columns keep their magnitudes to 1%).
+
+8. (bias checks only) a bias vector comes from
+   ``Generator(PCG64(SeedSequence([seed, 4])))``:
+   ``bias = float32(0.5 * standard_normal(N))``, stored as fp16, or as bf16 by
+   the truncation of step 7.
+
 Natural N(0,1) entries can still cross the threshold on their own; the set of
 outlier columns is always whatever the method computes, not ``cols``.
 """
@@ -43,7 +52,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "make_weight", "make_activations", "make", "make_output_grad",
-           "make_state"]
+           "make_state", "as_bf16_input", "make_bias"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -129,8 +138,23 @@ def make_state(seed: int, n: int) -> np.ndarray:
     return s
 
 
+def as_bf16_input(x16: np.ndarray) -> np.ndarray:
+    """Step 7 of the recipe: bf16 bit patterns (uint16) of fp16 draws, by truncation."""
+    bits = np.ascontiguousarray(np.asarray(x16, dtype=np.float16).astype(np.float32)).view(np.uint32)
+    return (bits >> np.uint32(16)).astype(np.uint16)
+
+
+def make_bias(seed: int, N: int, bf16: bool = False) -> np.ndarray:
+    """Step 8 of the recipe: a bias vector [N], fp16 values or bf16 bit patterns."""
+    b = rng_for(seed, 4).standard_normal(N, dtype=np.float32) * np.float32(0.5)
+    if bf16:
+        return (np.ascontiguousarray(b).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return b.astype(np.float16)
+
+
 def rng_for(seed: int, stream: int) -> np.random.Generator:
-    """Stream 0 draws the weight, 1 the activations, 2 output gradients, 3 codec states."""
+    """Stream 0 draws the weight, 1 the activations, 2 output gradients, 3 codec
+    states, 4 biases."""
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
 
 

@@ -189,3 +189,110 @@ def dequantize_blockwise(q, absmax, block, to_fp16):
         v = f32(f32(c * absmax[i // block]) / 127.0)
         out.append(f16(v) if to_fp16 else v)
     return out
+
+
+# --------------------------------------------------------------------------- 4-bit weight path
+
+NF4_P_MAX = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0)
+
+
+def phi(x: float) -> float:
+    """Standard normal CDF from math.erfc."""
+    return 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def normal_quantile(p: float) -> float:
+    """Phi^-1(p) by bisection on ``phi`` (no library inverse)."""
+    lo, hi = -12.0, 12.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if mid in (lo, hi):
+            break
+        if phi(mid) < p:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def nf4_book():
+    """NF4 levels by code: normal quantiles on two evenly spaced probability
+    grids (8 positive, 7 negative) plus zero, scaled so the largest is 1."""
+    d = normal_quantile(NF4_P_MAX)
+    pos = [normal_quantile(NF4_P_MAX + i * ((0.5 - NF4_P_MAX) / 8.0)) / d for i in range(8)]
+    neg = [-normal_quantile(NF4_P_MAX + i * ((0.5 - NF4_P_MAX) / 7.0)) / d for i in range(7)]
+    return [f32(v) for v in sorted(neg + [0.0] + pos)]
+
+
+def fp4_book():
+    """FP4 (E2M1) levels by code, decoded through an fp32 bit pattern, then / 6."""
+    out = []
+    for code in range(16):
+        sign, e, m = code >> 3, (code >> 1) & 3, code & 1
+        if e == 0 and m == 0:
+            bits = sign << 31
+        elif e == 0:
+            bits = (sign << 31) | (126 << 23)               # subnormal 0.5
+        else:
+            bits = (sign << 31) | ((e - 1 + 127) << 23) | (m << 22)
+        v = struct.unpack("<f", struct.pack("<I", bits))[0]
+        out.append(f32(v / 6.0))
+    return out
+
+
+def _levels(book):
+    """(level value, code) pairs of the distinct levels, ascending; -0 dropped."""
+    pairs = [(v, c) for c, v in enumerate(book) if not (v == 0.0 and math.copysign(1.0, v) < 0)]
+    return sorted(pairs)
+
+
+def quantize_4bit(vals, block, book):
+    """Blockwise 4-bit codes of a flat list of 16-bit-valued floats; packed bytes, absmax."""
+    lev = _levels(book)
+    mids = [f32(f32(lev[i][0] + lev[i + 1][0]) * 0.5) for i in range(len(lev) - 1)]
+    codes, absmax = [], []
+    for b0 in range(0, len(vals), block):
+        blk = vals[b0:b0 + block]
+        a = 0.0
+        for v in blk:
+            a = max(a, abs(v))
+        absmax.append(a)
+        for v in blk:
+            xn = f32(v / a) if a > 0 else 0.0
+            rank = 0
+            for m in mids:
+                if m < xn:
+                    rank += 1
+            codes.append(lev[rank][1])
+    if len(codes) % 2:
+        codes.append(0)
+    packed = [codes[i] | (codes[i + 1] << 4) for i in range(0, len(codes), 2)]
+    return packed, absmax
+
+
+def dequantize_4bit(packed, absmax, block, book, n, to_bf16=False):
+    out = []
+    for i in range(n):
+        code = (packed[i // 2] >> (4 * (i % 2))) & 15
+        v = f32(book[code] * absmax[i // block])
+        out.append(bf16(v) if to_bf16 else f16(v))
+    return out
+
+
+def linear_4bit(X, packed, absmax, block, book, N, to_bf16=False, bias=None):
+    """Y[t][n] = r16(sum_k X[t][k] * Wdeq[n][k] + bias[n]), exact sum, one rounding."""
+    K = len(X[0])
+    Wd = dequantize_4bit(packed, absmax, block, book, N * K, to_bf16)
+    r = bf16_of_fraction if to_bf16 else f16_of_fraction
+    Y = []
+    for row in X:
+        out = []
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(row[k]) * Fraction(Wd[n * K + k])
+            if bias is not None:
+                acc += Fraction(bias[n])
+            out.append(r(acc))
+        Y.append(out)
+    return Y

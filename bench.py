@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-backward", action="store_true", help="skip the input-gradient workload")
     p.add_argument("--no-codec", action="store_true", help="skip the blockwise codec workload")
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 + bias workload")
+    p.add_argument("--no-fourbit", action="store_true", help="skip the 4-bit weight workload")
     p.add_argument("--decode-copies", type=int, default=24,
                    help="distinct weight copies cycled in the decode timing (> last-level cache)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -290,6 +291,80 @@ def main():
             del cps
         result["bf16_bias"] = {"workload": "bf16 X, bias and Y; the prefill and decode layers",
                                "timing": "whole calls between two events", **bf}
+
+    # ---- 4-bit (NF4) weights: the decode-shaped linear that streams the codes,
+    # at the decode layer (K = N = 4096) and the large layer (K = 8192, N = 28672)
+    if not args.no_fourbit:
+        fb = {}
+        block = 64
+        for lname, cfg, Ts, ncopies in (("decode_layer", workloads.CONFIGS["decode"], (1, 8), 32),
+                                        ("large_layer", workloads.CONFIGS["large"], (1, 8), 3)):
+            K4, N4 = cfg.K, cfg.N
+            W4 = torch.from_numpy(workloads.make_weight(workloads.rng_for(cfg.seed, 0), N4, K4,
+                                                        cfg.sigma)).to(dev)
+            pk, am = m8.llmint8_quantize_4bit(W4, block, "nf4")
+            del W4
+            cps = [(pk.clone(), am.clone()) for _ in range(ncopies)]
+            X4all = workloads.make(cfg, T=max(Ts), with_weight=False)[1]
+            for T4 in Ts:
+                X4 = torch.from_numpy(np.ascontiguousarray(X4all[:T4])).to(dev)
+                Y4 = torch.empty((T4, N4), dtype=torch.float16, device=dev)
+
+                def call(i, X4=X4, Y4=Y4, N4=N4):
+                    p_, a_ = cps[i % len(cps)]
+                    m8.llmint8_linear_4bit(X4, p_, a_, N4, block, "nf4", Y=Y4)
+
+                i = 0
+                t_w = time.perf_counter()
+                while i < max(args.warmup, 2 * len(cps)) or (time.perf_counter() - t_w) * 1e3 < args.warmup_ms:
+                    call(i)
+                    i += 1
+                    if i % 16 == 0:
+                        torch.cuda.synchronize()
+                torch.cuda.synchronize()
+                reps = max(args.steps, 2 * len(cps)) // len(cps) * len(cps)
+                q0 = torch.cuda.Event(enable_timing=True)
+                q1 = torch.cuda.Event(enable_timing=True)
+                q0.record(stream)
+                for i in range(reps):
+                    call(i)
+                q1.record(stream)
+                torch.cuda.synchronize()
+                us = q0.elapsed_time(q1) / reps * 1e3
+                nbytes = N4 * K4 // 2 + 4 * (N4 * K4 // block) + 2 * T4 * K4 + 2 * T4 * N4
+                gbs = nbytes / (us * 1e-6) / 1e9
+                fb[f"{lname}_T{T4}"] = {"K": K4, "N": N4, "T": T4, "us_per_call": round(us, 3),
+                                        "GB_per_s": round(gbs, 1),
+                                        "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+                                        "algorithmic_bytes": nbytes, "weight_copies_cycled": len(cps)}
+            if lname == "large_layer":
+                # the standalone dequantization of the same weight (fp16 out)
+                outs = [torch.empty((N4 * K4,), dtype=torch.float16, device=dev) for _ in range(2)]
+                for i in range(4):
+                    m8.llmint8_dequantize_4bit(cps[i % 2][0], cps[i % 2][1], block, "nf4",
+                                               out=outs[i % 2])
+                torch.cuda.synchronize()
+                q0 = torch.cuda.Event(enable_timing=True)
+                q1 = torch.cuda.Event(enable_timing=True)
+                q0.record(stream)
+                for i in range(10):
+                    m8.llmint8_dequantize_4bit(cps[i % 2][0], cps[i % 2][1], block, "nf4",
+                                               out=outs[i % 2])
+                q1.record(stream)
+                torch.cuda.synchronize()
+                us = q0.elapsed_time(q1) / 10 * 1e3
+                nbytes = N4 * K4 // 2 + 4 * (N4 * K4 // block) + 2 * N4 * K4
+                fb["large_layer_dequantize"] = {"us_per_call": round(us, 2),
+                                                "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                                "pct_hbm": round(100.0 * nbytes / (us * 1e-6) / 1e9
+                                                                 / PEAK_HBM_GBS, 2),
+                                                "algorithmic_bytes": nbytes}
+                del outs
+            del cps, pk, am
+        result["fourbit_nf4"] = {"workload": "NF4 weights, block 64, fp16 activations; the decode "
+                                             "and large layers", "kernel": "kn_gemv",
+                                 "bound": "hbm", "peak_GB_per_s": PEAK_HBM_GBS,
+                                 "timing": "whole calls between two events", **fb}
 
     # ---- input gradient through the frozen layer, at the prefill layer's shape
     if not args.no_backward:

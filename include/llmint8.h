@@ -250,6 +250,72 @@ LLMINT8_API llmint8_status llmint8_linear_debug_ex(const void* X, int dtype, int
                                                    int32_t* outlier_idx, int32_t* outlier_count,
                                                    int8_t* Xq, float* aX, int32_t* C);
 
+/*
+ * 4-bit weights: NF4 and FP4 ("bitsandbytes: GPU-Accelerated Inference and
+ * Training at Lower Bit Depths", introduction: the 4-bit layer supports FP4
+ * and NF4, quantizes the weight in blocks that each carry a scaling factor and
+ * computes in FP16 or BF16 with the weight dequantized per operation;
+ * "Hugging Face Quantization with bitsandbytes ...", section 4: NF4 places its
+ * levels where normally distributed weights concentrate, FP4 is a generic
+ * 4-bit float).
+ *
+ * Code books (the pages name the types but print no values; this library
+ * computes them on the host in binary64 and rounds once to fp32):
+ *   NF4  the published NormalFloat construction: standard-normal quantiles at
+ *        probabilities p_max + i (0.5 - p_max) / 8 (i = 0..7) above zero and
+ *        their mirror images at p_max + i (0.5 - p_max) / 7 (i = 0..6) below,
+ *        plus an exact zero, divided by the quantile at p_max = 1 - (1/32 +
+ *        1/30) / 2; code c is the c-th level in ascending order (code 7 = 0).
+ *   FP4  E2M1 (sign, two exponent bits with bias 1, one mantissa bit, exponent
+ *        0 subnormal) divided by 6: code = 8 sign + magnitude bits, magnitudes
+ *        {0, .5, 1, 1.5, 2, 3, 4, 6} / 6.
+ * llmint8_code_book_4bit writes the 16 fp32 values, indexed by code, to the
+ * host array `values`.
+ *
+ * Blockwise codes of a flat 16-bit tensor of n elements (a weight [N, K] is
+ * taken row-major): block b is elements [b * block, (b + 1) * block);
+ *   absmax[b] = max |w| over block b (fp32, exact)
+ *   code      = the level nearest to fl32(w / absmax[b]) (0 when absmax is 0),
+ *               decided against the fp32 midpoints fl32(fl32(l_i + l_{i+1}) *
+ *               0.5) of adjacent distinct levels; a value on a midpoint takes
+ *               the lower level; FP4 writes zero as +0
+ *   packed    = two codes per byte, element 2 j in the low nibble of byte j
+ *   Wdeq      = r16(fl32(value[code] * absmax[b])) in dtype (dequantize_4bit)
+ * Arguments:
+ *   W, out     device, dtype LLMINT8_DTYPE_F16 or _BF16, n elements, 16-byte aligned
+ *   packed     device uint8 [n / 2], 16-byte aligned
+ *   absmax     device fp32 [ceil(n / block)], 4-byte aligned
+ *   quant_type LLMINT8_QUANT_NF4 or LLMINT8_QUANT_FP4 (else LLMINT8_ERR_INVALID_ARG)
+ * Requires block a power of two in [64, 4096], n % 16 == 0 and n < 2^31
+ * (LLMINT8_ERR_UNSUPPORTED otherwise); n == 0 is a no-op. Inputs must be
+ * finite. Codes, absmax and Wdeq are bit-exact.
+ *
+ * llmint8_linear_4bit: Y = r16(X . Wdeq^T + bias), the decode-shaped forward
+ * of a 4-bit layer, with the weight dequantized on the fly and never stored:
+ *   X       device [T, K] in dtype, 16-byte aligned
+ *   packed  device [N, K] codes (as above, n = N K), absmax per block
+ *   bias    device [N] in dtype (2-byte aligned) or NULL
+ *   Y       device [T, N] in dtype, 2-byte aligned
+ * The products of the 16-bit operands are summed in fp32 and Y is rounded
+ * once. Requires K % 128 == 0, N K < 2^31 and T K < 2^31
+ * (LLMINT8_ERR_UNSUPPORTED); T == 0 is a no-op. Any T runs; the weight is read
+ * once per 16 rows of X, so the route is meant for small T (decode).
+ * All calls are asynchronous on `stream`, allocate nothing and use no workspace.
+ */
+#define LLMINT8_QUANT_NF4 0
+#define LLMINT8_QUANT_FP4 1
+LLMINT8_API llmint8_status llmint8_code_book_4bit(int quant_type, float* values);
+LLMINT8_API llmint8_status llmint8_quantize_4bit(const void* W, int dtype, int64_t n, int64_t block,
+                                                 int quant_type, uint8_t* packed, float* absmax,
+                                                 void* stream);
+LLMINT8_API llmint8_status llmint8_dequantize_4bit(const uint8_t* packed, const float* absmax,
+                                                   int64_t n, int64_t block, int quant_type,
+                                                   void* out, int dtype, void* stream);
+LLMINT8_API llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t T, int64_t K,
+                                               const uint8_t* packed, const float* absmax,
+                                               int64_t block, int quant_type, int64_t N,
+                                               const void* bias, void* Y, void* stream);
+
 /* Largest T the fused GEMV route accepts for this K (0 if none). */
 LLMINT8_API int llmint8_gemv_max_rows(int64_t K);
 

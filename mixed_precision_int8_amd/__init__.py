@@ -20,6 +20,8 @@ __all__ = [
     "LLMINT8_DTYPE_F16", "LLMINT8_DTYPE_F32", "llmint8_quantize_blockwise",
     "llmint8_dequantize_blockwise", "EXPORTED_SYMBOLS", "LLMINT8_DTYPE_BF16",
     "llmint8_quantize_weight_ex", "llmint8_linear_ex", "llmint8_linear_debug_ex",
+    "LLMINT8_QUANT_NF4", "LLMINT8_QUANT_FP4", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
+    "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -28,6 +30,8 @@ LLMINT8_PATH_GEMV = 2
 LLMINT8_DTYPE_F16 = 0
 LLMINT8_DTYPE_F32 = 1
 LLMINT8_DTYPE_BF16 = 2
+LLMINT8_QUANT_NF4 = 0
+LLMINT8_QUANT_FP4 = 1
 
 EXPORTED_SYMBOLS = (
     "llmint8_quantize_weight", "llmint8_workspace_bytes", "llmint8_linear",
@@ -36,7 +40,8 @@ EXPORTED_SYMBOLS = (
     "llmint8_dequantize_weight_t", "llmint8_linear_backward_input",
     "llmint8_linear_backward_input_timed", "llmint8_quantize_blockwise",
     "llmint8_dequantize_blockwise", "llmint8_quantize_weight_ex", "llmint8_linear_ex",
-    "llmint8_linear_debug_ex",
+    "llmint8_linear_debug_ex", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
+    "llmint8_dequantize_4bit", "llmint8_linear_4bit",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +108,15 @@ def load_library():
     lib.llmint8_linear_ex.restype = ctypes.c_int
     lib.llmint8_linear_debug_ex.argtypes = lin_ex + [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.llmint8_linear_debug_ex.restype = ctypes.c_int
+    lib.llmint8_code_book_4bit.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    lib.llmint8_code_book_4bit.restype = ctypes.c_int
+    lib.llmint8_quantize_4bit.argtypes = [_vp, ctypes.c_int, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]
+    lib.llmint8_quantize_4bit.restype = ctypes.c_int
+    lib.llmint8_dequantize_4bit.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_int, _vp, ctypes.c_int, _vp]
+    lib.llmint8_dequantize_4bit.restype = ctypes.c_int
+    lib.llmint8_linear_4bit.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64, ctypes.c_int,
+                                        _i64, _vp, _vp, _vp]
+    lib.llmint8_linear_4bit.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
     lib.llmint8_gemv_max_rows.restype = ctypes.c_int
     lib.llmint8_status_string.argtypes = [ctypes.c_int]
@@ -427,6 +441,118 @@ def llmint8_dequantize_blockwise(q, absmax, block: int = 4096, dtype=None, out=N
                                             _codec_dtype(out.dtype), _stream(stream, q.device)),
            "llmint8_dequantize_blockwise")
     return out
+
+
+def _quant_type(q):
+    if isinstance(q, str):
+        codes = {"nf4": LLMINT8_QUANT_NF4, "fp4": LLMINT8_QUANT_FP4}
+        if q.lower() not in codes:
+            raise ValueError(f"4-bit type: 'nf4' or 'fp4', got {q!r}")
+        return codes[q.lower()]
+    return int(q)
+
+
+def llmint8_code_book_4bit(quant_type="nf4"):
+    """The 16 fp32 levels of a 4-bit type, indexed by code (a host list)."""
+    vals = (ctypes.c_float * 16)()
+    _check(load_library().llmint8_code_book_4bit(_quant_type(quant_type), vals),
+           "llmint8_code_book_4bit")
+    return list(vals)
+
+
+def llmint8_quantize_4bit(W, block: int = 64, quant_type="nf4", packed=None, absmax=None,
+                          stream=None):
+    """Blockwise 4-bit codes of a contiguous fp16/bf16 tensor taken flat:
+    (packed uint8 [n / 2], absmax fp32 [ceil(n / block)])."""
+    import torch
+    lib = load_library()
+    if not (isinstance(W, torch.Tensor) and W.is_cuda and W.is_contiguous()):
+        raise ValueError("W: expected a contiguous CUDA tensor")
+    n = W.numel()
+    nb = -(-n // block)
+    if packed is None:
+        packed = torch.empty((n // 2,), dtype=torch.uint8, device=W.device)
+    if absmax is None:
+        absmax = torch.empty((nb,), dtype=torch.float32, device=W.device)
+    _need(packed, torch.uint8, (n // 2,), "packed")
+    _need(absmax, torch.float32, (nb,), "absmax")
+    _check(lib.llmint8_quantize_4bit(_ptr(W), _act_dtype(W.dtype), n, block, _quant_type(quant_type),
+                                     _ptr(packed), _ptr(absmax), _stream(stream, W.device)),
+           "llmint8_quantize_4bit")
+    return packed, absmax
+
+
+def llmint8_dequantize_4bit(packed, absmax, block: int = 64, quant_type="nf4", dtype=None,
+                            out=None, stream=None):
+    """Inverse of llmint8_quantize_4bit: fp16 (default) or bf16 [2 * packed.numel()]."""
+    import torch
+    lib = load_library()
+    n = 2 * packed.numel()
+    nb = -(-n // block)
+    _need(packed, torch.uint8, (n // 2,), "packed")
+    _need(absmax, torch.float32, (nb,), "absmax")
+    if out is None:
+        out = torch.empty((n,), dtype=dtype or torch.float16, device=packed.device)
+    if not (out.is_cuda and out.is_contiguous() and out.numel() == n):
+        raise ValueError("out: expected a contiguous CUDA tensor of n elements")
+    _check(lib.llmint8_dequantize_4bit(_ptr(packed), _ptr(absmax), n, block, _quant_type(quant_type),
+                                       _ptr(out), _act_dtype(out.dtype), _stream(stream, packed.device)),
+           "llmint8_dequantize_4bit")
+    return out
+
+
+def llmint8_linear_4bit(X, packed, absmax, N: int, block: int = 64, quant_type="nf4", bias=None,
+                        Y=None, stream=None):
+    """Y [T, N] = X [T, K] . Wdeq^T (+ bias) with the 4-bit weight [N, K] dequantized on the fly.
+    X, bias and Y share one type (fp16 or bf16)."""
+    import torch
+    lib = load_library()
+    T, K = X.shape
+    _need(X, X.dtype, (T, K), "X")
+    _need(packed, torch.uint8, (N * K // 2,), "packed")
+    _need(absmax, torch.float32, (-(-N * K // block),), "absmax")
+    if bias is not None:
+        _need(bias, X.dtype, (N,), "bias")
+    if Y is None:
+        Y = torch.empty((T, N), dtype=X.dtype, device=X.device)
+    _need(Y, X.dtype, (T, N), "Y")
+    _check(lib.llmint8_linear_4bit(_ptr(X), _act_dtype(X.dtype), T, K, _ptr(packed), _ptr(absmax),
+                                   block, _quant_type(quant_type), N, _ptr(bias), _ptr(Y),
+                                   _stream(stream, X.device)),
+           "llmint8_linear_4bit")
+    return Y
+
+
+class Linear4bit:
+    """Drop-in 4-bit (NF4 by default, or FP4) replacement of an fp16 or bf16 linear layer.
+
+    The weight is quantized blockwise once at construction ("bitsandbytes: GPU-
+    Accelerated Inference ...", introduction: the 4-bit layer keeps the weight
+    in blocks with their own scaling factors and computes in a 16-bit type with
+    the weight dequantized per operation); ``forward`` streams the codes and
+    never stores the dequantized weight. Activations, bias and output take the
+    weight's type.
+    """
+
+    def __init__(self, weight, bias=None, block: int = 64, quant_type="nf4"):
+        self.out_features, self.in_features = weight.shape
+        self.block, self.quant_type = int(block), quant_type
+        self.dtype = weight.dtype
+        self.packed, self.absmax = llmint8_quantize_4bit(weight.contiguous(), self.block, quant_type)
+        self.bias = None if bias is None else bias.detach().to(weight.dtype).contiguous()
+
+    def memory_bytes(self) -> int:
+        extra = 0 if self.bias is None else self.bias.numel() * 2
+        return self.packed.numel() + self.absmax.numel() * 4 + extra
+
+    def forward(self, X):
+        shape = X.shape
+        X2 = X.reshape(-1, self.in_features).contiguous()
+        Y = llmint8_linear_4bit(X2, self.packed, self.absmax, self.out_features, self.block,
+                                self.quant_type, bias=self.bias)
+        return Y.reshape(*shape[:-1], self.out_features)
+
+    __call__ = forward
 
 
 def _autograd_function():

@@ -360,6 +360,84 @@ llmint8_status llmint8_dequantize_blockwise(const int8_t* q, const float* absmax
                                                 static_cast<hipStream_t>(stream)));
 }
 
+static llmint8_status check_4bit(int dtype, int quant_type, int64_t n, int64_t block) {
+  if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_BF16) return LLMINT8_ERR_INVALID_ARG;
+  if (quant_type != LLMINT8_QUANT_NF4 && quant_type != LLMINT8_QUANT_FP4) return LLMINT8_ERR_INVALID_ARG;
+  if (n < 0 || block <= 0) return LLMINT8_ERR_INVALID_ARG;
+  if (block > 4096 || !blockwise_supported((int)block) || n % 16 != 0 || (double)n >= kTwo31)
+    return LLMINT8_ERR_UNSUPPORTED;
+  return LLMINT8_OK;
+}
+
+llmint8_status llmint8_code_book_4bit(int quant_type, float* values) {
+  if (!values) return LLMINT8_ERR_INVALID_ARG;
+  Code4 book;
+  if (!code_book_4bit(quant_type, &book)) return LLMINT8_ERR_INVALID_ARG;
+  for (int c = 0; c < 16; ++c) values[c] = book.value[c];
+  return LLMINT8_OK;
+}
+
+llmint8_status llmint8_quantize_4bit(const void* W, int dtype, int64_t n, int64_t block,
+                                     int quant_type, uint8_t* packed, float* absmax, void* stream) {
+  llmint8_status st = check_4bit(dtype, quant_type, n, block);
+  if (st != LLMINT8_OK) return st;
+  if (n == 0) return LLMINT8_OK;
+  if (!W || !packed || !absmax) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return LLMINT8_ERR_INVALID_ARG;
+  Code4 book;
+  code_book_4bit(quant_type, &book);
+  return hip_status(launch_quantize_4bit(static_cast<const uint16_t*>(W), dtype == LLMINT8_DTYPE_BF16,
+                                         (int)n, (int)block, book, packed, absmax, device_cu_count(),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+llmint8_status llmint8_dequantize_4bit(const uint8_t* packed, const float* absmax, int64_t n,
+                                       int64_t block, int quant_type, void* out, int dtype,
+                                       void* stream) {
+  llmint8_status st = check_4bit(dtype, quant_type, n, block);
+  if (st != LLMINT8_OK) return st;
+  if (n == 0) return LLMINT8_OK;
+  if (!packed || !absmax || !out) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(absmax, 4) || !aligned(out, 16)) return LLMINT8_ERR_INVALID_ARG;
+  Code4 book;
+  code_book_4bit(quant_type, &book);
+  return hip_status(launch_dequantize_4bit(packed, absmax, (int)n, (int)block, book,
+                                           static_cast<uint16_t*>(out), dtype == LLMINT8_DTYPE_BF16,
+                                           device_cu_count(), static_cast<hipStream_t>(stream)));
+}
+
+llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t T, int64_t K,
+                                   const uint8_t* packed, const float* absmax, int64_t block,
+                                   int quant_type, int64_t N, const void* bias, void* Y,
+                                   void* stream) {
+  if (T < 0 || K <= 0 || N <= 0) return LLMINT8_ERR_INVALID_ARG;
+  llmint8_status st = check_4bit(dtype, quant_type, 0, block);
+  if (st != LLMINT8_OK) return st;
+  if (K % 128 != 0 || (double)N * (double)K >= kTwo31 || (double)T * (double)K >= kTwo31)
+    return LLMINT8_ERR_UNSUPPORTED;
+  if (T == 0) return LLMINT8_OK;
+  if (!X || !packed || !absmax || !Y) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(Y, 2) ||
+      (bias && !aligned(bias, 2)))
+    return LLMINT8_ERR_INVALID_ARG;
+  Code4 book;
+  code_book_4bit(quant_type, &book);
+  int shift = 0;
+  while ((int64_t(1) << shift) < block) ++shift;
+  FourBitArgs a;
+  a.X = static_cast<const uint16_t*>(X);
+  a.W4 = packed;
+  a.absmax = absmax;
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.Y = static_cast<uint16_t*>(Y);
+  a.T = (int)T;
+  a.K = (int)K;
+  a.N = (int)N;
+  a.block_shift = shift;
+  return hip_status(launch_linear_4bit(a, book, dtype == LLMINT8_DTYPE_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int llmint8_gemv_max_rows(int64_t K) {
   if (K <= 0 || K % 16 != 0 || K > kMaxK) return 0;
   return gemv_max_rows((int)K);

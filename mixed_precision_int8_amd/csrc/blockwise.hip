@@ -19,13 +19,6 @@
 
 namespace llmint8 {
 
-template <int LPB>
-__device__ __forceinline__ uint32_t segment_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = LPB / 2; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
-}
-
 // 4 fp32 values -> 4 int8 codes rne(fl32(v * s)) in one word (|v * s| <= 127:
 // adding 1.5 * 2^23 leaves the integer, rounded half to even, in the low bits)
 __device__ __forceinline__ uint32_t quantize4_f32(const uint4& v, float s) {

@@ -47,6 +47,14 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return v;
 }
 
+// Maximum over aligned segments of LPB lanes (a power of two up to 64).
+template <int LPB>
+__device__ __forceinline__ uint32_t segment_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = LPB / 2; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
 // |x| codes of 8 16-bit values packed in a uint4, as 4 packed u16 pairs.
 __device__ __forceinline__ void abs_codes(const uint4& v, v2u16 out[4]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};

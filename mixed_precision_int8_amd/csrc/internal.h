@@ -110,4 +110,30 @@ hipError_t launch_quantize_blockwise(const void* x, bool f32, int n, int block, 
 hipError_t launch_dequantize_blockwise(const int8_t* q, const float* absmax, int n, int block,
                                        void* out, bool f32, int num_cus, hipStream_t stream);
 
+
+// 4-bit weights (NF4 / FP4): a code book and its quantizer's decision table.
+struct Code4 {
+  float value[16];   // value of each code
+  float mid[15];     // midpoints between adjacent distinct levels, ascending (+inf when unused)
+  uint32_t rank_lo;  // code of the level of rank r (r < 8) in nibble r
+  uint32_t rank_hi;  // code of the level of rank r (8 <= r < 16) in nibble r - 8
+};
+bool code_book_4bit(int quant_type, Code4* out);  // false for an unknown type (host)
+
+// Operands of the 4-bit linear Y = X . Wdeq^T (+ bias).
+struct FourBitArgs {
+  const uint16_t* X;     // [T, K], 16-bit
+  const uint8_t* W4;     // [N, K] codes, two per byte, even index in the low nibble
+  const float* absmax;   // one per block of the flat weight
+  const uint16_t* bias;  // [N] or null
+  uint16_t* Y;           // [T, N]
+  int T, K, N, block_shift;
+};
+hipError_t launch_quantize_4bit(const uint16_t* w, bool bf16, int n, int block, const Code4& book,
+                                uint8_t* packed, float* absmax, int num_cus, hipStream_t stream);
+hipError_t launch_dequantize_4bit(const uint8_t* packed, const float* absmax, int n, int block,
+                                  const Code4& book, uint16_t* out, bool bf16, int num_cus,
+                                  hipStream_t stream);
+hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, hipStream_t stream);
+
 }  // namespace llmint8

@@ -223,3 +223,44 @@ def test_ex_entry_points_argument_errors(lib):
     assert q(MISALIGNED, BF16, 16, 64, ALIGNED, ALIGNED, None) == INVALID
     # the codec takes fp16 or fp32, not bf16
     assert lib.llmint8_quantize_blockwise(ALIGNED, BF16, 4096, 64, ALIGNED, ALIGNED, None) == INVALID
+
+
+def test_4bit_code_books_match_the_oracle(lib):
+    import numpy as np
+    import oracle
+    for name, code in (("nf4", m8.LLMINT8_QUANT_NF4), ("fp4", m8.LLMINT8_QUANT_FP4)):
+        vals = (ctypes.c_float * 16)()
+        assert lib.llmint8_code_book_4bit(code, vals) == OK
+        got = np.array(list(vals), np.float32)
+        assert np.array_equal(got.view(np.uint32), oracle.code_book(name).view(np.uint32)), name
+    assert lib.llmint8_code_book_4bit(7, (ctypes.c_float * 16)()) == INVALID
+    assert lib.llmint8_code_book_4bit(0, None) == INVALID
+
+
+def test_4bit_argument_errors(lib):
+    F16, BF16, F32 = m8.LLMINT8_DTYPE_F16, m8.LLMINT8_DTYPE_BF16, m8.LLMINT8_DTYPE_F32
+    NF4, FP4 = m8.LLMINT8_QUANT_NF4, m8.LLMINT8_QUANT_FP4
+    q, d, lin = lib.llmint8_quantize_4bit, lib.llmint8_dequantize_4bit, lib.llmint8_linear_4bit
+    assert q(ALIGNED, F32, 4096, 64, NF4, ALIGNED, ALIGNED, None) == INVALID     # fp32 weight
+    assert q(ALIGNED, F16, 4096, 64, 5, ALIGNED, ALIGNED, None) == INVALID       # unknown type
+    assert q(None, F16, 4096, 64, NF4, ALIGNED, ALIGNED, None) == INVALID
+    assert q(MISALIGNED, BF16, 4096, 64, FP4, ALIGNED, ALIGNED, None) == INVALID
+    assert q(ALIGNED, F16, 4104, 64, NF4, ALIGNED, ALIGNED, None) == UNSUPPORTED  # n % 16
+    assert q(ALIGNED, F16, 4096, 32, NF4, ALIGNED, ALIGNED, None) == UNSUPPORTED  # block < 64
+    assert q(ALIGNED, F16, 4096, 96, NF4, ALIGNED, ALIGNED, None) == UNSUPPORTED
+    assert q(None, F16, 0, 64, NF4, None, None, None) == OK                        # empty: no-op
+    assert d(ALIGNED, ALIGNED, 4096, 64, NF4, MISALIGNED, F16, None) == INVALID
+    assert d(None, ALIGNED, 4096, 64, FP4, ALIGNED, BF16, None) == INVALID
+
+    def call(X=ALIGNED, dtype=F16, T=4, K=4096, block=64, qt=NF4, N=4096, bias=None, Y=ALIGNED):
+        return lin(X, dtype, T, K, ALIGNED, ALIGNED, block, qt, N, bias, Y, None)
+    assert call(dtype=F32) == INVALID
+    assert call(qt=9) == INVALID
+    assert call(X=None) == INVALID
+    assert call(X=MISALIGNED) == INVALID
+    assert call(bias=ctypes.c_void_p(P + 1)) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(K=4160) == UNSUPPORTED              # K % 128 != 0
+    assert call(block=100) == UNSUPPORTED
+    assert call(N=1 << 20, K=4096) == UNSUPPORTED   # N K >= 2^31
+    assert call(T=0, X=None, Y=None) == OK          # no-op

@@ -23,16 +23,13 @@ import pytest
 
 import oracle
 import workloads
+from parity_util import check_y
 
 torch = pytest.importorskip("torch")
 import mixed_precision_int8_amd as m8  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-F16_TOL = 1e-3
-BF16_TOL = 2.0 ** -7
-BF16_SLACK = 2.0 ** -16
-BF16_EXACT_FRACTION = 0.99
 GEMM, GEMV, AUTO = m8.LLMINT8_PATH_GEMM, m8.LLMINT8_PATH_GEMV, m8.LLMINT8_PATH_AUTO
 
 
@@ -67,33 +64,6 @@ def _host(t):
 
 def _bits16(a):
     return np.ascontiguousarray(a).view(np.uint16)
-
-
-def _ordered(bits):
-    b = bits.astype(np.int32)
-    mag = b & 0x7FFF
-    return np.where(b >> 15 != 0, -mag, mag)
-
-
-def check_y(Y, Y_ref, dtype):
-    """The Y bar above; returns the max-abs-relative error."""
-    if dtype == "f16":
-        err = oracle.parity_error(Y, Y_ref)
-        assert err <= F16_TOL, f"Y parity error {err}"
-        return err
-    got, want = oracle.bf16_bits_to_f32(Y), oracle.bf16_bits_to_f32(Y_ref)
-    err = oracle.parity_error(got, want)
-    assert err <= BF16_TOL, f"bf16 Y parity error {err}"
-    if Y.size == 0:
-        return err
-    steps = np.abs(_ordered(Y) - _ordered(Y_ref))
-    slack = BF16_SLACK * float(np.abs(want.astype(np.float64)).max())
-    far = (steps > 1) & (np.abs(got.astype(np.float64) - want) > slack)
-    assert not far.any(), f"{int(far.sum())} bf16 outputs more than one step away"
-    same = float(np.mean(Y == Y_ref))
-    assert same >= BF16_EXACT_FRACTION or int(np.sum(Y != Y_ref)) <= 1, \
-        f"only {same:.4f} of bf16 outputs bit-identical"
-    return err
 
 
 def quantize_weight_checked(W, dtype):

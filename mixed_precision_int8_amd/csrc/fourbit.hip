@@ -22,10 +22,10 @@
 // nibble. Dequantization: r16(fl32(value[code] * a)) in the 16-bit compute type.
 //
 // The linear Y = X . Wdeq^T (+ bias) streams the codes once: a workgroup owns
-// 16 weight rows and its 4 wavefronts split K. Each lane loads 16 bytes of codes
+// 16 weight rows and its 16 wavefronts split K. Each lane loads 16 bytes of codes
 // (32 codes of one row, one block) per 128-column step, dequantizes them through
 // a 16-entry table in LDS and feeds v_mfma_f32_16x16x32_{f16,bf16} with the
-// weight rows as A and up to 16 rows of X (read straight from L2) as B. The four
+// weight rows as A and up to 16 rows of X (read straight from L2) as B. The
 // partial sums are added in a fixed order through LDS, the bias is added and Y
 // is rounded once.
 #include <algorithm>
@@ -161,16 +161,43 @@ __global__ __launch_bounds__(256) void kq4_blockwise(const uint16_t* __restrict_
 
 // 8 codes (one word, element e in nibble e) -> 8 16-bit values r16(fl32(c * a)):
 // an fp32 multiply per value, then one packed conversion (v_cvt_pk_f16_f32 /
-// v_cvt_pk_bf16_f32, round to nearest even) per pair.
+// v_cvt_pk_bf16_f32, round to nearest even) per pair. The empty asm operands
+// keep each product an fp32 value: otherwise the compiler may fold multiply and
+// conversion into v_fma_mixlo_f16, which rounds the exact product to fp16 once
+// and differs from the two roundings whenever fl32(c * a) lands on an fp16
+// rounding midpoint.
+// Byte SEL of w times 4 in one instruction (an SDWA operand select): the LDS
+// byte offset of a table entry whose index sits alone in that byte.
+template <int SEL>
+__device__ __forceinline__ uint32_t byte_x4(uint32_t w) {
+  uint32_t r;
+  if constexpr (SEL == 0)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if constexpr (SEL == 1)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if constexpr (SEL == 2)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint4 dequant8(uint32_t cw, float a, const float* lut) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  // even codes alone in the bytes of `ev`, odd codes in `od`: one instruction per
+  // table address instead of a shift and a mask
+  const uint32_t ev = cw & 0x0f0f0f0fu, od = (cw >> 4) & 0x0f0f0f0fu;
+  const uint32_t ae[4] = {byte_x4<0>(ev), byte_x4<1>(ev), byte_x4<2>(ev), byte_x4<3>(ev)};
+  const uint32_t ao[4] = {byte_x4<0>(od), byte_x4<1>(od), byte_x4<2>(od), byte_x4<3>(od)};
+  const char* base = reinterpret_cast<const char*>(lut);
   uint32_t o[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float lo = lut[(cw >> (8 * p)) & 15u] * a;
-    const float hi = lut[(cw >> (8 * p + 4)) & 15u] * a;
+    float lo = *reinterpret_cast<const float*>(base + ae[p]) * a;
+    float hi = *reinterpret_cast<const float*>(base + ao[p]) * a;
+    asm volatile("" : "+v"(lo), "+v"(hi));
     if constexpr (BF16) {
       b2 v;
       v.x = (__bf16)lo;
@@ -207,21 +234,30 @@ __global__ __launch_bounds__(256) void kdq4_blockwise(const uint8_t* __restrict_
 
 // ------------------------------------------------------------------ the 4-bit linear
 
-constexpr int kN4Waves = 4;   // wavefronts per workgroup, splitting K
-constexpr int kN4Unroll = 4;  // 128-column steps in flight per wavefront
+constexpr int kN4Waves = 16;  // wavefronts per workgroup, splitting K
+constexpr int kN4Unroll = 2;  // 128-column steps in flight per wavefront
+// Two 1024-thread workgroups per CU need at most 64 VGPRs per lane (8 waves
+// per SIMD); at 65 or more only one fits and the kernel runs ~40% slower.
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void kn_gemv(FourBitArgs a, Code4 book) {
+__global__ __launch_bounds__(kN4Waves * 64) void kn_gemv(FourBitArgs a, Code4 book) {
   using A16 = Act16<BF16>;
   __shared__ float lut[16];
+  __shared__ float bias_l[16];
   __shared__ v4f part[kN4Waves][64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
   if (tid == 0) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) lut[c] = book.value[c];
   }
+  // the block's 16 bias values, staged before the main loop (read in the
+  // epilogue they would hold registers through it)
+  if (tid >= 64 && tid < 80) {
+    const int nb = n0 + tid - 64;
+    bias_l[tid - 64] = a.bias && nb < a.N ? A16::to_f32(a.bias[nb]) : 0.0f;
+  }
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
   const int K = a.K;
   const uint32_t row_bytes = (uint32_t)K / 2;
   const uint32_t nblocks = (uint32_t)(((size_t)a.N * K + (1u << a.block_shift) - 1) >> a.block_shift);
@@ -240,42 +276,55 @@ __global__ __launch_bounds__(256) void kn_gemv(FourBitArgs a, Code4 book) {
   const int s0 = min(steps, wave * per), s1 = min(steps, s0 + per);
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   __syncthreads();
-  for (int s = s0; s < s1; s += kN4Unroll) {
-    uint4 cw[kN4Unroll];
-    float sc[kN4Unroll];
-    uint4 xb[kN4Unroll][4];
+  struct Steps {
+    uint4 cw[kN4Unroll];     // codes
+    float sc[kN4Unroll];     // block maxima
+    uint4 xb[kN4Unroll][4];  // X fragments
+  };
+  auto load = [&](Steps& b, int s) {
 #pragma unroll
     for (int u = 0; u < kN4Unroll; ++u) {
       const int si = s + u;
       const bool ok = si < s1;
-      cw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rw, ok && wvalid ? wbase + 64u * si : kOobOffset, 0, 0));
-      sc[u] = __builtin_bit_cast(
+      b.cw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rw, ok && wvalid ? wbase + 64u * si : kOobOffset, 0, 0));
+      b.sc[u] = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(
                      ra, ok && wvalid ? ((ebase + 128u * si) >> a.block_shift) * 4u : kOobOffset, 0, 0));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xb[u][j] = __builtin_bit_cast(
+        b.xb[u][j] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
                        rx, ok && xvalid ? xbase + 256u * si + 16u * j : kOobOffset, 0, 0));
     }
+  };
+  auto compute = [&](const Steps& b) {
 #pragma unroll
     for (int u = 0; u < kN4Unroll; ++u) {
-      const uint32_t c[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+      const uint32_t c[4] = {b.cw[u].x, b.cw[u].y, b.cw[u].z, b.cw[u].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8<BF16>(c[j], sc[u], lut), xb[u][j], acc);
+      for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8<BF16>(c[j], b.sc[u], lut), b.xb[u][j], acc);
     }
+  };
+  // written as load + compute per iteration; the compiler rotates the loop so
+  // that the next iteration's loads are issued before this one's arithmetic
+  for (int s = s0; s < s1; s += kN4Unroll) {
+    Steps b;
+    load(b, s);
+    compute(b);
   }
   part[wave][lane] = acc;
   __syncthreads();
-  // output element (row 4 (l / 16) + v, column l % 16) of the 16 x 16 block,
-  // with l = tid % 64 and v = tid / 64
-  const int l = tid & 63, v = tid >> 6;
-  const float y = ((part[0][l][v] + part[1][l][v]) + part[2][l][v]) + part[3][l][v];
-  const int nn = n0 + 4 * (l >> 4) + v, tt = t0 + (l & 15);
-  if (nn < a.N && tt < a.T) {
-    const float b = a.bias ? A16::to_f32(a.bias[nn]) : 0.0f;
-    a.Y[(size_t)tt * a.N + nn] = A16::from_f32(y + b);
+  // threads 0..255: output element (row 4 (l / 16) + v, column l % 16) of the
+  // 16 x 16 block, l = tid % 64, v = tid / 64; partial sums added in wave order
+  for (int e = tid; e < 256; e += kN4Waves * 64) {
+    const int l = e & 63, v = e >> 6;
+    float y = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kN4Waves; ++w) y += part[w][l][v];
+    const int nl = 4 * (l >> 4) + v;
+    const int nn = n0 + nl, tt = t0 + (l & 15);
+    if (nn < a.N && tt < a.T) a.Y[(size_t)tt * a.N + nn] = A16::from_f32(y + bias_l[nl]);
   }
 }
 
@@ -340,9 +389,9 @@ hipError_t launch_dequantize_4bit(const uint8_t* packed, const float* absmax, in
 hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, hipStream_t stream) {
   const dim3 grid((a.N + 15) / 16, (a.T + 15) / 16);
   if (bf16) {
-    hipLaunchKernelGGL(kn_gemv<true>, grid, dim3(256), 0, stream, a, book);
+    hipLaunchKernelGGL(kn_gemv<true>, grid, dim3(kN4Waves * 64), 0, stream, a, book);
   } else {
-    hipLaunchKernelGGL(kn_gemv<false>, grid, dim3(256), 0, stream, a, book);
+    hipLaunchKernelGGL(kn_gemv<false>, grid, dim3(kN4Waves * 64), 0, stream, a, book);
   }
   return hipGetLastError();
 }

@@ -34,6 +34,23 @@ PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "kb_gemm_prefill_counters.txt")
 PROFILE_BWD_COUNTERS = os.path.join(ROOT, "profiles", "kg_backward_prefill_counters.txt")
 BWD_SOURCES = ("bwd.hip", "gemm_common.h", "device_util.h", "internal.h")
+PROFILE_NEXT_COUNTERS = os.path.join(ROOT, "profiles", "bf16_codec_nf4_counters.txt")
+NEXT_SOURCES = ("gemm.hip", "gemm_common.h", "blockwise.hip", "fourbit.hip", "device_util.h",
+                "internal.h")
+
+
+def roofline(bound, kernel, achieved, peak, unit, traffic, **extra):
+    """The roofline object of one kernel: achieved / peak, with the counter traffic."""
+    return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic, **extra}
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return os.cpu_count() or 1
 
 
 def parse():
@@ -264,10 +281,31 @@ def main():
         pms = timed_calls(lambda i: m8.llmint8_linear_ex(Xb, Wqb, sWb, thr, bias=biasb, Y=Yb,
                                                          workspace=ws),
                           args.steps, max(args.warmup, 20))
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for row in bev:          # torch creates the HIP event on its first record
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        nkb = 0
+        for row in bev:
+            nkb = m8.llmint8_linear_timed_ex(Xb, Wqb, sWb, thr, Yb, ws, row, bias=biasb)
+        torch.cuda.synchronize()
+        kms = [float(np.mean([r[i].elapsed_time(r[i + 1]) for r in bev])) for i in range(nkb)]
+        bgemm = kms[-1]
         bf = {"prefill": {"T": T, "K": K, "N": N, "ms_per_call": round(pms, 5),
                           "TOPS": round(ops / (pms * 1e-3) / 1e12, 2),
                           "pct_int8_peak": round(100.0 * ops / (pms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
-                          "fp16_no_bias_ms_per_call": round(ms_per_step, 5)}}
+                          "fp16_no_bias_ms_per_call": round(ms_per_step, 5),
+                          "kernels_ms": {n_: round(v, 5) for n_, v in
+                                         zip(["ka_scan", "ka_prepare", "kb_gemm"], kms)},
+                          "roofline": roofline("mfma", "kb_gemm (bf16 activations, bias)",
+                                               ops / (bgemm * 1e-3) / 1e12, PEAK_INT8_TOPS,
+                                               "TFLOP/s",
+                                               committed_traffic(PROFILE_NEXT_COUNTERS, NEXT_SOURCES,
+                                                                 "bf16_gemm_hbm_bytes_per_launch"),
+                                               unit_note="int8 tera-ops/s, 2 ops per multiply-add",
+                                               algorithmic_ops_per_launch=ops,
+                                               avg_launch_ms=round(bgemm, 5))}}
         if not args.no_decode:
             wd = workloads.CONFIGS["decode"]
             Wd3, X3, _, _ = workloads.make(wd, T=1)
@@ -361,10 +399,19 @@ def main():
                                                 "algorithmic_bytes": nbytes}
                 del outs
             del cps, pk, am
+        big = fb.get("large_layer_T1")
+        rl = None
+        if big:
+            rl = roofline("hbm", "kn_gemv (large layer, T = 1)", big["GB_per_s"], PEAK_HBM_GBS, "GB/s",
+                          committed_traffic(PROFILE_NEXT_COUNTERS, NEXT_SOURCES,
+                                            "nf4_large_hbm_bytes_per_launch"),
+                          algorithmic_bytes_per_launch=big["algorithmic_bytes"],
+                          avg_launch_us=big["us_per_call"])
         result["fourbit_nf4"] = {"workload": "NF4 weights, block 64, fp16 activations; the decode "
                                              "and large layers", "kernel": "kn_gemv",
                                  "bound": "hbm", "peak_GB_per_s": PEAK_HBM_GBS,
-                                 "timing": "whole calls between two events", **fb}
+                                 "timing": "whole calls (one kernel each) between two events",
+                                 "roofline": rl, **fb}
 
     # ---- input gradient through the frozen layer, at the prefill layer's shape
     if not args.no_backward:
@@ -468,19 +515,24 @@ def main():
                         "us_per_call": round(us, 2), "GB_per_s": round(gbs, 1),
                         "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2), "bytes": nbytes[op]}
             del ins, qs, ams, outs
+        q64 = codec["f16_weight_block64_quantize"]
         result["blockwise_codec"] = {"workload": f"{N * K} elements (the prefill weight, and an fp32 "
                                                  "state of the same size)", "bound": "hbm",
-                                     "copies_cycled": copies, "peak_GB_per_s": PEAK_HBM_GBS, **codec}
+                                     "copies_cycled": copies, "peak_GB_per_s": PEAK_HBM_GBS,
+                                     "roofline": roofline(
+                                         "hbm", "kq_blockwise (fp16, block 64)", q64["GB_per_s"],
+                                         PEAK_HBM_GBS, "GB/s",
+                                         committed_traffic(PROFILE_NEXT_COUNTERS, NEXT_SOURCES,
+                                                           "codec_quantize_hbm_bytes_per_launch"),
+                                         algorithmic_bytes_per_launch=q64["bytes"],
+                                         avg_launch_us=q64["us_per_call"]),
+                                     **codec}
         del tensors
 
     # ---- CPU oracle baseline on this host (bounded: the full prefill call once)
     if not args.no_cpu:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # noqa: BLE001
-            threads = os.cpu_count() or 1
+        threads = oracle_threads()
         Yg = Y.cpu().numpy()
         c0 = time.perf_counter()
         Wq_ref, sW_ref = oracle.quantize_weight(W)
@@ -498,13 +550,46 @@ def main():
         if "bf16_bias" in result:
             rows = np.sort(np.random.default_rng(w.seed + 1).choice(T, size=16, replace=False))
             Wqb_ref, sWb_ref = oracle.quantize_weight(Wb_np, "bf16")
+            c5 = time.perf_counter()
             stb = oracle.linear(Xb_np, Wqb_ref, sWb_ref, thr, rows=rows, dtype="bf16", bias=bias_np)
+            c6 = time.perf_counter()
+            result["bf16_bias"]["cpu_oracle"] = {
+                "value": round(2.0 * len(rows) * N * K / (c6 - c5) / 1e12, 5), "unit": "TOPS",
+                "cores": threads, "kind": "oracle",
+                "sample": f"{len(rows)} output rows of the bf16 prefill call (the outlier scan and "
+                          f"activation quantization cover all {T} rows), {c6 - c5:.2f} s"}
             Ybg = Yb.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
             result["bf16_bias"]["parity"] = {
                 "Y_max_abs_rel_err_sampled_rows": oracle.parity_error(
                     oracle.bf16_bits_to_f32(Ybg), oracle.bf16_bits_to_f32(stb.Y)),
                 "Y_bit_identical_fraction": float(np.mean(Ybg == stb.Y)), "rows": len(rows),
                 "weight_codes_identical": bool(np.array_equal(Wqb.cpu().numpy(), Wqb_ref))}
+        if "blockwise_codec" in result:
+            sl = W[: (1 << 24) // K]                 # 16 M elements of the fp16 weight
+            c7 = time.perf_counter()
+            qc, ac = oracle.quantize_blockwise(sl, 64)
+            c8 = time.perf_counter()
+            oracle.dequantize_blockwise(qc, ac, 64)
+            c9 = time.perf_counter()
+            nq = sl.size
+            result["blockwise_codec"]["cpu_oracle"] = {
+                "value": round((3 * nq + 4 * nq // 64) / (c8 - c7) / 1e9, 3), "unit": "GB/s",
+                "dequantize_GB_per_s": round((3 * nq + 4 * nq // 64) / (c9 - c8) / 1e9, 3),
+                "cores": threads, "kind": "oracle",
+                "sample": f"quantize then dequantize {nq} fp16 elements, block 64"}
+        if "fourbit_nf4" in result:
+            wd4 = workloads.CONFIGS["decode"]
+            W4 = workloads.make_weight(workloads.rng_for(wd4.seed, 0), wd4.N, wd4.K, wd4.sigma)
+            X4 = workloads.make(wd4, T=1, with_weight=False)[1]
+            p4, a4 = oracle.quantize_4bit(W4, 64, "nf4")
+            c10 = time.perf_counter()
+            oracle.linear_4bit(X4, p4, a4, 64, "nf4", wd4.N)
+            c11 = time.perf_counter()
+            nb4 = wd4.N * wd4.K // 2 + 4 * wd4.N * wd4.K // 64 + 2 * wd4.K + 2 * wd4.N
+            result["fourbit_nf4"]["cpu_oracle"] = {
+                "value": round(nb4 / (c11 - c10) / 1e9, 4), "unit": "GB/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"one NF4 linear of the decode layer (T=1, K=N={wd4.K}), {c11 - c10:.2f} s"}
         if "backward_input" in result:
             # oracle input gradient on a seeded sample of rows: parity, and its CPU rate
             rows = np.sort(np.random.default_rng(w.seed).choice(T, size=64, replace=False))

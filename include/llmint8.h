@@ -234,7 +234,8 @@ LLMINT8_API llmint8_status llmint8_dequantize_blockwise(const int8_t* q, const f
  *          added to the fp32 sum before the single rounding of Y:
  *          Y = r16( C * a[t] * b[n] / 127^2 + X[:,O] . Wd^T + bias[n] )
  * Other arguments and rules as for llmint8_quantize_weight / llmint8_linear /
- * llmint8_linear_debug; an unknown dtype is LLMINT8_ERR_INVALID_ARG.
+ * llmint8_linear_timed / llmint8_linear_debug; an unknown dtype is
+ * LLMINT8_ERR_INVALID_ARG.
  */
 LLMINT8_API llmint8_status llmint8_quantize_weight_ex(const void* W, int dtype, int64_t N, int64_t K,
                                                       int8_t* Wq, float* sW, void* stream);
@@ -242,6 +243,12 @@ LLMINT8_API llmint8_status llmint8_linear_ex(const void* X, int dtype, int64_t T
                                              const int8_t* Wq, const float* sW, int64_t N,
                                              float threshold, const void* bias, void* Y,
                                              void* workspace, size_t workspace_bytes, void* stream);
+LLMINT8_API llmint8_status llmint8_linear_timed_ex(const void* X, int dtype, int64_t T, int64_t K,
+                                                   const int8_t* Wq, const float* sW, int64_t N,
+                                                   float threshold, const void* bias, void* Y,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   void* stream, int path, void* const* events,
+                                                   int n_events, int* kernels_launched);
 LLMINT8_API llmint8_status llmint8_linear_debug_ex(const void* X, int dtype, int64_t T, int64_t K,
                                                    const int8_t* Wq, const float* sW, int64_t N,
                                                    float threshold, const void* bias, void* Y,

@@ -21,7 +21,7 @@ __all__ = [
     "llmint8_dequantize_blockwise", "EXPORTED_SYMBOLS", "LLMINT8_DTYPE_BF16",
     "llmint8_quantize_weight_ex", "llmint8_linear_ex", "llmint8_linear_debug_ex",
     "LLMINT8_QUANT_NF4", "LLMINT8_QUANT_FP4", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
-    "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit",
+    "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit", "llmint8_linear_timed_ex",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "llmint8_linear_backward_input_timed", "llmint8_quantize_blockwise",
     "llmint8_dequantize_blockwise", "llmint8_quantize_weight_ex", "llmint8_linear_ex",
     "llmint8_linear_debug_ex", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
-    "llmint8_dequantize_4bit", "llmint8_linear_4bit",
+    "llmint8_dequantize_4bit", "llmint8_linear_4bit", "llmint8_linear_timed_ex",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +107,9 @@ def load_library():
     lib.llmint8_linear_ex.argtypes = lin_ex
     lib.llmint8_linear_ex.restype = ctypes.c_int
     lib.llmint8_linear_debug_ex.argtypes = lin_ex + [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.llmint8_linear_timed_ex.argtypes = lin_ex + [ctypes.c_int, ctypes.POINTER(_vp), ctypes.c_int,
+                                                     ctypes.POINTER(ctypes.c_int)]
+    lib.llmint8_linear_timed_ex.restype = ctypes.c_int
     lib.llmint8_linear_debug_ex.restype = ctypes.c_int
     lib.llmint8_code_book_4bit.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
     lib.llmint8_code_book_4bit.restype = ctypes.c_int
@@ -267,6 +270,25 @@ def llmint8_linear_ex(X, Wq, sW, threshold: float = 6.0, bias=None, Y=None, work
                                  _stream(stream, X.device)),
            "llmint8_linear_ex")
     return Y
+
+
+def llmint8_linear_timed_ex(X, Wq, sW, threshold, Y, workspace, events, bias=None,
+                            path=LLMINT8_PATH_AUTO, stream=None):
+    """llmint8_linear_ex recording ``events`` (created torch.cuda.Event) around each kernel.
+
+    Returns the number of kernels launched.
+    """
+    lib = load_library()
+    code = _act_dtype(X.dtype)
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias)
+    handles = (_vp * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    nk = ctypes.c_int(0)
+    _check(lib.llmint8_linear_timed_ex(_ptr(X), code, T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(bias),
+                                       _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream, X.device), int(path), handles, len(events),
+                                       ctypes.byref(nk)),
+           "llmint8_linear_timed_ex")
+    return nk.value
 
 
 def _debug_outputs(T, K, N, dev, want_C):

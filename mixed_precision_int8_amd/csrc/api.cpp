@@ -267,6 +267,19 @@ llmint8_status llmint8_linear_debug_ex(const void* X, int dtype, int64_t T, int6
                     dtype, bias);
 }
 
+llmint8_status llmint8_linear_timed_ex(const void* X, int dtype, int64_t T, int64_t K,
+                                       const int8_t* Wq, const float* sW, int64_t N, float threshold,
+                                       const void* bias, void* Y, void* workspace,
+                                       size_t workspace_bytes, void* stream, int path,
+                                       void* const* events, int n_events, int* kernels_launched) {
+  if (!events || n_events < 2) return LLMINT8_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events && i < 4; ++i)
+    if (!events[i]) return LLMINT8_ERR_INVALID_ARG;
+  return run_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, stream, path,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, events, n_events,
+                    kernels_launched, dtype, bias);
+}
+
 llmint8_status llmint8_linear_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
                                     const float* sW, int64_t N, float threshold, void* Y,
                                     void* workspace, size_t workspace_bytes, void* stream,

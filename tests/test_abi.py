@@ -264,3 +264,17 @@ def test_4bit_argument_errors(lib):
     assert call(block=100) == UNSUPPORTED
     assert call(N=1 << 20, K=4096) == UNSUPPORTED   # N K >= 2^31
     assert call(T=0, X=None, Y=None) == OK          # no-op
+
+
+def test_timed_ex_argument_errors(lib):
+    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    t = lib.llmint8_linear_timed_ex
+    ev = (ctypes.c_void_p * 4)(P, P, P, P)
+    nk = ctypes.c_int(0)
+    base = [ALIGNED, m8.LLMINT8_DTYPE_BF16, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, None, ALIGNED,
+            ALIGNED, need, None]
+    assert t(*base, 0, None, 4, ctypes.byref(nk)) == INVALID
+    assert t(*base, m8.LLMINT8_PATH_GEMM, ev, 2, ctypes.byref(nk)) == INVALID   # 3 kernels, 4 events
+    bad = list(base)
+    bad[1] = 9
+    assert t(*bad, m8.LLMINT8_PATH_GEMM, ev, 4, ctypes.byref(nk)) == INVALID   # unknown dtype

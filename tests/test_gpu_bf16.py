@@ -239,3 +239,22 @@ def test_bf16_prefill_workload():
     _, c = run_case("bf16 prefill", W, X, w.threshold, AUTO, "bf16", bias=b,
                     rows=_sample_rows(w.T, 48, 11))
     assert c >= w.n_out
+
+
+def test_timed_ex_records_kernel_events():
+    W, X = _as("bf16", *_small(256, 1024, 512, seed=52))
+    b = _bias(6, 512, "bf16")
+    _say("timed_ex bf16 + bias")
+    Wq, sW = m8.llmint8_quantize_weight_ex(_dev(W))
+    Xd, bd = _dev(X), _dev(b)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    ws = torch.empty((m8.llmint8_workspace_bytes(256, 1024, 512),), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((256, 512), dtype=torch.bfloat16, device="cuda")
+    nk = m8.llmint8_linear_timed_ex(Xd, Wq, sW, 6.0, Y, ws, ev, bias=bd, path=GEMM)
+    torch.cuda.synchronize()
+    assert nk == 3
+    assert all(ev[i].elapsed_time(ev[i + 1]) >= 0 for i in range(3))
+    Y2 = m8.llmint8_linear_ex(Xd, Wq, sW, 6.0, bias=bd, workspace=ws)
+    assert np.array_equal(_host(Y), _host(Y2))

@@ -48,7 +48,7 @@ reason, in the design notes):
       stored weight dequantized per operation, ``Wdeq = fp16(fl32(fl32(q * b) /
       127))`` for every entry (as in R7); quantizing X has no useful derivative.
       ``dX = fp16(dY . Wdeq)``: fp16 operands, a wide accumulation, one
-      rounding to fp16.
+      rounding to fp16. With bf16 activations (B2) dY, Wdeq and dX are bf16.
 
 * B2  bf16 activations: with ``dtype="bf16"`` X, the bias and Y are bfloat16
       (carried here as uint16 bit patterns). Every bf16 value is exact in
@@ -329,25 +329,34 @@ def parity_error(Y_test: np.ndarray, Y_ref: np.ndarray) -> float:
     return float(np.abs(a[fin] - r[fin]).max() / den)
 
 
-def dequantize_weight(Wq: np.ndarray, sW: np.ndarray) -> np.ndarray:
-    """The stored weight dequantized per operation ([DCT-S]; R7, B1).
+def dequantize_weight(Wq: np.ndarray, sW: np.ndarray, dtype: str = "f16") -> np.ndarray:
+    """The stored weight dequantized per operation ([DCT-S]; R7, B1, B2).
 
-    ``Wdeq[n, k] = fp16(fl32(fl32(Wq[n, k] * sW[n]) / 127))`` for every entry;
-    the outlier operand ``Wd`` of the forward is its columns at the outliers.
+    ``Wdeq[n, k] = r16(fl32(fl32(Wq[n, k] * sW[n]) / 127))`` for every entry,
+    ``r16`` the rounding to fp16 (or, with ``dtype="bf16"``, to bf16 bit
+    patterns); the outlier operand ``Wd`` of the forward is its columns at the
+    outliers.
     """
     q32 = np.asarray(Wq).astype(np.float32)
-    return ((q32 * np.asarray(sW, dtype=np.float32)[:, None]) / _F32_127).astype(np.float16)
+    d32 = (q32 * np.asarray(sW, dtype=np.float32)[:, None]) / _F32_127
+    if dtype == "bf16":
+        return f32_to_bf16_bits(d32)
+    return d32.astype(np.float16)
 
 
-def linear_backward_input(dY16: np.ndarray, Wq: np.ndarray, sW: np.ndarray) -> np.ndarray:
+def linear_backward_input(dY16: np.ndarray, Wq: np.ndarray, sW: np.ndarray,
+                          dtype: str = "f16") -> np.ndarray:
     """Input gradient of the frozen layer, the step that lets an adapter train on top of it ([HFQ-T]; B1).
 
-    ``dX = fp16( dY @ Wdeq )`` with ``Wdeq = dequantize_weight(Wq, sW)``: the
-    fp16 products are exact in float64, the sum is formed in float64 and the
-    result is rounded once to fp16.
+    ``dX = r16( dY @ Wdeq )`` with ``Wdeq = dequantize_weight(Wq, sW, dtype)``:
+    the 16-bit products are exact in float64, the sum is formed in float64 and
+    the result is rounded once to the 16-bit type (fp16, or bf16 as bit
+    patterns with ``dtype="bf16"``, where dY is bf16 bit patterns too: B2).
     """
-    Wd = dequantize_weight(Wq, sW)
-    dX64 = np.asarray(dY16).astype(np.float64) @ Wd.astype(np.float64)
+    Wd = dequantize_weight(Wq, sW, dtype)
+    dX64 = _to_f64(np.asarray(dY16), dtype) @ _to_f64(Wd, dtype)
+    if dtype == "bf16":
+        return f64_to_bf16_bits(dX64)
     with np.errstate(over="ignore"):
         return dX64.astype(np.float16)
 

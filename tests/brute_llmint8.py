@@ -149,18 +149,21 @@ def forward(X, W, thr, bf16_io=False, bias=None):
             "Y": [[y for _, y in r] for r in Y], "Y_exact": [[e for e, _ in r] for r in Y]}
 
 
-def backward_input(dY, Wq, sW):
+def backward_input(dY, Wq, sW, to_bf16=False):
     """Input gradient through the frozen layer, for tiny inputs.
 
-    dY: T x N list of fp16-valued floats; Wq: N x K list of ints; sW: N floats.
-    Each dequantized entry is fp16(fl32(fl32(q * b) / 127)) (fp32 product and
-    quotient by the rounding facts above); the sum over n of dY * Wdeq is an
-    exact Fraction, rounded once to fp16.
+    dY: T x N list of fp16-valued (bf16-valued with ``to_bf16``) floats; Wq:
+    N x K list of ints; sW: N floats. Each dequantized entry is
+    r16(fl32(fl32(q * b) / 127)) (fp32 product and quotient by the rounding
+    facts above); the sum over n of dY * Wdeq is an exact Fraction, rounded
+    once to the 16-bit type.
     """
+    r16 = bf16 if to_bf16 else f16
+    r16_exact = bf16_of_fraction if to_bf16 else f16_of_fraction
     T = len(dY)
     N = len(Wq)
     K = len(Wq[0]) if N else 0
-    Wdeq = [[f16(f32(f32(Wq[n][k] * sW[n]) / 127.0)) for k in range(K)] for n in range(N)]
+    Wdeq = [[r16(f32(f32(Wq[n][k] * sW[n]) / 127.0)) for k in range(K)] for n in range(N)]
     dX = []
     for t in range(T):
         row = []
@@ -168,7 +171,7 @@ def backward_input(dY, Wq, sW):
             acc = Fraction(0)
             for n in range(N):
                 acc += Fraction(dY[t][n]) * Fraction(Wdeq[n][k])
-            row.append(f16_of_fraction(acc))
+            row.append(r16_exact(acc))
         dX.append(row)
     return Wdeq, dX
 

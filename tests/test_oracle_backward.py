@@ -69,6 +69,57 @@ def test_p12_bruteforce_twin_tiny_shapes():
     assert not bad, bad[:3]
 
 
+def _bf16(a):
+    b = np.ascontiguousarray(np.asarray(a, np.float32)).view(np.uint32)
+    return (b >> np.uint32(16)).astype(np.uint16)             # truncation: exact bf16 inputs
+
+
+def _check_twin_bf16(bw=None, deq=None):
+    bw = bw or oracle.linear_backward_input
+    deq = deq or oracle.dequantize_weight
+    bad = []
+    for dY, W in _tiny_cases():
+        Wb, dYb = _bf16(W.astype(np.float32)), _bf16(dY.astype(np.float32))
+        Wq, sW = oracle.quantize_weight(Wb, "bf16")
+        dY_vals = oracle.bf16_bits_to_f32(dYb).astype(float).tolist()
+        Wd_ref, dX_ref = brute.backward_input(dY_vals, Wq.astype(int).tolist(),
+                                              sW.astype(float).tolist(), to_bf16=True)
+        if oracle.bf16_bits_to_f32(deq(Wq, sW, "bf16")).astype(float).tolist() != Wd_ref:
+            bad.append(("Wdeq", W.shape))
+        if oracle.bf16_bits_to_f32(bw(dYb, Wq, sW, "bf16")).astype(float).tolist() != dX_ref:
+            bad.append(("dX", dY.shape, W.shape))
+    return bad
+
+
+def test_p12_bf16_twin_tiny_shapes():
+    """P12 with bf16 activations (B2): Wdeq and dX rounded to bf16 equal the exact twin."""
+    bad = _check_twin_bf16()
+    assert not bad, bad[:3]
+
+
+def test_p12_bf16_planted_mistakes_are_caught():
+    """Rounding Wdeq through fp16, or the sum to fp16, in bf16 mode fails the bf16 twin."""
+    good_deq = oracle.dequantize_weight
+
+    def deq_via_fp16(Wq, sW, dtype="f16"):
+        d = good_deq(Wq, sW, "f16").astype(np.float32)
+        return oracle.f32_to_bf16_bits(d) if dtype == "bf16" else d.astype(np.float16)
+
+    def bw_fp16_sum(dY, Wq, sW, dtype="f16"):
+        Wd = oracle.bf16_bits_to_f32(good_deq(Wq, sW, "bf16")).astype(np.float64)
+        out = (oracle.bf16_bits_to_f32(dY).astype(np.float64) @ Wd).astype(np.float16)
+        return oracle.f32_to_bf16_bits(out.astype(np.float32))
+
+    def bw_via(deq):
+        def f(dY, Wq, sW, dtype="f16"):
+            Wd = oracle.bf16_bits_to_f32(deq(Wq, sW, "bf16")).astype(np.float64)
+            return oracle.f64_to_bf16_bits(oracle.bf16_bits_to_f32(dY).astype(np.float64) @ Wd)
+        return f
+
+    assert _check_twin_bf16(bw=bw_via(deq_via_fp16), deq=deq_via_fp16)
+    assert _check_twin_bf16(bw=bw_fp16_sum)
+
+
 def _p13(fn=None):
     bw = fn or oracle.linear_backward_input
     rng = np.random.default_rng(13)

@@ -188,6 +188,25 @@ LLMINT8_API llmint8_status llmint8_linear_backward_input_timed(
 LLMINT8_API llmint8_status llmint8_dequantize_weight_t(const int8_t* Wq, const float* sW, int64_t N,
                                                        int64_t K, void* WdT, void* stream);
 
+/*
+ * The input gradient and the transposed dequantization in a chosen 16-bit
+ * type (dtype LLMINT8_DTYPE_F16 or LLMINT8_DTYPE_BF16; constants below): dY,
+ * WdT and dX are of that type, WdT = r16(fl32(fl32(Wq * b) / 127)) and
+ * dX = r16(dY . Wdeq) with fp32 sums, r16 rounding to that type ("Hugging Face
+ * Quantization with bitsandbytes ...", section 5: bfloat16 as the compute
+ * type). Arguments, workspace and rules otherwise as for
+ * llmint8_linear_backward_input / llmint8_dequantize_weight_t; an unknown
+ * dtype is LLMINT8_ERR_INVALID_ARG.
+ */
+LLMINT8_API llmint8_status llmint8_linear_backward_input_ex(const void* dY, int dtype, int64_t T,
+                                                            int64_t K, const int8_t* Wq,
+                                                            const float* sW, int64_t N, void* dX,
+                                                            void* workspace, size_t workspace_bytes,
+                                                            void* stream);
+LLMINT8_API llmint8_status llmint8_dequantize_weight_t_ex(const int8_t* Wq, const float* sW,
+                                                          int64_t N, int64_t K, void* WdT,
+                                                          int dtype, void* stream);
+
 /* Element types: activations (the _ex entry points: F16 or BF16) and the
  * blockwise codec (F16 or F32). */
 #define LLMINT8_DTYPE_F16  0 /* IEEE binary16 */

@@ -22,6 +22,7 @@ __all__ = [
     "llmint8_quantize_weight_ex", "llmint8_linear_ex", "llmint8_linear_debug_ex",
     "LLMINT8_QUANT_NF4", "LLMINT8_QUANT_FP4", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit", "llmint8_linear_timed_ex",
+    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "llmint8_dequantize_blockwise", "llmint8_quantize_weight_ex", "llmint8_linear_ex",
     "llmint8_linear_debug_ex", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "llmint8_linear_timed_ex",
+    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +98,11 @@ def load_library():
     lib.llmint8_linear_backward_input_timed.argtypes = bwd + [ctypes.POINTER(_vp), ctypes.c_int,
                                                               ctypes.POINTER(ctypes.c_int)]
     lib.llmint8_linear_backward_input_timed.restype = ctypes.c_int
+    lib.llmint8_linear_backward_input_ex.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64,
+                                                     _vp, _vp, ctypes.c_size_t, _vp]
+    lib.llmint8_linear_backward_input_ex.restype = ctypes.c_int
+    lib.llmint8_dequantize_weight_t_ex.argtypes = [_vp, _vp, _i64, _i64, _vp, ctypes.c_int, _vp]
+    lib.llmint8_dequantize_weight_t_ex.restype = ctypes.c_int
     lib.llmint8_quantize_blockwise.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _vp]
     lib.llmint8_quantize_blockwise.restype = ctypes.c_int
     lib.llmint8_dequantize_blockwise.argtypes = [_vp, _vp, _i64, _i64, _vp, ctypes.c_int, _vp]
@@ -376,16 +383,17 @@ def llmint8_dequantize_weight_t(Wq, sW, WdT=None, stream=None):
     return WdT
 
 
-def _backward_args(dY, Wq, sW, dX, workspace):
+def _backward_args(dY, Wq, sW, dX, workspace, dtype=None):
     import torch
     T, N = dY.shape
     K = Wq.shape[1]
-    _need(dY, torch.float16, (T, N), "dY")
+    dtype = dtype or torch.float16
+    _need(dY, dtype, (T, N), "dY")
     _need(Wq, torch.int8, (N, K), "Wq")
     _need(sW, torch.float32, (N,), "sW")
     if dX is None:
-        dX = torch.empty((T, K), dtype=torch.float16, device=dY.device)
-    _need(dX, torch.float16, (T, K), "dX")
+        dX = torch.empty((T, K), dtype=dtype, device=dY.device)
+    _need(dX, dtype, (T, K), "dX")
     if workspace is None:
         need = llmint8_backward_workspace_bytes(T, K, N)
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dY.device)
@@ -401,6 +409,35 @@ def llmint8_linear_backward_input(dY, Wq, sW, dX=None, workspace=None, stream=No
                                              _stream(stream, dY.device)),
            "llmint8_linear_backward_input")
     return dX
+
+
+def llmint8_linear_backward_input_ex(dY, Wq, sW, dX=None, workspace=None, stream=None):
+    """dX [T, K] = dY [T, N] . Wdeq in the type of dY (fp16 or bf16)."""
+    lib = load_library()
+    code = _act_dtype(dY.dtype)
+    T, K, N, dX, ws = _backward_args(dY, Wq, sW, dX, workspace, dY.dtype)
+    _check(lib.llmint8_linear_backward_input_ex(_ptr(dY), code, T, K, _ptr(Wq), _ptr(sW), N,
+                                                _ptr(dX), _ptr(ws), ws.numel() * ws.element_size(),
+                                                _stream(stream, dY.device)),
+           "llmint8_linear_backward_input_ex")
+    return dX
+
+
+def llmint8_dequantize_weight_t_ex(Wq, sW, dtype=None, WdT=None, stream=None):
+    """(Wq int8 [N, K], sW fp32 [N]) -> WdT [K, N] in ``dtype`` (fp16 default, or bf16)."""
+    import torch
+    lib = load_library()
+    N, K = Wq.shape
+    dtype = dtype or torch.float16
+    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(sW, torch.float32, (N,), "sW")
+    if WdT is None:
+        WdT = torch.empty((K, N), dtype=dtype, device=Wq.device)
+    _need(WdT, dtype, (K, N), "WdT")
+    _check(lib.llmint8_dequantize_weight_t_ex(_ptr(Wq), _ptr(sW), N, K, _ptr(WdT), _act_dtype(dtype),
+                                              _stream(stream, Wq.device)),
+           "llmint8_dequantize_weight_t_ex")
+    return WdT
 
 
 def llmint8_linear_backward_input_timed(dY, Wq, sW, events, dX=None, workspace=None, stream=None):
@@ -592,9 +629,11 @@ def _autograd_function():
         @staticmethod
         def backward(ctx, dY):
             layer = ctx.layer
-            if dY.dtype != torch.float16:
-                raise NotImplementedError("Int8Linear backward: fp16 gradients only")
-            dX = llmint8_linear_backward_input(dY.contiguous(), layer.Wq, layer.sW)
+            dY = dY.contiguous().to(layer.dtype)
+            if layer.dtype == torch.float16:
+                dX = llmint8_linear_backward_input(dY, layer.Wq, layer.sW)
+            else:
+                dX = llmint8_linear_backward_input_ex(dY, layer.Wq, layer.sW)
             return dX, None
 
     return _Int8LinearFn
@@ -615,9 +654,10 @@ class Int8Linear:
     introduction: quantization happens when the model loads); ``forward`` runs
     the LLM.int8() forward ("Hugging Face Quantization with bitsandbytes",
     sections 2 and 3; section 5 for bf16 as the compute type) with the bias
-    added before the output's rounding, and, for fp16 inputs that require a
-    gradient, registers the input-gradient kernels as its backward (same page,
-    section 6: the int8 weights stay frozen while an adapter on top is trained).
+    added before the output's rounding, and, for inputs that require a
+    gradient, registers the input-gradient kernels (fp16 or bf16) as its backward
+    (same page, section 6: the int8 weights stay frozen while an adapter on top
+    is trained).
     Activations, bias and output take the weight's type.
     """
 

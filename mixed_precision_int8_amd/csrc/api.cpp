@@ -175,14 +175,16 @@ llmint8_status check_backward_sizes(int64_t T, int64_t K, int64_t N) {
 
 size_t backward_workspace(int64_t K, int64_t N) { return align_up((size_t)2 * N * K, kWsAlign); }
 
-// dX = dY . Wdeq: dequantize-transpose into the workspace, then the fp16 GEMM.
+// dX = dY . Wdeq: dequantize-transpose into the workspace, then the 16-bit GEMM.
 llmint8_status run_backward_input(const void* dY, int64_t T, int64_t K, const int8_t* Wq,
                                   const float* sW, int64_t N, void* dX, void* workspace,
                                   size_t workspace_bytes, void* stream_ptr, void* const* events,
-                                  int n_events, int* kernels_launched) {
+                                  int n_events, int* kernels_launched,
+                                  int dtype = LLMINT8_DTYPE_F16) {
   if (kernels_launched) *kernels_launched = 0;
   llmint8_status st = check_backward_sizes(T, K, N);
   if (st != LLMINT8_OK) return st;
+  if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_BF16) return LLMINT8_ERR_INVALID_ARG;
   if (!Wq || !sW || !aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
   if (events && n_events < 3) return LLMINT8_ERR_INVALID_ARG;
   if (T == 0) return LLMINT8_OK;
@@ -201,8 +203,10 @@ llmint8_status run_backward_input(const void* dY, int64_t T, int64_t K, const in
   a.T = (int)T;
   a.K = (int)K;
   a.N = (int)N;
+  a.bf16 = dtype == LLMINT8_DTYPE_BF16 ? 1 : 0;
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_dequant_t(Wq, sW, (int)N, (int)K, static_cast<uint16_t*>(workspace), stream);
+  if (e == hipSuccess)
+    e = launch_dequant_t(Wq, sW, (int)N, (int)K, static_cast<uint16_t*>(workspace), a.bf16 != 0, stream);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_gemm_f16(a, device_cu_count(), stream);
   if (e == hipSuccess) e = mark(2);
@@ -311,14 +315,28 @@ size_t llmint8_backward_workspace_bytes(int64_t T, int64_t K, int64_t N) {
   return backward_workspace(K, N);
 }
 
-llmint8_status llmint8_dequantize_weight_t(const int8_t* Wq, const float* sW, int64_t N, int64_t K,
-                                           void* WdT, void* stream) {
+llmint8_status llmint8_dequantize_weight_t_ex(const int8_t* Wq, const float* sW, int64_t N,
+                                              int64_t K, void* WdT, int dtype, void* stream) {
   llmint8_status st = check_backward_sizes(0, K, N);
   if (st != LLMINT8_OK) return st;
+  if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_BF16) return LLMINT8_ERR_INVALID_ARG;
   if (!Wq || !sW || !WdT) return LLMINT8_ERR_INVALID_ARG;
   if (!aligned(Wq, 16) || !aligned(sW, 4) || !aligned(WdT, 16)) return LLMINT8_ERR_INVALID_ARG;
   return hip_status(launch_dequant_t(Wq, sW, (int)N, (int)K, static_cast<uint16_t*>(WdT),
-                                     static_cast<hipStream_t>(stream)));
+                                     dtype == LLMINT8_DTYPE_BF16, static_cast<hipStream_t>(stream)));
+}
+
+llmint8_status llmint8_dequantize_weight_t(const int8_t* Wq, const float* sW, int64_t N, int64_t K,
+                                           void* WdT, void* stream) {
+  return llmint8_dequantize_weight_t_ex(Wq, sW, N, K, WdT, LLMINT8_DTYPE_F16, stream);
+}
+
+llmint8_status llmint8_linear_backward_input_ex(const void* dY, int dtype, int64_t T, int64_t K,
+                                                const int8_t* Wq, const float* sW, int64_t N,
+                                                void* dX, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  return run_backward_input(dY, T, K, Wq, sW, N, dX, workspace, workspace_bytes, stream, nullptr, 0,
+                            nullptr, dtype);
 }
 
 llmint8_status llmint8_linear_backward_input(const void* dY, int64_t T, int64_t K, const int8_t* Wq,

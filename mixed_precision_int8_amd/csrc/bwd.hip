@@ -5,13 +5,17 @@
 // flow through them). The stored weight is dequantized for the operation
 // ("bitsandbytes" glossary, "Where it fits in the stack"):
 //
-//   WdT[k][n] = fp16(fl32(fl32(Wq[n][k] * b[n]) / 127))          kg_dequant_t
-//   dX[t][k]  = fp16( sum_n dY[t][n] * WdT[k][n] )  (fp32 sums)   kg_gemm_f16
+//   WdT[k][n] = r16(fl32(fl32(Wq[n][k] * b[n]) / 127))           kg_dequant_t
+//   dX[t][k]  = r16( sum_n dY[t][n] * WdT[k][n] )  (fp32 sums)    kg_gemm_f16
 //
-// The transposed copy makes both GEMM operands contiguous along the reduction
-// (n), so the fp16 product runs on the same direct-to-LDS K loop as the int8
-// forward (gemm_common.h) with v_mfma_f32_32x32x16_f16: a 32-byte k-step is
-// 16 halves instead of 32 int8 values.
+// r16 is the rounding to the 16-bit activation type: fp16, or bf16 where that
+// is the compute type ("Hugging Face Quantization with bitsandbytes ...",
+// section 5). The transposed copy makes both GEMM operands contiguous along
+// the reduction (n), so the 16-bit product runs on the same direct-to-LDS K
+// loop as the int8 forward (gemm_common.h) with v_mfma_f32_32x32x16_{f16,bf16}:
+// a 32-byte k-step is 16 halves instead of 32 int8 values.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace llmint8 {
@@ -21,13 +25,15 @@ namespace llmint8 {
 // block: it reads 64 weight rows of 128 bytes (whole cache lines), converts
 // them into an LDS tile [k][n] and writes 128 rows of WdT, 128 bytes each.
 // One multiply by fl32(1/127) replaces the division: for every scale that
-// weight quantization produces (an fp16 value, stored as fp32) and every code
-// the fp16 result is the same as the division's (checked exhaustively on the
-// host by the test suite).
+// weight quantization produces (an fp16 or bf16 value, stored as fp32) and
+// every code, the 16-bit result is the same as the division's (checked
+// exhaustively on the host by the test suite; for fp16 also when the product
+// is rounded to fp16 only once, as v_fma_mixlo_f16 does).
 // ---------------------------------------------------------------------------
 constexpr int kDqN = 64, kDqK = 128;
 constexpr int kDqLd = kDqN + 2;  // halves per LDS row: 132 bytes, rows k and k+16 on different banks
 
+template <bool BF16>
 __global__ __launch_bounds__(256) void kg_dequant_t(const int8_t* __restrict__ Wq,
                                                     const float* __restrict__ sW, int N, int K,
                                                     uint16_t* __restrict__ WdT) {
@@ -46,7 +52,7 @@ __global__ __launch_bounds__(256) void kg_dequant_t(const int8_t* __restrict__ W
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int q = (int)(int8_t)((w[i >> 2] >> ((i & 3) * 8)) & 0xffu);
-        tile[(c * 16 + i) * kDqLd + r] = float_to_half_bits(((float)q * b) * (1.0f / 127.0f));
+        tile[(c * 16 + i) * kDqLd + r] = Act16<BF16>::from_f32(((float)q * b) * (1.0f / 127.0f));
       }
     }
   }
@@ -72,18 +78,23 @@ __global__ __launch_bounds__(256) void kg_dequant_t(const int8_t* __restrict__ W
 }
 
 hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uint16_t* WdT,
-                            hipStream_t stream) {
+                            bool bf16, hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, kDqN), (unsigned)ceil_div(K, kDqK));
-  hipLaunchKernelGGL(kg_dequant_t, grid, dim3(256), 0, stream, Wq, sW, N, K, WdT);
+  if (bf16)
+    hipLaunchKernelGGL(kg_dequant_t<true>, grid, dim3(256), 0, stream, Wq, sW, N, K, WdT);
+  else
+    hipLaunchKernelGGL(kg_dequant_t<false>, grid, dim3(256), 0, stream, Wq, sW, N, K, WdT);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// fp16 GEMM dX = dY . WdT^T: WdT rows (output columns k) are the A operand, dY
-// rows (output rows t) the B operand, both 2N bytes long.
+// 16-bit GEMM dX = dY . WdT^T: WdT rows (output columns k) are the A operand,
+// dY rows (output rows t) the B operand, both 2N bytes long.
 // ---------------------------------------------------------------------------
-template <class G>
+template <class G, bool BF16>
 __global__ __launch_bounds__(G::kThreads, 1) void kg_gemm_f16(BwdArgs a, int tiles_t, int group_n) {
+  using A16 = Act16<BF16>;
+  using Mma = typename std::conditional<BF16, MmaBF16, MmaF16>::type;
   __shared__ __attribute__((aligned(1024))) char smem[G::LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -98,7 +109,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void kg_gemm_f16(BwdArgs a, int til
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.dY + (size_t)t0 * N, (uint32_t)(rows_t * Kb));
 
   v16f acc[G::FN][G::FT];
-  gemm_kloop<G, MmaF16>(smem, rA, rB, Kb, wave, lane, acc, [] {});
+  gemm_kloop<G, Mma>(smem, rA, rB, Kb, wave, lane, acc, [] {});
 
   // Output block layout: lane holds, for row t = lane&31, columns
   // k = 8*q + 4*(lane>>5) + r in register 4*q + r (q, r = 0..3).
@@ -116,10 +127,10 @@ __global__ __launch_bounds__(G::kThreads, 1) void kg_gemm_f16(BwdArgs a, int til
         const int k = kl + i * 32 + 8 * q;
         if (k >= K) continue;  // K % 16 == 0: the 4 columns are all in range
         uint2 p;
-        p.x = (uint32_t)float_to_half_bits(acc[i][j][4 * q]) |
-              ((uint32_t)float_to_half_bits(acc[i][j][4 * q + 1]) << 16);
-        p.y = (uint32_t)float_to_half_bits(acc[i][j][4 * q + 2]) |
-              ((uint32_t)float_to_half_bits(acc[i][j][4 * q + 3]) << 16);
+        p.x = (uint32_t)A16::from_f32(acc[i][j][4 * q]) |
+              ((uint32_t)A16::from_f32(acc[i][j][4 * q + 1]) << 16);
+        p.y = (uint32_t)A16::from_f32(acc[i][j][4 * q + 2]) |
+              ((uint32_t)A16::from_f32(acc[i][j][4 * q + 3]) << 16);
         *reinterpret_cast<uint2*>(a.dX + (size_t)t * K + k) = p;
       }
     }
@@ -129,7 +140,10 @@ __global__ __launch_bounds__(G::kThreads, 1) void kg_gemm_f16(BwdArgs a, int til
 template <class G>
 hipError_t launch_gemm_f16_tile(const BwdArgs& a, hipStream_t stream, int group_n) {
   const int tk = (a.K + G::BN - 1) / G::BN, tt = (a.T + G::BT - 1) / G::BT;
-  hipLaunchKernelGGL(kg_gemm_f16<G>, dim3(tk * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
+  if (a.bf16)
+    hipLaunchKernelGGL((kg_gemm_f16<G, true>), dim3(tk * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
+  else
+    hipLaunchKernelGGL((kg_gemm_f16<G, false>), dim3(tk * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
   return hipGetLastError();
 }
 

@@ -103,6 +103,15 @@ struct MmaF16 {
   }
 };
 
+struct MmaBF16 {
+  typedef v16f acc_t;
+  static __device__ __forceinline__ acc_t zero() { return MmaF16::zero(); }
+  static __device__ __forceinline__ acc_t run(v4i a, v4i b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                    __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  }
+};
+
 // Tile order. Hardware deals blocks round-robin over the 8 XCDs; each XCD gets
 // a contiguous run of tile ids. Ids are then grouped: group_n A row-blocks
 // sweep all B row-blocks with A fastest, so the tiles an XCD runs concurrently

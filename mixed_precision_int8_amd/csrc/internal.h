@@ -84,10 +84,11 @@ struct LinearArgs {
 // Operands of the input gradient dX = dY . Wdeq (WdT: the dequantized weight,
 // transposed, in the workspace).
 struct BwdArgs {
-  const uint16_t* dY;  // fp16 [T, N]
-  const uint16_t* WdT; // fp16 [K, N]
-  uint16_t* dX;        // fp16 [T, K]
+  const uint16_t* dY;  // 16-bit [T, N]
+  const uint16_t* WdT; // 16-bit [K, N]
+  uint16_t* dX;        // 16-bit [T, K]
   int T, K, N;
+  int bf16;            // 16-bit type: 0 fp16, 1 bf16
 };
 
 // Launchers (each enqueues exactly one kernel on `stream`).
@@ -101,7 +102,7 @@ hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream);
 int gemv_max_rows(int K);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uint16_t* WdT,
-                            hipStream_t stream);
+                            bool bf16, hipStream_t stream);
 hipError_t launch_gemm_f16(const BwdArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_f16_variant(const BwdArgs& a, int variant, hipStream_t stream);
 bool blockwise_supported(int block);  // a power of two in [64, 4096]

@@ -139,3 +139,78 @@ def test_int8linear_autograd_uses_the_kernels():
     assert torch.equal(X.grad.view(torch.int16), ref.view(torch.int16))
     Y2 = m8.llmint8_linear(X.detach(), layer.Wq, layer.sW, 6.0)
     assert torch.equal(Y.detach().view(torch.int16), Y2.view(torch.int16))
+
+
+# --------------------------------------------------------------------------- bf16 (reading B2 on B1)
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _bf16_host(t):
+    torch.cuda.synchronize()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _weights_bf16(seed, N, K, sigma=0.02):
+    W = workloads.as_bf16_input(workloads.make_weight(workloads.rng_for(seed, 0), N, K, sigma))
+    Wq_ref, sW_ref = oracle.quantize_weight(W, "bf16")
+    return _dev(Wq_ref), _dev(sW_ref), Wq_ref, sW_ref
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (200, 336), (8, 16), (1000, 1040), (11008, 4096)])
+def test_dequantize_transposed_bf16_bit_exact(N, K):
+    _say(f"dequantize_weight_t_ex bf16 N={N} K={K}")
+    Wq, sW, Wq_ref, sW_ref = _weights_bf16(23, N, K)
+    WdT = _bf16_host(m8.llmint8_dequantize_weight_t_ex(Wq, sW, dtype=torch.bfloat16))
+    ref = oracle.dequantize_weight(Wq_ref, sW_ref, "bf16").T
+    assert np.array_equal(WdT, np.ascontiguousarray(ref))
+
+
+@pytest.mark.parametrize("T,K,N", [(16, 1024, 1024), (37, 336, 200), (300, 512, 264),
+                                   (1, 4096, 4096), (257, 144, 520), (5, 16, 8)])
+def test_backward_input_bf16_parity(T, K, N):
+    from parity_util import check_y
+    _say(f"backward_input_ex bf16 T={T} K={K} N={N}")
+    Wq, sW, Wq_ref, sW_ref = _weights_bf16(24, N, K)
+    dY = workloads.as_bf16_input(workloads.make_output_grad(24, T, N))
+    dX = _bf16_host(m8.llmint8_linear_backward_input_ex(_bf16_dev(dY), Wq, sW))
+    ref = oracle.linear_backward_input(dY, Wq_ref, sW_ref, "bf16")
+    check_y(dX, ref, "bf16")
+    # the fp16 entry through _ex equals the plain entry point
+    dYh = workloads.make_output_grad(24, T, N)
+    Wq2, sW2, _, _ = _weights(24, N, K)
+    a = _host(m8.llmint8_linear_backward_input_ex(_dev(dYh), Wq2, sW2)).view(np.uint16)
+    b = _host(m8.llmint8_linear_backward_input(_dev(dYh), Wq2, sW2)).view(np.uint16)
+    assert np.array_equal(a, b)
+
+
+def test_backward_input_bf16_prefill_layer_sampled_rows():
+    from parity_util import check_y
+    w = workloads.CONFIGS["prefill"]
+    _say(f"backward_input_ex bf16 prefill layer T={w.T} K={w.K} N={w.N}")
+    Wq, sW, Wq_ref, sW_ref = _weights_bf16(w.seed, w.N, w.K, w.sigma)
+    dY = workloads.as_bf16_input(workloads.make_output_grad(w.seed, w.T, w.N))
+    dX = _bf16_host(m8.llmint8_linear_backward_input_ex(_bf16_dev(dY), Wq, sW))
+    rows = np.unique(np.concatenate([np.sort(np.random.default_rng(9).choice(w.T, 32, replace=False)),
+                                     [0, w.T - 1]]))
+    ref = oracle.linear_backward_input(dY[rows], Wq_ref, sW_ref, "bf16")
+    check_y(np.ascontiguousarray(dX[rows]), ref, "bf16")
+
+
+def test_int8linear_bf16_autograd_uses_the_kernels():
+    _say("Int8Linear bf16 autograd")
+    N, K, T = 264, 512, 24
+    W = workloads.as_bf16_input(workloads.make_weight(workloads.rng_for(25, 0), N, K, 0.05))
+    layer = m8.Int8Linear(_bf16_dev(W), threshold=6.0)
+    X = workloads.as_bf16_input(workloads.make(
+        workloads.Workload("g", T=T, K=K, N=N, sigma=0.05, n_out=3, lo=20, hi=60, threshold=6.0,
+                           seed=25), with_weight=False)[1])
+    Xd = _bf16_dev(X).requires_grad_(True)
+    Y = layer(Xd.reshape(2, T // 2, K))
+    gY = _bf16_dev(workloads.as_bf16_input(workloads.make_output_grad(25, T, N))).reshape(2, T // 2, N)
+    Y.backward(gY)
+    got = _bf16_host(Xd.grad.detach().contiguous())
+    want = _bf16_host(m8.llmint8_linear_backward_input_ex(gY.reshape(T, N).contiguous(),
+                                                          layer.Wq, layer.sW))
+    assert np.array_equal(got, want)

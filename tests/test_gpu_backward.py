@@ -214,3 +214,14 @@ def test_int8linear_bf16_autograd_uses_the_kernels():
     want = _bf16_host(m8.llmint8_linear_backward_input_ex(gY.reshape(T, N).contiguous(),
                                                           layer.Wq, layer.sW))
     assert np.array_equal(got, want)
+
+
+def test_backward_input_maximum_n():
+    """N = 65536, the largest reduction length the input gradient takes."""
+    from parity_util import check_y
+    T, K, N = 9, 64, 65536
+    _say(f"backward_input T={T} K={K} N={N}")
+    Wq, sW, Wq_ref, sW_ref = _weights(26, N, K)
+    dY = workloads.make_output_grad(26, T, N)
+    dX = _host(m8.llmint8_linear_backward_input(_dev(dY), Wq, sW))
+    check_y(dX, oracle.linear_backward_input(dY, Wq_ref, sW_ref), "f16")

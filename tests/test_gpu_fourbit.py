@@ -197,3 +197,10 @@ def test_repeat_calls_bit_identical_and_module():
     ref = oracle.linear_4bit(X, p_ref, a_ref, 64, "nf4", 300, "f16", workloads.make_bias(9, 300))
     check_y(Y, ref, "f16")
     assert layer.memory_bytes() == 300 * 1024 // 2 + 4 * (300 * 1024 // 64) + 2 * 300
+
+
+@pytest.mark.parametrize("quant_type", ["nf4", "fp4"])
+def test_linear_long_rows(quant_type):
+    """K = 65536: each of the 16 wavefronts of a row block walks 32 steps."""
+    W, X = _weights(67, 40, 65536, 0.02), _acts(68, 3, 65536)
+    linear_case("K=65536", W, X, 256, quant_type, "f16", bias=workloads.make_bias(69, 40))

@@ -246,3 +246,25 @@ def test_sweep_workload(n_out):
     W, X, _, _ = workloads.make(w)
     for thr in workloads.SWEEP_THRESHOLDS:
         run_case(f"sweep n_out={n_out}", W, X, thr, AUTO, rows=_sample_rows(w.T, 16, 3 + n_out))
+
+
+# --------------------------------------------------------------------------- limits
+
+def test_maximum_k():
+    """K = 65536, the largest K the library takes: the bitmap prefix tables fill
+    LDS and no rows fit the fused decode kernel, so every T goes to the GEMM."""
+    assert m8.llmint8_gemv_max_rows(65536) == 0
+    W, X = _small(5, 65536, 72, seed=65, n_out=20)
+    _, c = run_case("K=65536", W, X, 6.0, AUTO, check_auto=True)
+    assert c >= 20
+
+
+def test_many_outliers_at_large_k():
+    """|O| in the thousands: the gather beyond the LDS index table (binary search
+    over the bitmap prefix) and 32-column chunks far apart."""
+    rng = _rng(66)
+    X = workloads.random_fp16(rng, (9, 16384), 1.0)
+    X[3, ::3] = np.float16(9.0)                     # 5462 outlier columns
+    W = workloads.random_fp16(rng, (40, 16384), 0.02)
+    _, c = run_case("|O|=5462", W, X, 6.0, GEMM)
+    assert c >= 5461

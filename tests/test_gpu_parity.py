@@ -156,6 +156,16 @@ def test_threshold_ties_and_zero_rows(path):
     assert c == 2
 
 
+@pytest.mark.parametrize("path", [GEMM, GEMV])
+def test_single_outlier_column(path):
+    rng = _rng(6)
+    X = np.clip(workloads.random_fp16(rng, (13, 384), 1.0).astype(np.float32), -5, 5).astype(np.float16)
+    X[6, 201] = np.float16(-37.5)                 # |O| = 1, in one row only
+    W = workloads.random_fp16(rng, (88, 384), 0.05)
+    _, c = run_case("|O|=1", W, X, 6.0, path)
+    assert c == 1
+
+
 def test_integer_inputs_quantize_exactly():
     rng = _rng(9)
     X = rng.integers(-127, 128, size=(20, 128)).astype(np.float16)

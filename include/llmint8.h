@@ -69,6 +69,13 @@ typedef int llmint8_status;
 #define LLMINT8_PATH_AUTO 0 /* what llmint8_linear uses */
 #define LLMINT8_PATH_GEMM 1 /* scan + quantize + int8 MFMA GEMM (3 kernels), any T */
 #define LLMINT8_PATH_GEMV 2 /* one fused weight-streaming kernel, small T only */
+/* The GEMM route with a fixed output tile (N x T) instead of the one the
+ * host's cost model picks: for tests and tuning, debug and timed calls only. */
+#define LLMINT8_PATH_GEMM_256x256 16
+#define LLMINT8_PATH_GEMM_192x256 17
+#define LLMINT8_PATH_GEMM_256x128 18
+#define LLMINT8_PATH_GEMM_128x128 19
+#define LLMINT8_PATH_GEMM_352x256 20
 
 /*
  * Vector-wise int8 quantization of a weight, done once when a layer is loaded
@@ -112,7 +119,8 @@ LLMINT8_API llmint8_status llmint8_linear(const void* X, int64_t T, int64_t K, c
  * results, taken from the same kernels llmint8_linear runs. Every output
  * pointer below may be NULL (not written).
  *   path            LLMINT8_PATH_AUTO / _GEMM / _GEMV (GEMV needs
- *                   T <= llmint8_gemv_max_rows(K); else LLMINT8_ERR_UNSUPPORTED)
+ *                   T <= llmint8_gemv_max_rows(K); else LLMINT8_ERR_UNSUPPORTED),
+ *                   or LLMINT8_PATH_GEMM_<tile> (the GEMM route with that tile)
  *   outlier_bitmap  uint32 [ceil(K/32)]: bit h%32 of word h/32 set iff h in O
  *   outlier_idx     int32 [K]: ascending outlier columns in the first |O| slots
  *   outlier_count   int32 [1]: |O|

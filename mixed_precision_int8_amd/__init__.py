@@ -12,7 +12,8 @@ import math
 import os
 
 __all__ = [
-    "LLMINT8_PATH_AUTO", "LLMINT8_PATH_GEMM", "LLMINT8_PATH_GEMV", "Llmint8Error",
+    "LLMINT8_PATH_AUTO", "LLMINT8_PATH_GEMM", "LLMINT8_PATH_GEMV", "LLMINT8_PATH_GEMM_TILES",
+    "Llmint8Error",
     "library_path", "load_library", "llmint8_quantize_weight", "llmint8_workspace_bytes",
     "llmint8_linear", "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
     "llmint8_status_string", "llmint8_backward_workspace_bytes", "llmint8_dequantize_weight_t",
@@ -28,6 +29,8 @@ __all__ = [
 LLMINT8_PATH_AUTO = 0
 LLMINT8_PATH_GEMM = 1
 LLMINT8_PATH_GEMV = 2
+# the GEMM route with a fixed output tile (N x T), for tests and tuning
+LLMINT8_PATH_GEMM_TILES = {"256x256": 16, "192x256": 17, "256x128": 18, "128x128": 19, "352x256": 20}
 LLMINT8_DTYPE_F16 = 0
 LLMINT8_DTYPE_F32 = 1
 LLMINT8_DTYPE_BF16 = 2

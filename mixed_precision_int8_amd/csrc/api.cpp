@@ -97,7 +97,16 @@ LinearArgs make_args(const void* X, int64_t T, int64_t K, const int8_t* Wq, cons
 
 int choose_path(int path, int64_t T, int64_t K) {
   if (path == LLMINT8_PATH_AUTO) return T <= gemv_max_rows((int)K) ? LLMINT8_PATH_GEMV : LLMINT8_PATH_GEMM;
-  return path;
+  return path == LLMINT8_PATH_GEMV ? LLMINT8_PATH_GEMV : LLMINT8_PATH_GEMM;
+}
+
+static_assert(LLMINT8_PATH_GEMM_352x256 - LLMINT8_PATH_GEMM_256x256 + 1 == kGemmTiles,
+              "one path value per GEMM tile, in the order of launch_gemm's candidates");
+// A forced GEMM tile from the path argument, or -1 (the cost model picks).
+int forced_tile(int path) {
+  return path >= LLMINT8_PATH_GEMM_256x256 && path < LLMINT8_PATH_GEMM_256x256 + kGemmTiles
+             ? path - LLMINT8_PATH_GEMM_256x256
+             : -1;
 }
 
 // The whole forward; `events` (nullable) are recorded around each kernel.
@@ -112,7 +121,8 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   llmint8_status st = validate_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes,
                                       dtype, bias);
   if (st != LLMINT8_OK) return st;
-  if (path != LLMINT8_PATH_AUTO && path != LLMINT8_PATH_GEMM && path != LLMINT8_PATH_GEMV)
+  if (path != LLMINT8_PATH_AUTO && path != LLMINT8_PATH_GEMM && path != LLMINT8_PATH_GEMV &&
+      forced_tile(path) < 0)
     return LLMINT8_ERR_INVALID_ARG;
   const int route = choose_path(path, T, K);
   if (route == LLMINT8_PATH_GEMV && T > gemv_max_rows((int)K)) return LLMINT8_ERR_UNSUPPORTED;
@@ -146,7 +156,7 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_prepare(a, groups, cus, stream);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_gemm(a, cus, stream);
+  if (e == hipSuccess) e = launch_gemm(a, cus, stream, forced_tile(path));
   if (e == hipSuccess) e = mark(3);
   if (e != hipSuccess) return hip_status(e);
   if (kernels_launched) *kernels_launched = 3;

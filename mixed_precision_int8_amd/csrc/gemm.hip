@@ -15,103 +15,52 @@
 // vector-wise scales (one per row of X, one per output row of W).
 //
 // Design (CDNA4): a workgroup of 4 or 8 wavefronts owns a BN x BT output tile
-// (BN along N, BT along T); each wavefront keeps its (BN/WAVES_N) x
-// (BT/WAVES_T) int32 accumulators in registers as 32x32 MFMA blocks
-// (v_mfma_i32_32x32x32_i8 runs at twice the int8 rate of the 16x16x64 form on
-// gfx950). Both operands are K-contiguous, the natural MFMA layout; the K loop
-// (direct-to-LDS copy ring, swizzled fragments, XCD-aware tile order) is the
-// shared one of gemm_common.h, with Wq rows as A and Xq rows as B.
+// (BN along N, BT along T); each wavefront keeps its share of the int32
+// accumulators in registers as 32x32 MFMA blocks (v_mfma_i32_32x32x32_i8 runs
+// at twice the int8 rate of the 16x16x64 form on gfx950). Both operands are
+// K-contiguous, the natural MFMA layout; the K loops (direct-to-LDS copy ring,
+// swizzled fragments, XCD-aware tile order) are those of gemm_common.h, with
+// Wq rows as A and Xq rows as B. kb_gemm takes the evenly split tiles;
+// kb_gemm_split the 352 x 256 tile, whose 11 row blocks split 6 + 5 over the
+// two wavefront columns, so that 256 tiles of it cover a 2048 x 11008 output
+// in one round of the 256 CUs.
 #include "gemm_common.h"
 
 namespace llmint8 {
 
-template <class G, bool BF16>
-__global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tiles_t, int group_n) {
+// Epilogue of one wavefront: its FNW x FT accumulator blocks, weight rows
+// nw0.. and activation rows tw0.. of the output. sW_w / aX_w / bias_w point at
+// the wavefront's first entries of the tile's scales and bias in LDS (bias_w
+// null without bias). `wf(i, h)` / `xf(j, h)` give the 16-bit operands of the
+// first chunk of 32 outlier columns (k-step h of block i / j); later chunks
+// are read from memory here. Output layout of a 32x32 block: lane holds, for
+// column (t) lane&31, rows (n) 8*q + 4*(lane>>5) + r in register 4*q + r.
+template <bool BF16, int FNW, int FT, class WF, class XF>
+__device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&acc)[FNW][FT], int nw0,
+                                              int tw0, const float* sW_w, const float* aX_w,
+                                              const uint16_t* bias_w, int nch, int lane, WF&& wf,
+                                              XF&& xf) {
   using A16 = Act16<BF16>;
-  __shared__ __attribute__((aligned(1024))) char smem[G::LDS + (G::BN + G::BT) * 4 + G::BN * 2];
-  // the tile's weight and activation scales and bias, read by the epilogue
-  float* sW_l = reinterpret_cast<float*>(smem + G::LDS);
-  float* aX_l = sW_l + G::BN;
-  uint16_t* bias_l = reinterpret_cast<uint16_t*>(aX_l + G::BT);
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave % G::WAVES_N, wt = wave / G::WAVES_N;
-
-  const TileCoords tc = tile_coords<G>(a.N, tiles_t, group_n);
-  const int K = a.K, N = a.N, T = a.T;
-  const int n0 = tc.a0, t0 = tc.b0;
-  const int rows_n = min(G::BN, N - n0), rows_t = min(G::BT, T - t0);
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.Wq + (size_t)n0 * K, (uint32_t)(rows_n * K));
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.Xq + (size_t)t0 * K, (uint32_t)(rows_t * K));
-
-  uint16_t bias_v = 0;  // requested before the K loop, written to LDS after it
-  auto scales_to_lds = [&]() {
-    if (a.bias && tid < G::BN && n0 + tid < N) bias_v = a.bias[n0 + tid];
-    // scales -> LDS by direct copy (rows past the matrix read as zero). They
-    // are issued before the first K stage, so the stage waits cover them.
-    constexpr int CS = (G::BN + 63) / 64, CX = (G::BT + 63) / 64;
-    const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.sW + n0, (uint32_t)(rows_n * 4));
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.aX + t0, (uint32_t)(rows_t * 4));
-    for (int c = wave; c < CS + CX; c += G::NWAVES) {
-      const bool is_w = c < CS;  // wave-uniform
-      const int cc = is_w ? c : c - CS;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          is_w ? rS : rX, (__attribute__((address_space(3))) void*)((is_w ? sW_l : aX_l) + cc * 64),
-          4, (uint32_t)((cc * 64 + lane) * 4), 0, 0, 0);
-    }
-  };
-  v16i acc[G::FN][G::FT];
-  gemm_kloop<G, MmaI8>(smem, rA, rB, K, wave, lane, acc, scales_to_lds);
+  const int N = a.N, T = a.T;
   const int fi = lane & 31, fg = lane >> 5;
-  if (a.bias) {  // uniform
-    if (tid < G::BN) bias_l[tid] = bias_v;
-    __syncthreads();
-  }
-
-  // ---- epilogue, one 32-row block of n at a time. Output layout of a 32x32
-  // block: lane holds, for column (t) lane&31, rows (n) 8*q + 4*(lane>>5) + r
-  // in register 4*q + r (q, r = 0..3).
-  const int nl = n0 + wn * G::WN + 4 * fg;  // + i*32 + 8*q + r
-  const int tl = t0 + wt * G::WT + fi;      // + j*32
-  float as[G::FT];
+  const int nl = nw0 + 4 * fg;  // + i*32 + 8*q + r
+  const int tl = tw0 + fi;      // + j*32
+  float as[FT];
 #pragma unroll
-  for (int j = 0; j < G::FT; ++j) as[j] = aX_l[wt * G::WT + fi + j * 32];
+  for (int j = 0; j < FT; ++j) as[j] = aX_w[fi + j * 32];
   const bool vec_ok = (N & 3) == 0;
-  const int count = *a.count;
-  const int nch = (count + kOutChunk - 1) / kOutChunk;
-  // Operands of the first chunk of 32 outlier columns (the common case is a
-  // single chunk), all requested before the first is used so that the
-  // epilogue pays one memory latency rather than one per block.
-  uint4 wf0[G::FN][2], xf0[G::FT][2];
-  if (nch > 0) {
 #pragma unroll
-    for (int i = 0; i < G::FN; ++i) {
-      const int nrow = min(n0 + wn * G::WN + i * 32 + fi, N - 1);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        wf0[i][h] = *reinterpret_cast<const uint4*>(a.Wd + (size_t)nrow * kOutChunk + h * 16 + fg * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < G::FT; ++j) {
-      const int t = min(tl + j * 32, T - 1);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        xf0[j][h] = *reinterpret_cast<const uint4*>(a.Xo + (size_t)t * kOutChunk + h * 16 + fg * 8);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < G::FN; ++i) {
+  for (int i = 0; i < FNW; ++i) {
     float bs[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const v4f w4 = *reinterpret_cast<const v4f*>(sW_l + wn * G::WN + 4 * fg + i * 32 + 8 * q);
+      const v4f w4 = *reinterpret_cast<const v4f*>(sW_w + 4 * fg + i * 32 + 8 * q);
 #pragma unroll
       for (int r = 0; r < 4; ++r) bs[4 * q + r] = w4[r] * (1.0f / 16129.0f);
     }
     if (a.dbg_C) {
 #pragma unroll
-      for (int j = 0; j < G::FT; ++j) {
+      for (int j = 0; j < FT; ++j) {
         const int t = tl + j * 32;
         if (t >= T) continue;
 #pragma unroll
@@ -121,44 +70,46 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
         }
       }
     }
-    v16f y[G::FT];
+    v16f y[FT];
 #pragma unroll
-    for (int j = 0; j < G::FT; ++j)
+    for (int j = 0; j < FT; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) y[j][v] = (float)acc[i][j][v] * (as[j] * bs[v]);
     // outlier columns: 16-bit operands (the activation type), fp32 accumulation
     // on top of the int8 part; a chunk of 32 outlier columns is two 32x32x16 steps.
     if (nch > 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        const uint4 w = wf(i, h);
 #pragma unroll
-        for (int j = 0; j < G::FT; ++j) y[j] = A16::mma32(wf0[i][h], xf0[j][h], y[j]);
+        for (int j = 0; j < FT; ++j) y[j] = A16::mma32(w, xf(j, h), y[j]);
+      }
     }
-    const int nrow = min(n0 + wn * G::WN + i * 32 + fi, N - 1);
+    const int nrow = min(nw0 + i * 32 + fi, N - 1);
     for (int c = 1; c < nch; ++c) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint4 wf = *reinterpret_cast<const uint4*>(
+        const uint4 w = *reinterpret_cast<const uint4*>(
             a.Wd + ((size_t)c * N + nrow) * kOutChunk + h * 16 + fg * 8);
 #pragma unroll
-        for (int j = 0; j < G::FT; ++j) {
+        for (int j = 0; j < FT; ++j) {
           const int t = min(tl + j * 32, T - 1);
-          const uint4 xf = *reinterpret_cast<const uint4*>(
+          const uint4 x = *reinterpret_cast<const uint4*>(
               a.Xo + ((size_t)c * T + t) * kOutChunk + h * 16 + fg * 8);
-          y[j] = A16::mma32(wf, xf, y[j]);
+          y[j] = A16::mma32(w, x, y[j]);
         }
       }
     }
-    if (a.bias) {
+    if (bias_w) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float bv = A16::to_f32(bias_l[wn * G::WN + 4 * fg + i * 32 + 8 * (v >> 2) + (v & 3)]);
+        const float bv = A16::to_f32(bias_w[4 * fg + i * 32 + 8 * (v >> 2) + (v & 3)]);
 #pragma unroll
-        for (int j = 0; j < G::FT; ++j) y[j][v] += bv;
+        for (int j = 0; j < FT; ++j) y[j][v] += bv;
       }
     }
 #pragma unroll
-    for (int j = 0; j < G::FT; ++j) {
+    for (int j = 0; j < FT; ++j) {
       const int t = tl + j * 32;
       if (t >= T) continue;
 #pragma unroll
@@ -179,6 +130,156 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
   }
 }
 
+// The tile's weight and activation scales -> LDS by direct copy, 64 entries per
+// piece (entries past the matrix read as zero; the arrays hold whole pieces).
+// Issued before the first K stage, so the stage waits cover them.
+template <int BN, int BT, int NWAVES>
+__device__ __forceinline__ void scales_to_lds(const LinearArgs& a, int n0, int t0, int rows_n, int rows_t,
+                                              float* sW_l, float* aX_l, int wave, int lane) {
+  constexpr int CS = (BN + 63) / 64, CX = (BT + 63) / 64;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.sW + n0, (uint32_t)(rows_n * 4));
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.aX + t0, (uint32_t)(rows_t * 4));
+  for (int c = wave; c < CS + CX; c += NWAVES) {
+    const bool is_w = c < CS;  // wave-uniform
+    const int cc = is_w ? c : c - CS;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        is_w ? rS : rX, (__attribute__((address_space(3))) void*)((is_w ? sW_l : aX_l) + cc * 64),
+        4, (uint32_t)((cc * 64 + lane) * 4), 0, 0, 0);
+  }
+}
+
+template <class G, bool BF16>
+__global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tiles_t, int group_n) {
+  static_assert(G::BN % 64 == 0 && G::BT % 64 == 0, "whole scale pieces");
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDS + (G::BN + G::BT) * 4 + G::BN * 2];
+  // the tile's weight and activation scales and bias, read by the epilogue
+  float* sW_l = reinterpret_cast<float*>(smem + G::LDS);
+  float* aX_l = sW_l + G::BN;
+  uint16_t* bias_l = reinterpret_cast<uint16_t*>(aX_l + G::BT);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % G::WAVES_N, wt = wave / G::WAVES_N;
+
+  const TileCoords tc = tile_coords<G>(a.N, tiles_t, group_n);
+  const int K = a.K, N = a.N, T = a.T;
+  const int n0 = tc.a0, t0 = tc.b0;
+  const int rows_n = min(G::BN, N - n0), rows_t = min(G::BT, T - t0);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.Wq + (size_t)n0 * K, (uint32_t)(rows_n * K));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.Xq + (size_t)t0 * K, (uint32_t)(rows_t * K));
+
+  uint16_t bias_v = 0;  // requested before the K loop, written to LDS after it
+  auto before_prologue = [&]() {
+    if (a.bias && tid < G::BN && n0 + tid < N) bias_v = a.bias[n0 + tid];
+    scales_to_lds<G::BN, G::BT, G::NWAVES>(a, n0, t0, rows_n, rows_t, sW_l, aX_l, wave, lane);
+  };
+  v16i acc[G::FN][G::FT];
+  gemm_kloop<G, MmaI8>(smem, rA, rB, K, wave, lane, acc, before_prologue);
+  const int fi = lane & 31, fg = lane >> 5;
+  if (a.bias) {  // uniform
+    if (tid < G::BN) bias_l[tid] = bias_v;
+    __syncthreads();
+  }
+
+  const int nw0 = n0 + wn * G::WN, tw0 = t0 + wt * G::WT;
+  const int count = *a.count;
+  const int nch = (count + kOutChunk - 1) / kOutChunk;
+  // Operands of the first chunk of 32 outlier columns (the common case is a
+  // single chunk), all requested before the first is used so that the
+  // epilogue pays one memory latency rather than one per block.
+  uint4 wf0[G::FN][2], xf0[G::FT][2];
+  if (nch > 0) {
+#pragma unroll
+    for (int i = 0; i < G::FN; ++i) {
+      const int nrow = min(nw0 + i * 32 + fi, N - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wf0[i][h] = *reinterpret_cast<const uint4*>(a.Wd + (size_t)nrow * kOutChunk + h * 16 + fg * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < G::FT; ++j) {
+      const int t = min(tw0 + fi + j * 32, T - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        xf0[j][h] = *reinterpret_cast<const uint4*>(a.Xo + (size_t)t * kOutChunk + h * 16 + fg * 8);
+    }
+  }
+  gemm_epilogue<BF16, G::FN, G::FT>(
+      a, acc, nw0, tw0, sW_l + wn * G::WN, aX_l + wt * G::WT, a.bias ? bias_l + wn * G::WN : nullptr,
+      nch, lane, [&](int i, int h) { return wf0[i][h]; }, [&](int j, int h) { return xf0[j][h]; });
+}
+
+// One wavefront column of a SplitTile: FNW row blocks from tile row wrow.
+template <class G, bool BF16, int FNW>
+__device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, int n0, int t0, int rows_n,
+                                             int rows_t, int wave, int lane, int wrow, int wcol) {
+  float* sW_l = reinterpret_cast<float*>(smem + G::LDS);
+  float* aX_l = sW_l + G::SW_PAD;
+  uint16_t* bias_l = reinterpret_cast<uint16_t*>(aX_l + G::AX_PAD);
+  const int tid = threadIdx.x;
+  const int K = a.K, N = a.N;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.Wq + (size_t)n0 * K, (uint32_t)(rows_n * K));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.Xq + (size_t)t0 * K, (uint32_t)(rows_t * K));
+  uint16_t bias_v = 0;  // requested before the K loop, written to LDS after it
+  auto before_prologue = [&]() {
+    if (a.bias && tid < G::BN && n0 + tid < N) bias_v = a.bias[n0 + tid];
+    scales_to_lds<G::BN, G::BT, G::NWAVES>(a, n0, t0, rows_n, rows_t, sW_l, aX_l, wave, lane);
+  };
+  const int count = *a.count;
+  const int nch = (count + kOutChunk - 1) / kOutChunk;
+  // The first chunk of 32 outlier columns (the common case is a single chunk):
+  // the tile's BN rows of Wd and BT rows of Xo, 64 bytes each, are copied into
+  // the ring slot that the last K stage leaves free, while its MFMAs run.
+  const char* epi = nullptr;
+  auto outliers_to_lds = [&](char* free_slot) {
+    epi = free_slot;
+    if (nch == 0) return;
+    constexpr int CW = G::BN * 64 / 1024, CXO = G::BT * 64 / 1024;
+    static_assert(G::BN * 64 % 1024 == 0 && G::BT * 64 % 1024 == 0, "1 KB pieces");
+    static_assert((G::BN + G::BT) * 64 <= G::STAGE, "fits a slot");
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.Wd + (size_t)n0 * kOutChunk, (uint32_t)(rows_n * 64));
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.Xo + (size_t)t0 * kOutChunk, (uint32_t)(rows_t * 64));
+    for (int c = wave; c < CW + CXO; c += G::NWAVES) {
+      const bool is_w = c < CW;  // wave-uniform
+      lds_dma16(is_w ? rW : rO, free_slot + c * 1024, (uint32_t)((is_w ? c : c - CW) * 1024 + lane * 16));
+    }
+  };
+  v16i acc[FNW][G::FT];
+  gemm_kloop_split<G, MmaI8, FNW>(smem, rA, rB, K, wave, lane, wrow, wcol, acc, before_prologue,
+                                  outliers_to_lds);
+  if (a.bias) {  // uniform
+    if (tid < G::BN) bias_l[tid] = bias_v;
+    __syncthreads();
+  }
+  const int fi = lane & 31, fg = lane >> 5;
+  gemm_epilogue<BF16, FNW, G::FT>(
+      a, acc, n0 + wrow, t0 + wcol, sW_l + wrow, aX_l + wcol, a.bias ? bias_l + wrow : nullptr, nch,
+      lane,
+      [&](int i, int h) {
+        return *reinterpret_cast<const uint4*>(epi + (wrow + i * 32 + fi) * 64 + h * 32 + fg * 16);
+      },
+      [&](int j, int h) {
+        return *reinterpret_cast<const uint4*>(epi + (G::BN + wcol + j * 32 + fi) * 64 + h * 32 + fg * 16);
+      });
+}
+
+template <class G, bool BF16>
+__global__ __launch_bounds__(G::kThreads, 1) void kb_gemm_split(LinearArgs a, int tiles_t, int group_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[G::SMEM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wavefront column (wn) and row (wt): the two wavefronts that share a SIMD
+  // (w and w + 4) take different columns, so every SIMD does the same work
+  const int wn = (wave + (wave >> 2)) & 1, wt = (wave >> 1) & 3;
+  const TileCoords tc = tile_coords<G>(a.N, tiles_t, group_n);
+  const int n0 = tc.a0, t0 = tc.b0;
+  const int rows_n = min(G::BN, a.N - n0), rows_t = min(G::BT, a.T - t0);
+  if (wn == 0)
+    split_column<G, BF16, G::FN0>(a, smem, n0, t0, rows_n, rows_t, wave, lane, 0, wt * G::WT);
+  else
+    split_column<G, BF16, G::FN1>(a, smem, n0, t0, rows_n, rows_t, wave, lane, G::FN0 * 32, wt * G::WT);
+}
+
 template <class G>
 hipError_t launch_gemm_tile(const LinearArgs& a, hipStream_t stream, int group_n) {
   const int tn = (a.N + G::BN - 1) / G::BN, tt = (a.T + G::BT - 1) / G::BT;
@@ -190,33 +291,53 @@ hipError_t launch_gemm_tile(const LinearArgs& a, hipStream_t stream, int group_n
   return hipGetLastError();
 }
 
+template <class G>
+hipError_t launch_gemm_split(const LinearArgs& a, hipStream_t stream, int group_n) {
+  const int tn = (a.N + G::BN - 1) / G::BN, tt = (a.T + G::BT - 1) / G::BT;
+  if (group_n < 1) group_n = 1;
+  if (a.bf16)
+    hipLaunchKernelGGL((kb_gemm_split<G, true>), dim3(tn * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
+  else
+    hipLaunchKernelGGL((kb_gemm_split<G, false>), dim3(tn * tt), dim3(G::kThreads), 0, stream, a, tt, group_n);
+  return hipGetLastError();
+}
+
 // Tile shapes (BN x BT, BK, LDS stages, wavefronts along N x T).
 using Tile256x256 = GemmTile<256, 256, 128, 2, 2, 4>;  // 8 wavefronts of 128x64
 using Tile192x256 = GemmTile<192, 256, 128, 2, 2, 4>;  // 8 wavefronts of 96x64
 using Tile256x128 = GemmTile<256, 128, 128, 2, 2, 4>;  // 8 wavefronts of 128x32
 using Tile128x128 = GemmTile<128, 128, 128, 4, 2, 2>;  // 4 wavefronts of 64x64
+using Tile352x256 = SplitTile<352, 256>;               // 8 wavefronts of 192x64 / 160x64
 
 constexpr int kGroupN = 8;  // weight row-blocks per rasterization group
 
 // Tile choice: minimise (rounds of CUs) x (time per tile), where a tile's
 // time is its MFMA work divided by a per-shape efficiency (measured on gfx950:
-// smaller tiles move more operand bytes per MFMA and run less efficiently).
-hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream) {
+// smaller tiles move more operand bytes per MFMA and run less efficiently; the
+// 352 x 256 tile runs about as efficiently per op as 256 x 256 and exists for
+// outputs that it covers in fewer rounds). `tile` >= 0 forces a candidate.
+hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream, int tile) {
   struct Cand { int bn, bt; double eff; };
-  const Cand cands[] = {{256, 256, 1.0}, {192, 256, 0.93}, {256, 128, 0.8}, {128, 128, 0.55}};
+  const Cand cands[kGemmTiles] = {{256, 256, 1.0}, {192, 256, 0.93}, {256, 128, 0.8}, {128, 128, 0.55},
+                                  {352, 256, 1.0}};
   int best = 0;
-  double best_cost = 1e300;
-  for (int i = 0; i < 4; ++i) {
-    const double tiles = (double)ceil_div(a.N, cands[i].bn) * (double)ceil_div(a.T, cands[i].bt);
-    const double rounds = std::ceil(tiles / num_cus);
-    const double cost = rounds * cands[i].bn * cands[i].bt / cands[i].eff;
-    if (cost < best_cost * 0.999) { best_cost = cost; best = i; }
+  if (tile >= 0 && tile < kGemmTiles) {
+    best = tile;
+  } else {
+    double best_cost = 1e300;
+    for (int i = 0; i < kGemmTiles; ++i) {
+      const double tiles = (double)ceil_div(a.N, cands[i].bn) * (double)ceil_div(a.T, cands[i].bt);
+      const double rounds = std::ceil(tiles / num_cus);
+      const double cost = rounds * cands[i].bn * cands[i].bt / cands[i].eff;
+      if (cost < best_cost * 0.999) { best_cost = cost; best = i; }
+    }
   }
   switch (best) {
     case 0: return launch_gemm_tile<Tile256x256>(a, stream, kGroupN);
     case 1: return launch_gemm_tile<Tile192x256>(a, stream, kGroupN);
     case 2: return launch_gemm_tile<Tile256x128>(a, stream, kGroupN);
-    default: return launch_gemm_tile<Tile128x128>(a, stream, kGroupN);
+    case 3: return launch_gemm_tile<Tile128x128>(a, stream, kGroupN);
+    default: return launch_gemm_split<Tile352x256>(a, stream, kGroupN);
   }
 }
 

@@ -271,4 +271,144 @@ __device__ __forceinline__ void gemm_kloop(char* smem, __amdgpu_buffer_rsrc_t rA
   mfma(f1);  // last k-step of the last stage
 }
 
+// Tiles whose accumulators take most of a wavefront's registers: 8
+// wavefronts, 2 along N x 4 along T, 2-slot ring of 128-byte stages. BN need
+// not split evenly: the wavefront columns own ceil(BN/64) and floor(BN/64)
+// 32-row blocks (352 = 192 + 160 rows), and the copy of A is spread over the
+// wavefronts as evenly as 1 KB pieces allow. With 2 slots every stage waits
+// for all of its copies (vmcnt(0)), so the per-wavefront copy counts may differ.
+template <int BN_, int BT_>
+struct SplitTile {
+  static constexpr int BN = BN_, BT = BT_, BK = 128, NSTAGE = 2;
+  static constexpr int WAVES_T = 4, NWAVES = 8, kThreads = 64 * NWAVES;
+  static constexpr int NB = BN / 32;                       // 32-row blocks along N
+  static constexpr int FN0 = (NB + 1) / 2, FN1 = NB - FN0;  // per wavefront column
+  static constexpr int WT = BT / WAVES_T, FT = WT / 32;
+  static constexpr int KS = BK / 32, CPR = BK / 16, RPB = 64 / CPR;
+  static constexpr int A_BYTES = BN * BK, B_BYTES = BT * BK, STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS = STAGE * NSTAGE;
+  static constexpr int A_BLOCKS = BN / RPB;                 // 1 KB copy pieces of A per stage
+  static constexpr int A_ISSUES = (A_BLOCKS + NWAVES - 1) / NWAVES, A_FULL = A_BLOCKS / NWAVES;
+  static constexpr int B_ISSUES = BT / RPB / NWAVES;
+  // scales are copied in 64-entry pieces; the arrays are padded to whole pieces
+  static constexpr int SW_PAD = (BN + 63) / 64 * 64, AX_PAD = (BT + 63) / 64 * 64;
+  static constexpr int SMEM = LDS + (SW_PAD + AX_PAD) * 4 + BN * 2;
+  static_assert(BN % 32 == 0 && FT == 2 && BT % (RPB * NWAVES) == 0, "tile shape");
+  static_assert((NWAVES * RPB) % 32 == 0, "copy pieces keep the row swizzle");
+  static_assert(BN <= kThreads && SMEM <= 160 * 1024, "LDS");
+};
+
+// K loop of a SplitTile wavefront owning FNW x FT accumulator blocks, A rows
+// wrow.. and B rows wcol.. of the tile. The fragments are single-buffered:
+// MFMAs run column-block major (all i for j = 0, then all i for j = 1) and each
+// fragment is replaced by the next k-step's right after its last use, which
+// gives every read about FNW MFMAs of lead and leaves the registers to the
+// accumulators. The last stage has no successor to copy: `into_free_slot`
+// receives the ring slot it leaves free and may fill it with direct copies
+// (covered by that stage's wait and barrier).
+template <class G, class Mma, int FNW, class Pre, class Last>
+__device__ __forceinline__ void gemm_kloop_split(char* smem, __amdgpu_buffer_rsrc_t rA,
+                                                 __amdgpu_buffer_rsrc_t rB, int K, int wave, int lane,
+                                                 int wrow, int wcol,
+                                                 typename Mma::acc_t (&acc)[FNW][G::FT],
+                                                 Pre&& before_prologue, Last&& into_free_slot) {
+  constexpr int FT = G::FT;
+  // Copy piece i of a wavefront holds rows (i * NWAVES + wave) * RPB + lane / CPR;
+  // i * NWAVES * RPB is a multiple of 32, so every piece has the same swizzled
+  // chunk and the offsets step by the uniform NWAVES * RPB * K.
+  const int pr = lane / G::CPR, pc = lane % G::CPR;
+  const int row0 = wave * G::RPB + pr;
+  const int kc = (pc ^ swz<G::CPR>(row0)) * 16;
+  const uint32_t off0 = (uint32_t)(row0 * K + kc);
+  const uint32_t istride = (uint32_t)(G::NWAVES * G::RPB * K);
+  auto issue = [&](int slot, int kt) {
+    const int kb = kt * G::BK;
+    char* sA = smem + slot * G::STAGE;
+    char* sB = sA + G::A_BYTES;
+    const bool ok = kb + G::BK <= K || kb + kc < K;  // K past the end reads zeros
+    const uint32_t o = off0 + kb;
+#pragma unroll
+    for (int i = 0; i < G::A_ISSUES; ++i)
+      if (i < G::A_FULL || i * G::NWAVES + wave < G::A_BLOCKS)
+        lds_dma16(rA, sA + (i * G::NWAVES + wave) * 1024, ok ? o + i * istride : kOobOffset);
+#pragma unroll
+    for (int i = 0; i < G::B_ISSUES; ++i)
+      lds_dma16(rB, sB + (i * G::NWAVES + wave) * 1024, ok ? o + i * istride : kOobOffset);
+  };
+  // fragment addresses: the per-lane part (row fi, swizzled chunk of k-step ks)
+  // is the same for A and B
+  const int fi = lane & 31, fg = lane >> 5;
+  const int fswz = swz<G::CPR>(fi);
+  int loff[G::KS];
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) loff[ks] = fi * G::BK + ((ks * 2 + fg) ^ fswz) * 16;
+  const int abase = wrow * G::BK, bbase = G::A_BYTES + wcol * G::BK;
+  v4i fa[FNW], fb[FT];
+  auto read_a = [&](int i, int slot, int ks) {
+    fa[i] = *reinterpret_cast<const v4i*>(smem + slot * G::STAGE + abase + loff[ks] + i * 32 * G::BK);
+  };
+  auto read_b = [&](int j, int slot, int ks) {
+    fb[j] = *reinterpret_cast<const v4i*>(smem + slot * G::STAGE + bbase + loff[ks] + j * 32 * G::BK);
+  };
+#pragma unroll
+  for (int i = 0; i < FNW; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) acc[i][j] = Mma::zero();
+  // MFMAs of the fragments in registers; each fragment then receives k-step
+  // (nslot, nks)
+  auto step = [&](int nslot, int nks) {
+#pragma unroll
+    for (int i = 0; i < FNW; ++i) acc[i][0] = Mma::run(fa[i], fb[0], acc[i][0]);
+    read_b(0, nslot, nks);
+#pragma unroll
+    for (int i = 0; i < FNW; ++i) {
+      acc[i][1] = Mma::run(fa[i], fb[1], acc[i][1]);
+      read_a(i, nslot, nks);
+    }
+    read_b(1, nslot, nks);
+    __builtin_amdgcn_sched_group_barrier(0x008, FNW, 0);  // MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+#pragma unroll
+    for (int i = 0; i < FNW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  };
+  const int KT = (K + G::BK - 1) / G::BK;
+  // stage kt in `slot`: copy the next stage (or hand over the free slot), the
+  // MFMAs of k-steps 0..KS-2 with the reads of 1..KS-1, then the waits and the
+  // barrier; the MFMAs of its last k-step run after the barrier, with the reads
+  // of the next stage's first.
+  auto body = [&](int slot, int kt) {
+    if (kt + 1 < KT) issue(slot ^ 1, kt + 1);
+    else into_free_slot(smem + (slot ^ 1) * G::STAGE);
+#pragma unroll
+    for (int ks = 1; ks < G::KS; ++ks) step(slot, ks);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    barrier_no_fence();
+  };
+  before_prologue();
+  issue(0, 0);
+  wait_vmcnt<0>();
+  barrier_no_fence();
+#pragma unroll
+  for (int i = 0; i < FNW; ++i) read_a(i, 0, 0);
+#pragma unroll
+  for (int j = 0; j < FT; ++j) read_b(j, 0, 0);
+  body(0, 0);
+  int slot = 1;
+  for (int kt = 1; kt < KT; ++kt) {
+    step(slot, 0);
+    body(slot, kt);
+    slot ^= 1;
+  }
+#pragma unroll
+  for (int j = 0; j < FT; ++j)
+#pragma unroll
+    for (int i = 0; i < FNW; ++i) acc[i][j] = Mma::run(fa[i], fb[j], acc[i][j]);
+}
+
 }  // namespace llmint8

@@ -98,7 +98,10 @@ int scan_row_groups(int T, int K, int num_cus);
 uint32_t threshold_code(float thr, bool bf16);  // smallest 16-bit |x| code whose value reaches thr
 hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream);
 hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStream_t stream);
-hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream);
+// int8 GEMM tiles (N x T): 256x256, 192x256, 256x128, 128x128, 352x256; the
+// host picks one by cost unless `tile` (0..kGemmTiles-1) forces it.
+constexpr int kGemmTiles = 5;
+hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream, int tile = -1);
 int gemv_max_rows(int K);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uint16_t* WdT,

@@ -97,6 +97,13 @@ def test_debug_and_timed_argument_errors(lib):
     d = lib.llmint8_linear_debug
     base = [ALIGNED, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, ALIGNED, ALIGNED, need, None]
     assert d(*base, 7, None, None, None, None, None, None) == INVALID        # unknown path
+    for p in (3, 15, 21, -1):                                                  # around the tile paths
+        assert d(*base, p, None, None, None, None, None, None) == INVALID
+    tiles = sorted(m8.LLMINT8_PATH_GEMM_TILES.values())
+    assert tiles == list(range(16, 21))
+    # a forced tile is the GEMM route: 3 kernels, so 2 events are too few
+    assert lib.llmint8_linear_timed(*base, tiles[-1], (ctypes.c_void_p * 4)(P, P, P, P), 2,
+                                    ctypes.byref(ctypes.c_int(0))) == INVALID
     assert d(*base, m8.LLMINT8_PATH_GEMM, None, None, None, MISALIGNED, None, None) == INVALID
     big_t = lib.llmint8_gemv_max_rows(1024) + 1
     need2 = lib.llmint8_workspace_bytes(big_t, 1024, 1024)

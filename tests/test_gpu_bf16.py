@@ -191,6 +191,15 @@ def test_bf16_many_outlier_chunks():
     run_case("bf16 100 outliers gemv", W, X[:9], 6.0, GEMV, "bf16", bias=b)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("tile", sorted(m8.LLMINT8_PATH_GEMM_TILES))
+def test_every_gemm_tile_with_bias(dtype, tile):
+    path = m8.LLMINT8_PATH_GEMM_TILES[tile]
+    for (T, K, N, n_out, seed) in ((300, 1040, 1000, 3, 31), (70, 1024, 706, 100, 32)):
+        W, X = _as(dtype, *_small(T, K, N, seed=seed, n_out=n_out))
+        run_case(f"tile {tile}", W, X, 6.0, path, dtype, bias=_bias(seed, N, dtype))
+
+
 @pytest.mark.parametrize("path", [GEMM, GEMV])
 def test_fp16_ex_without_bias_matches_the_plain_entry(path):
     W, X = _small(7, 1024, 264, seed=61)

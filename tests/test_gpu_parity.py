@@ -166,6 +166,20 @@ def test_single_outlier_column(path):
     assert c == 1
 
 
+@pytest.mark.parametrize("tile", sorted(m8.LLMINT8_PATH_GEMM_TILES))
+def test_every_gemm_tile_ragged(tile):
+    """Each GEMM tile, forced, on ragged T, K and N: partial tiles along both
+    output axes, a K tail, no outliers, one chunk and several chunks."""
+    path = m8.LLMINT8_PATH_GEMM_TILES[tile]
+    for (T, K, N, n_out, seed) in ((300, 1040, 1000, 3, 1), (257, 4096, 705, 0, 2),
+                                   (64, 272, 360, 40, 3), (513, 640, 2100, 100, 4)):
+        W, X = _small(T, K, N, seed=seed, n_out=n_out)
+        # every tile computes each output element with the same operations:
+        # the plain call (tile by cost) must give the same bits
+        _, c = run_case(f"tile {tile}", W, X, 6.0 if n_out else math.inf, path, check_auto=True)
+        assert (c > 0) == (n_out > 0)
+
+
 def test_integer_inputs_quantize_exactly():
     rng = _rng(9)
     X = rng.integers(-127, 128, size=(20, 128)).astype(np.float16)

@@ -229,7 +229,11 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
   const int nch = (count + kOutChunk - 1) / kOutChunk;
   // The first chunk of 32 outlier columns (the common case is a single chunk):
   // the tile's BN rows of Wd and BT rows of Xo, 64 bytes each, are copied into
-  // the ring slot that the last K stage leaves free, while its MFMAs run.
+  // the ring slot that the last K stage leaves free, while its MFMAs run. Row r
+  // of that area keeps its 16-byte chunk c at position c ^ ((r >> 2) & 3), so
+  // that the epilogue's reads (32 rows x 2 chunks per instruction) are free of
+  // bank conflicts.
+  static_assert(G::BN % 16 == 0 && G::FN0 * 32 % 16 == 0, "swizzle rows stay aligned");
   const char* epi = nullptr;
   auto outliers_to_lds = [&](char* free_slot) {
     epi = free_slot;
@@ -241,7 +245,10 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
     const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.Xo + (size_t)t0 * kOutChunk, (uint32_t)(rows_t * 64));
     for (int c = wave; c < CW + CXO; c += G::NWAVES) {
       const bool is_w = c < CW;  // wave-uniform
-      lds_dma16(is_w ? rW : rO, free_slot + c * 1024, (uint32_t)((is_w ? c : c - CW) * 1024 + lane * 16));
+      const int r = c * 16 + (lane >> 2);  // row of the staged area this lane fills
+      const uint32_t src = (uint32_t)((is_w ? c : c - CW) * 1024 + (lane >> 2) * 64 +
+                                      (((lane & 3) ^ ((r >> 2) & 3)) * 16));
+      lds_dma16(is_w ? rW : rO, free_slot + c * 1024, src);
     }
   };
   v16i acc[FNW][G::FT];
@@ -256,10 +263,12 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
       a, acc, n0 + wrow, t0 + wcol, sW_l + wrow, aX_l + wcol, a.bias ? bias_l + wrow : nullptr, nch,
       lane,
       [&](int i, int h) {
-        return *reinterpret_cast<const uint4*>(epi + (wrow + i * 32 + fi) * 64 + h * 32 + fg * 16);
+        const int r = wrow + i * 32 + fi;
+        return *reinterpret_cast<const uint4*>(epi + r * 64 + (((2 * h + fg) ^ ((r >> 2) & 3)) * 16));
       },
       [&](int j, int h) {
-        return *reinterpret_cast<const uint4*>(epi + (G::BN + wcol + j * 32 + fi) * 64 + h * 32 + fg * 16);
+        const int r = G::BN + wcol + j * 32 + fi;
+        return *reinterpret_cast<const uint4*>(epi + r * 64 + (((2 * h + fg) ^ ((r >> 2) & 3)) * 16));
       });
 }
 

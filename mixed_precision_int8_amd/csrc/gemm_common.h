@@ -1,8 +1,12 @@
-// K-loop shared by the gfx950 GEMM kernels of this library: tile shapes,
+// K-loops shared by the gfx950 GEMM kernels of this library: tile shapes,
 // the direct-to-LDS copy ring and the MFMA software pipeline. A kernel supplies
 // the two operands as K-contiguous byte rows (A: BN rows, B: BT rows), the MFMA
-// flavour, and its own epilogue; the loop leaves each wavefront's
-// (BN/WAVES_N) x (BT/WAVES_T) accumulators in registers as 32x32 blocks.
+// flavour, and its own epilogue; the loop leaves each wavefront's accumulators
+// in registers as 32x32 blocks. gemm_kloop serves evenly split tiles
+// (GemmTile: (BN/WAVES_N) x (BT/WAVES_T) per wavefront, fragments
+// double-buffered); gemm_kloop_split serves SplitTile, whose two wavefront
+// columns may differ by one row block and whose accumulators leave room for a
+// single set of fragment registers only.
 //
 // Design (CDNA4): K-stages of BK bytes are copied global->LDS with
 // buffer_load_dwordx4 ... lds (no VGPR staging) into a ring of NSTAGE buffers,

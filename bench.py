@@ -97,6 +97,29 @@ def committed_traffic(path=None, files=None, key="hbm_bytes_per_launch"):
     return float(m.group(1)) if m else None
 
 
+def graph_us_per_call(fn, n_calls, replays, stream):
+    """fn(0) .. fn(n_calls - 1) captured once in a HIP graph and replayed: microseconds
+    per call without the per-call host (Python) submission cost. The calls must
+    launch kernels only (no memsets, no allocations)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (replays * n_calls) * 1e3
+    del g
+    return us
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -219,20 +242,10 @@ def main():
             us = a0.elapsed_time(a1) / reps * 1e3
             # the same loop captured in a HIP graph: back-to-back calls without
             # the per-call host (Python) submission cost
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(len(copies)):
-                    q, s = copies[i % len(copies)]
-                    m8.llmint8_linear(Xt, q, s, wd.threshold, Y=Yt, workspace=wst)
-            g.replay()
-            torch.cuda.synchronize()
-            greps = max(1, reps // len(copies))
-            a0.record(stream)
-            for _ in range(greps):
-                g.replay()
-            a1.record(stream)
-            torch.cuda.synchronize()
-            gus = a0.elapsed_time(a1) / (greps * len(copies)) * 1e3
+            gus = graph_us_per_call(
+                lambda i: m8.llmint8_linear(Xt, copies[i][0], copies[i][1], wd.threshold, Y=Yt,
+                                            workspace=wst),
+                len(copies), max(1, reps // len(copies)), stream)
             nbytes = wd.N * wd.K + 4 * wd.N + 2 * Td * wd.K + 2 * Td * wd.N
             gbs = nbytes / (us * 1e-6) / 1e9
             ggbs = nbytes / (gus * 1e-6) / 1e9
@@ -241,7 +254,6 @@ def main():
                              "graph_us_per_call": round(gus, 3), "graph_GB_per_s": round(ggbs, 1),
                              "graph_pct_hbm": round(100.0 * ggbs / PEAK_HBM_GBS, 2),
                              "algorithmic_bytes": nbytes}
-            del g
         result["decode"] = {"workload": "decode_gemv K=4096 N=4096", "kernel": "kd_gemv",
                             "weight_copies_cycled": len(copies), **dec}
         del copies
@@ -321,10 +333,17 @@ def main():
                                                              cps[i % len(cps)][1], wd.threshold,
                                                              bias=b3, Y=Y3, workspace=ws3),
                               reps, args.warmup)
+            gus = graph_us_per_call(
+                lambda i: m8.llmint8_linear_ex(X3b, cps[i][0], cps[i][1], wd.threshold, bias=b3,
+                                               Y=Y3, workspace=ws3),
+                len(cps), max(1, reps // len(cps)), stream)
             nbytes = wd.N * wd.K + 4 * wd.N + 2 * wd.K + 2 * wd.N + 2 * wd.N
             bf["decode_T1"] = {"K": wd.K, "N": wd.N, "us_per_call": round(dms * 1e3, 3),
                                "GB_per_s": round(nbytes / (dms * 1e-3) / 1e9, 1),
                                "pct_hbm": round(100.0 * nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                               "graph_us_per_call": round(gus, 3),
+                               "graph_pct_hbm": round(100.0 * nbytes / (gus * 1e-6) / 1e9
+                                                      / PEAK_HBM_GBS, 2),
                                "algorithmic_bytes": nbytes, "weight_copies_cycled": len(cps)}
             del cps
         result["bf16_bias"] = {"workload": "bf16 X, bias and Y; the prefill and decode layers",
@@ -369,11 +388,16 @@ def main():
                 q1.record(stream)
                 torch.cuda.synchronize()
                 us = q0.elapsed_time(q1) / reps * 1e3
+                gus = graph_us_per_call(lambda i: call(i), len(cps), max(2, reps // len(cps)),
+                                        stream)
                 nbytes = N4 * K4 // 2 + 4 * (N4 * K4 // block) + 2 * T4 * K4 + 2 * T4 * N4
                 gbs = nbytes / (us * 1e-6) / 1e9
                 fb[f"{lname}_T{T4}"] = {"K": K4, "N": N4, "T": T4, "us_per_call": round(us, 3),
                                         "GB_per_s": round(gbs, 1),
                                         "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+                                        "graph_us_per_call": round(gus, 3),
+                                        "graph_pct_hbm": round(100.0 * nbytes / (gus * 1e-6) / 1e9
+                                                               / PEAK_HBM_GBS, 2),
                                         "algorithmic_bytes": nbytes, "weight_copies_cycled": len(cps)}
             if lname == "large_layer":
                 # the standalone dequantization of the same weight (fp16 out)

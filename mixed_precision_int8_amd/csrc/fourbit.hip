@@ -56,9 +56,7 @@ double normal_quantile_upper(double p) {
   return x;
 }
 
-}  // namespace
-
-bool code_book_4bit(int quant_type, Code4* out) {
+bool build_code_book_4bit(int quant_type, Code4* out) {
   double v[16];
   if (quant_type == LLMINT8_QUANT_NF4) {
     const double pmax = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
@@ -94,6 +92,27 @@ bool code_book_4bit(int quant_type, Code4* out) {
     if (r < 8) out->rank_lo |= (uint32_t)order[r] << (4 * r);
     else out->rank_hi |= (uint32_t)order[r] << (4 * (r - 8));
   }
+  return true;
+}
+
+}  // namespace
+
+// Each book is built once per process (thread-safe static initialisation): the
+// NF4 book takes 15 quantile solves, too slow for every call of a decode step.
+bool code_book_4bit(int quant_type, Code4* out) {
+  static const Code4 nf4 = [] {
+    Code4 c{};
+    build_code_book_4bit(LLMINT8_QUANT_NF4, &c);
+    return c;
+  }();
+  static const Code4 fp4 = [] {
+    Code4 c{};
+    build_code_book_4bit(LLMINT8_QUANT_FP4, &c);
+    return c;
+  }();
+  if (quant_type == LLMINT8_QUANT_NF4) *out = nf4;
+  else if (quant_type == LLMINT8_QUANT_FP4) *out = fp4;
+  else return false;
   return true;
 }
 

@@ -67,6 +67,7 @@ def parse():
     p.add_argument("--no-codec", action="store_true", help="skip the blockwise codec workload")
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 + bias workload")
     p.add_argument("--no-fourbit", action="store_true", help="skip the 4-bit weight workload")
+    p.add_argument("--no-probe", action="store_true", help="skip the matrix-core rate probe")
     p.add_argument("--decode-copies", type=int, default=24,
                    help="distinct weight copies cycled in the decode timing (> last-level cache)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -214,6 +215,32 @@ def main():
         "kernels_ms": {n: round(v, 5) for n, v in zip(names, per_kernel)},
         "wall_s_timed_region": round(wall, 4),
     }
+
+    # ---- the GEMM's MFMA instruction on its own (register operands, no memory
+    # traffic): what the chip delivers at its running clock
+    if not args.no_probe:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        pblocks, piters = 4 * cus, 2000
+        pout = torch.empty((pblocks * 256,), dtype=torch.int32, device=dev)
+        for _ in range(3):
+            pops = m8.llmint8_probe_mfma_i8(pblocks, piters, pout)
+        torch.cuda.synchronize()
+        pms = []
+        for _ in range(5):
+            p0 = torch.cuda.Event(enable_timing=True)
+            p1 = torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            m8.llmint8_probe_mfma_i8(pblocks, piters, pout)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            pms.append(p0.elapsed_time(p1))
+        ptops = pops / (sorted(pms)[len(pms) // 2] * 1e-3) / 1e12
+        gemm_tops = result["roofline"]["achieved"] if result.get("roofline") else None
+        result["mfma_probe"] = {
+            "instruction": "v_mfma_i32_32x32x32_i8", "workgroups": pblocks, "ops_per_call": pops,
+            "TOPS": round(ptops, 1), "pct_int8_peak": round(100.0 * ptops / PEAK_INT8_TOPS, 2),
+            "gemm_fraction_of_probe": round(gemm_tops / ptops, 4) if gemm_tops else None}
+        del pout
 
     # ---- decode-shaped workload: HBM-bound weight streaming
     if not args.no_decode:

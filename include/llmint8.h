@@ -350,6 +350,18 @@ LLMINT8_API llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t
                                                int64_t block, int quant_type, int64_t N,
                                                const void* bias, void* Y, void* stream);
 
+/*
+ * Measurement helper, not part of the method: the rate of the matrix-core
+ * instruction the int8 GEMM uses (v_mfma_i32_32x32x32_i8, 2 x 32 x 32 x 32
+ * int8 operations each) with no memory traffic. Enqueues `blocks` workgroups
+ * of 256 threads; each of their 4 wavefronts issues iters x 4 independent
+ * MFMAs, then every thread writes one checksum to out (int32 [blocks * 256],
+ * device) so that the work is kept. Operations per call:
+ * blocks * 4 * iters * 4 * 65536. LLMINT8_ERR_INVALID_ARG for blocks <= 0,
+ * iters <= 0 or out NULL.
+ */
+LLMINT8_API llmint8_status llmint8_probe_mfma_i8(int blocks, int iters, int32_t* out, void* stream);
+
 /* Largest T the fused GEMV route accepts for this K (0 if none). */
 LLMINT8_API int llmint8_gemv_max_rows(int64_t K);
 

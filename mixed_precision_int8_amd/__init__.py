@@ -23,7 +23,7 @@ __all__ = [
     "llmint8_quantize_weight_ex", "llmint8_linear_ex", "llmint8_linear_debug_ex",
     "LLMINT8_QUANT_NF4", "LLMINT8_QUANT_FP4", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit", "llmint8_linear_timed_ex",
-    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
+    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex", "llmint8_probe_mfma_i8",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -46,7 +46,7 @@ EXPORTED_SYMBOLS = (
     "llmint8_dequantize_blockwise", "llmint8_quantize_weight_ex", "llmint8_linear_ex",
     "llmint8_linear_debug_ex", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "llmint8_linear_timed_ex",
-    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
+    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex", "llmint8_probe_mfma_i8",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -130,6 +130,8 @@ def load_library():
     lib.llmint8_linear_4bit.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64, ctypes.c_int,
                                         _i64, _vp, _vp, _vp]
     lib.llmint8_linear_4bit.restype = ctypes.c_int
+    lib.llmint8_probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
+    lib.llmint8_probe_mfma_i8.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
     lib.llmint8_gemv_max_rows.restype = ctypes.c_int
     lib.llmint8_status_string.argtypes = [ctypes.c_int]
@@ -175,6 +177,18 @@ def _need(t, dtype, shape, name):
 
 def llmint8_workspace_bytes(T: int, K: int, N: int) -> int:
     return int(load_library().llmint8_workspace_bytes(T, K, N))
+
+
+def llmint8_probe_mfma_i8(blocks: int, iters: int, out, stream=None):
+    """Measurement helper: enqueue the matrix-core rate probe (blocks x 4 wavefronts, each
+    iters x 4 v_mfma_i32_32x32x32_i8); ``out`` int32 [blocks * 256] receives checksums.
+    Returns the int8 operation count of the call."""
+    import torch
+    lib = load_library()
+    _need(out, torch.int32, (blocks * 256,), "out")
+    _check(lib.llmint8_probe_mfma_i8(int(blocks), int(iters), _ptr(out), _stream(stream, out.device)),
+           "llmint8_probe_mfma_i8")
+    return blocks * 4 * iters * 4 * 2 * 32 * 32 * 32
 
 
 def llmint8_gemv_max_rows(K: int) -> int:

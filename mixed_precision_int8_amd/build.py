@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libllmint8.so")
 
 SOURCES = ["prep.hip", "gemm.hip", "gemv.hip", "bwd.hip", "blockwise.hip", "fourbit.hip",
-           "api.cpp"]
+           "probe.hip", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

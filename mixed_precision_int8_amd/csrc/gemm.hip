@@ -233,7 +233,6 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
   // of that area keeps its 16-byte chunk c at position c ^ ((r >> 2) & 3), so
   // that the epilogue's reads (32 rows x 2 chunks per instruction) are free of
   // bank conflicts.
-  static_assert(G::BN % 16 == 0 && G::FN0 * 32 % 16 == 0, "swizzle rows stay aligned");
   const char* epi = nullptr;
   auto outliers_to_lds = [&](char* free_slot) {
     epi = free_slot;

@@ -102,6 +102,7 @@ hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStrea
 // host picks one by cost unless `tile` (0..kGemmTiles-1) forces it.
 constexpr int kGemmTiles = 5;
 hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream, int tile = -1);
+hipError_t launch_probe_mfma_i8(int blocks, int iters, int32_t* out, hipStream_t stream);
 int gemv_max_rows(int K);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uint16_t* WdT,

@@ -116,6 +116,14 @@ def test_debug_and_timed_argument_errors(lib):
     assert t(*base, m8.LLMINT8_PATH_GEMM, ev, 2, ctypes.byref(nk)) == INVALID   # 3 kernels need 4 events
 
 
+def test_probe_argument_errors(lib):
+    p = lib.llmint8_probe_mfma_i8
+    assert p(0, 10, ALIGNED, None) == INVALID
+    assert p(4, 0, ALIGNED, None) == INVALID
+    assert p(4, 10, None, None) == INVALID
+    assert p(4, 10, MISALIGNED, None) == INVALID
+
+
 def test_workspace_size_covers_worst_case(lib):
     for T, K, N in [(1, 16, 1), (16, 1024, 1024), (2048, 4096, 11008), (4096, 8192, 28672)]:
         ws = lib.llmint8_workspace_bytes(T, K, N)

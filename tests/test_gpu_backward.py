@@ -225,3 +225,31 @@ def test_backward_input_maximum_n():
     dY = workloads.make_output_grad(26, T, N)
     dX = _host(m8.llmint8_linear_backward_input(_dev(dY), Wq, sW))
     check_y(dX, oracle.linear_backward_input(dY, Wq_ref, sW_ref), "f16")
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_backward_input_random_sweep(i):
+    """Seeded random shapes (T up to 600, K up to 4800, N up to 2400 in steps
+    of 8) in fp16 and bf16: the transposed dequantized weight bit-exact and dX
+    within the bar of its type."""
+    from parity_util import check_y
+    rng = np.random.default_rng(8000 + i)
+    T = int(rng.integers(1, 601))
+    K = 16 * int(rng.integers(1, 301))
+    N = 8 * int(rng.integers(1, 301))
+    bf16 = bool(rng.random() < 0.5)
+    _say(f"backward sweep {i}: T={T} K={K} N={N} bf16={bf16}")
+    if bf16:
+        Wq, sW, Wq_ref, sW_ref = _weights_bf16(8100 + i, N, K)
+        dY = workloads.as_bf16_input(workloads.make_output_grad(8100 + i, T, N))
+        WdT = _bf16_host(m8.llmint8_dequantize_weight_t_ex(Wq, sW, dtype=torch.bfloat16))
+        assert np.array_equal(WdT, np.ascontiguousarray(oracle.dequantize_weight(Wq_ref, sW_ref, "bf16").T))
+        dX = _bf16_host(m8.llmint8_linear_backward_input_ex(_bf16_dev(dY), Wq, sW))
+        check_y(dX, oracle.linear_backward_input(dY, Wq_ref, sW_ref, "bf16"), "bf16")
+    else:
+        Wq, sW, Wq_ref, sW_ref = _weights(8100 + i, N, K)
+        dY = workloads.make_output_grad(8100 + i, T, N)
+        WdT = _host(m8.llmint8_dequantize_weight_t(Wq, sW)).view(np.uint16)
+        assert np.array_equal(WdT, np.ascontiguousarray(oracle.dequantize_weight(Wq_ref, sW_ref).T).view(np.uint16))
+        dX = _host(m8.llmint8_linear_backward_input(_dev(dY), Wq, sW))
+        assert oracle.parity_error(dX, oracle.linear_backward_input(dY, Wq_ref, sW_ref)) <= DX_TOL

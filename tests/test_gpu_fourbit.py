@@ -204,3 +204,21 @@ def test_linear_long_rows(quant_type):
     """K = 65536: each of the 16 wavefronts of a row block walks 32 steps."""
     W, X = _weights(67, 40, 65536, 0.02), _acts(68, 3, 65536)
     linear_case("K=65536", W, X, 256, quant_type, "f16", bias=workloads.make_bias(69, 40))
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_linear_random_sweep(i):
+    """Seeded random decode shapes (T up to 40, K up to 5120, N up to 600), block
+    sizes, both code books, both 16-bit types, with and without bias: codes,
+    maxima and dequantized weights bit-exact, Y within the bar of its type."""
+    rng = np.random.default_rng(6000 + i)
+    T = int(rng.integers(1, 41))
+    K = 128 * int(rng.integers(1, 41))
+    N = int(rng.integers(1, 601))
+    block = int(rng.choice([b for b in (64, 128, 256, 512, 1024, 2048, 4096) if b <= max(64, K)]))
+    quant_type = str(rng.choice(["nf4", "fp4"]))
+    dtype = "bf16" if rng.random() < 0.5 else "f16"
+    W, X = _weights(6100 + i, N, K, 0.05), _acts(6200 + i, T, K)
+    b = workloads.make_bias(6300 + i, N, bf16=dtype == "bf16") if rng.random() < 0.5 else None
+    codec_case(f"sweep {i} codec", _as(dtype, W), block, quant_type, dtype)
+    linear_case(f"sweep {i}", _as(dtype, W), _as(dtype, X), block, quant_type, dtype, bias=b)

@@ -95,3 +95,21 @@ def test_blockwise_edge_cases():
     q, a = m8.llmint8_quantize_blockwise(x, 64)               # all-zero tensor
     assert not torch.any(q) and not torch.any(a)
     assert not torch.any(m8.llmint8_dequantize_blockwise(q, a, 64))
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_blockwise_random_sweep(i):
+    """Seeded random lengths (multiples of 16 up to 3 M), block sizes, input types
+    and value scales (down to subnormal fp16 and up to 1e4): codes, maxima and
+    both dequantized types bit-exact."""
+    rng = np.random.default_rng(5000 + i)
+    n = 16 * int(rng.integers(1, 200000))
+    block = int(rng.choice(BLOCKS))
+    dtype = np.float16 if rng.random() < 0.5 else np.float32
+    scale = float(10.0 ** rng.uniform(-6, 4))
+    x = rng.standard_normal(n) * scale
+    x[rng.random(n) < 0.01] = 0.0
+    _say(f"blockwise sweep {i}: n={n} block={block} dtype={np.dtype(dtype).name} scale={scale:.3g}")
+    with np.errstate(over="ignore"):
+        x = x.astype(dtype)
+    _check(x, block)

@@ -207,7 +207,9 @@ def main():
         "config": {"workload": "prefill_mlp_up", "T": T, "K": K, "N": N, "threshold": thr,
                    "injected_outlier_columns": int(len(cols)), "seed": w.seed,
                    "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "kb_gemm", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "int8 GEMM (kb_gemm_split for the 352x256 tile, "
+                                                 "kb_gemm for the others)",
+                     "gemm_tile": m8.llmint8_gemm_tile(T, N), "achieved": round(achieved, 2),
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "unit_note": "int8 tera-ops/s, 2 ops per multiply-add",
                      "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic,

@@ -362,6 +362,14 @@ LLMINT8_API llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t
  */
 LLMINT8_API llmint8_status llmint8_probe_mfma_i8(int blocks, int iters, int32_t* out, void* stream);
 
+/*
+ * The GEMM tile the GEMM route picks for T rows and N output features on the
+ * current device (its CU count; 256 when no device answers), as the
+ * LLMINT8_PATH_GEMM_<tile> value that forces it; LLMINT8_ERR_INVALID_ARG for
+ * T <= 0 or N <= 0. Host only; enqueues nothing.
+ */
+LLMINT8_API int llmint8_gemm_tile(int64_t T, int64_t N);
+
 /* Largest T the fused GEMV route accepts for this K (0 if none). */
 LLMINT8_API int llmint8_gemv_max_rows(int64_t K);
 

@@ -24,6 +24,7 @@ __all__ = [
     "LLMINT8_QUANT_NF4", "LLMINT8_QUANT_FP4", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit", "llmint8_linear_timed_ex",
     "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex", "llmint8_probe_mfma_i8",
+    "llmint8_gemm_tile",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -47,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "llmint8_linear_debug_ex", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "llmint8_linear_timed_ex",
     "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex", "llmint8_probe_mfma_i8",
+    "llmint8_gemm_tile",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -132,6 +134,8 @@ def load_library():
     lib.llmint8_linear_4bit.restype = ctypes.c_int
     lib.llmint8_probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
     lib.llmint8_probe_mfma_i8.restype = ctypes.c_int
+    lib.llmint8_gemm_tile.argtypes = [_i64, _i64]
+    lib.llmint8_gemm_tile.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
     lib.llmint8_gemv_max_rows.restype = ctypes.c_int
     lib.llmint8_status_string.argtypes = [ctypes.c_int]
@@ -189,6 +193,14 @@ def llmint8_probe_mfma_i8(blocks: int, iters: int, out, stream=None):
     _check(lib.llmint8_probe_mfma_i8(int(blocks), int(iters), _ptr(out), _stream(stream, out.device)),
            "llmint8_probe_mfma_i8")
     return blocks * 4 * iters * 4 * 2 * 32 * 32 * 32
+
+
+def llmint8_gemm_tile(T: int, N: int) -> str:
+    """Name ("352x256", ...) of the tile the GEMM route picks for T rows and N outputs."""
+    code = int(load_library().llmint8_gemm_tile(T, N))
+    if code < 0:
+        raise Llmint8Error(code, "llmint8_gemm_tile", 0)
+    return {v: k for k, v in LLMINT8_PATH_GEMM_TILES.items()}[code]
 
 
 def llmint8_gemv_max_rows(K: int) -> int:

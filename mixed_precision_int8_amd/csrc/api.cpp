@@ -479,6 +479,11 @@ llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t T, int64_t 
                                        static_cast<hipStream_t>(stream)));
 }
 
+int llmint8_gemm_tile(int64_t T, int64_t N) {
+  if (T <= 0 || N <= 0) return LLMINT8_ERR_INVALID_ARG;
+  return LLMINT8_PATH_GEMM_256x256 + choose_gemm_tile(T, N, device_cu_count());
+}
+
 llmint8_status llmint8_probe_mfma_i8(int blocks, int iters, int32_t* out, void* stream) {
   if (blocks <= 0 || iters <= 0 || !out || !aligned(out, 4)) return LLMINT8_ERR_INVALID_ARG;
   return hip_status(launch_probe_mfma_i8(blocks, iters, out, static_cast<hipStream_t>(stream)));

@@ -324,22 +324,23 @@ constexpr int kGroupN = 8;  // weight row-blocks per rasterization group
 // smaller tiles move more operand bytes per MFMA and run less efficiently; the
 // 352 x 256 tile runs about as efficiently per op as 256 x 256 and exists for
 // outputs that it covers in fewer rounds). `tile` >= 0 forces a candidate.
-hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream, int tile) {
+int choose_gemm_tile(int64_t T, int64_t N, int num_cus) {
   struct Cand { int bn, bt; double eff; };
   const Cand cands[kGemmTiles] = {{256, 256, 1.0}, {192, 256, 0.93}, {256, 128, 0.8}, {128, 128, 0.55},
                                   {352, 256, 1.0}};
   int best = 0;
-  if (tile >= 0 && tile < kGemmTiles) {
-    best = tile;
-  } else {
-    double best_cost = 1e300;
-    for (int i = 0; i < kGemmTiles; ++i) {
-      const double tiles = (double)ceil_div(a.N, cands[i].bn) * (double)ceil_div(a.T, cands[i].bt);
-      const double rounds = std::ceil(tiles / num_cus);
-      const double cost = rounds * cands[i].bn * cands[i].bt / cands[i].eff;
-      if (cost < best_cost * 0.999) { best_cost = cost; best = i; }
-    }
+  double best_cost = 1e300;
+  for (int i = 0; i < kGemmTiles; ++i) {
+    const double tiles = (double)ceil_div(N, cands[i].bn) * (double)ceil_div(T, cands[i].bt);
+    const double rounds = std::ceil(tiles / num_cus);
+    const double cost = rounds * cands[i].bn * cands[i].bt / cands[i].eff;
+    if (cost < best_cost * 0.999) { best_cost = cost; best = i; }
   }
+  return best;
+}
+
+hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream, int tile) {
+  const int best = tile >= 0 && tile < kGemmTiles ? tile : choose_gemm_tile(a.T, a.N, num_cus);
   switch (best) {
     case 0: return launch_gemm_tile<Tile256x256>(a, stream, kGroupN);
     case 1: return launch_gemm_tile<Tile192x256>(a, stream, kGroupN);

@@ -101,6 +101,7 @@ hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStrea
 // int8 GEMM tiles (N x T): 256x256, 192x256, 256x128, 128x128, 352x256; the
 // host picks one by cost unless `tile` (0..kGemmTiles-1) forces it.
 constexpr int kGemmTiles = 5;
+int choose_gemm_tile(int64_t T, int64_t N, int num_cus);  // host: the cost model's candidate
 hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream, int tile = -1);
 hipError_t launch_probe_mfma_i8(int blocks, int iters, int32_t* out, hipStream_t stream);
 int gemv_max_rows(int K);

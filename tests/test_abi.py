@@ -116,6 +116,20 @@ def test_debug_and_timed_argument_errors(lib):
     assert t(*base, m8.LLMINT8_PATH_GEMM, ev, 2, ctypes.byref(nk)) == INVALID   # 3 kernels need 4 events
 
 
+def test_gemm_tile_choice(lib):
+    """The host cost model (rounds of 256 CUs x tile time): the 2048 x 11008
+    layer fits one round of 352 x 256 tiles; the 4096 x 28672 layer is seven
+    full rounds of 256 x 256; small outputs take 128 x 128."""
+    t = lib.llmint8_gemm_tile
+    tiles = m8.LLMINT8_PATH_GEMM_TILES
+    assert t(2048, 11008) == tiles["352x256"]
+    assert t(4096, 28672) == tiles["256x256"]
+    assert t(2048, 14336) == tiles["256x256"]
+    assert t(16, 1024) == tiles["128x128"]
+    assert t(0, 16) == INVALID and t(16, 0) == INVALID
+    assert m8.llmint8_gemm_tile(2048, 11008) == "352x256"
+
+
 def test_probe_argument_errors(lib):
     p = lib.llmint8_probe_mfma_i8
     assert p(0, 10, ALIGNED, None) == INVALID

@@ -7,6 +7,7 @@ its type)."""
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ from test_gpu_bf16 import GEMM, GEMV, AUTO, _as, _bias, _small, run_case  # noqa
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = int(os.environ.get("LLMINT8_SWEEP_CASES", "160"))  # more for a longer soak
 TILES = sorted(m8.LLMINT8_PATH_GEMM_TILES.values())
 
 

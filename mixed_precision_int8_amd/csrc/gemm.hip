@@ -35,11 +35,19 @@ namespace llmint8 {
 // first chunk of 32 outlier columns (k-step h of block i / j); later chunks
 // are read from memory here. Output layout of a 32x32 block: lane holds, for
 // column (t) lane&31, rows (n) 8*q + 4*(lane>>5) + r in register 4*q + r.
+//
+// Y is written one of two ways. Directly, each lane stores its 4-value pieces
+// (16 contiguous bytes of an output row per instruction). Or, when `stage`
+// (a wavefront-private LDS area of kStageBytes) is given, the tile lies wholly
+// inside Y and rows are 16-byte aligned, through LDS: two 32-row blocks are
+// gathered as 64 output rows of 128 bytes and stored as whole 128-byte lines.
+constexpr int kStagePitch = 144;  // bytes per staged output row: 128 + 16 (conflict-free writes)
+constexpr int kStageBytes = 64 * kStagePitch;
 template <bool BF16, int FNW, int FT, class WF, class XF>
 __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&acc)[FNW][FT], int nw0,
                                               int tw0, const float* sW_w, const float* aX_w,
                                               const uint16_t* bias_w, int nch, int lane, WF&& wf,
-                                              XF&& xf) {
+                                              XF&& xf, char* stage = nullptr) {
   using A16 = Act16<BF16>;
   const int N = a.N, T = a.T;
   const int fi = lane & 31, fg = lane >> 5;
@@ -107,6 +115,31 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
 #pragma unroll
         for (int j = 0; j < FT; ++j) y[j][v] += bv;
       }
+    }
+    if constexpr (FT == 2) if (stage) {  // uniform; 64 staged rows
+      // block i -> column half (i & 1) of the staged rows t = 32 j + fi
+#pragma unroll
+      for (int j = 0; j < FT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 p;
+          p.x = (uint32_t)A16::from_f32(y[j][4 * q]) | ((uint32_t)A16::from_f32(y[j][4 * q + 1]) << 16);
+          p.y = (uint32_t)A16::from_f32(y[j][4 * q + 2]) | ((uint32_t)A16::from_f32(y[j][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(stage + (j * 32 + fi) * kStagePitch + (i & 1) * 64 + 8 * fg + 16 * q) = p;
+        }
+      if ((i & 1) || i == FNW - 1) {
+        // flush: 64 rows of nb * 64 bytes, 16 bytes per lane and instruction
+        const int nb = (i & 1) + 1, cpr = 4 * nb;  // blocks, 16-byte chunks per row
+        const int i0 = i - (i & 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k * (64 / cpr) >= 64) break;  // nb == 1: four passes
+          const int row = lane / cpr + k * (64 / cpr), c = lane % cpr;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kStagePitch + c * 16);
+          *reinterpret_cast<uint4*>(a.Y + (size_t)(tw0 + row) * N + nw0 + i0 * 32 + c * 8) = v;
+        }
+      }
+      continue;
     }
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
@@ -204,9 +237,14 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
         xf0[j][h] = *reinterpret_cast<const uint4*>(a.Xo + (size_t)t * kOutChunk + h * 16 + fg * 8);
     }
   }
+  // Y through LDS in whole lines (2-slot rings only: their K loop ends with
+  // every copy landed, so the whole ring is free)
+  constexpr bool kCanStage = G::NSTAGE == 2 && G::FT == 2 && G::NWAVES * kStageBytes <= G::LDS;
+  const bool staged = kCanStage && rows_n == G::BN && rows_t == G::BT && (N & 7) == 0;
   gemm_epilogue<BF16, G::FN, G::FT>(
       a, acc, nw0, tw0, sW_l + wn * G::WN, aX_l + wt * G::WT, a.bias ? bias_l + wn * G::WN : nullptr,
-      nch, lane, [&](int i, int h) { return wf0[i][h]; }, [&](int j, int h) { return xf0[j][h]; });
+      nch, lane, [&](int i, int h) { return wf0[i][h]; }, [&](int j, int h) { return xf0[j][h]; },
+      staged ? smem + wave * kStageBytes : nullptr);
 }
 
 // One wavefront column of a SplitTile: FNW row blocks from tile row wrow.
@@ -258,6 +296,11 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
     __syncthreads();
   }
   const int fi = lane & 31, fg = lane >> 5;
+  // Y through LDS in whole lines when the tile lies inside Y and its rows are
+  // 16-byte aligned: each wavefront stages in its own part of the last slot
+  static_assert(G::NWAVES * kStageBytes <= G::STAGE, "staging fits the last slot");
+  const bool staged = rows_n == G::BN && rows_t == G::BT && (a.N & 7) == 0;
+  char* last_slot = epi == smem ? smem + G::STAGE : smem;  // the last stage's slot, free now
   gemm_epilogue<BF16, FNW, G::FT>(
       a, acc, n0 + wrow, t0 + wcol, sW_l + wrow, aX_l + wcol, a.bias ? bias_l + wrow : nullptr, nch,
       lane,
@@ -268,7 +311,8 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
       [&](int j, int h) {
         const int r = G::BN + wcol + j * 32 + fi;
         return *reinterpret_cast<const uint4*>(epi + r * 64 + (((2 * h + fg) ^ ((r >> 2) & 3)) * 16));
-      });
+      },
+      staged ? last_slot + wave * kStageBytes : nullptr);
 }
 
 template <class G, bool BF16>

@@ -41,8 +41,6 @@ namespace llmint8 {
 // (a wavefront-private LDS area of kStageBytes) is given, the tile lies wholly
 // inside Y and rows are 16-byte aligned, through LDS: two 32-row blocks are
 // gathered as 64 output rows of 128 bytes and stored as whole 128-byte lines.
-constexpr int kStagePitch = 144;  // bytes per staged output row: 128 + 16 (conflict-free writes)
-constexpr int kStageBytes = 64 * kStagePitch;
 template <bool BF16, int FNW, int FT, class WF, class XF>
 __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&acc)[FNW][FT], int nw0,
                                               int tw0, const float* sW_w, const float* aX_w,
@@ -125,20 +123,10 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
           uint2 p;
           p.x = (uint32_t)A16::from_f32(y[j][4 * q]) | ((uint32_t)A16::from_f32(y[j][4 * q + 1]) << 16);
           p.y = (uint32_t)A16::from_f32(y[j][4 * q + 2]) | ((uint32_t)A16::from_f32(y[j][4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(stage + (j * 32 + fi) * kStagePitch + (i & 1) * 64 + 8 * fg + 16 * q) = p;
+          stage_put(stage, i, j, q, fi, fg, p);
         }
-      if ((i & 1) || i == FNW - 1) {
-        // flush: 64 rows of nb * 64 bytes, 16 bytes per lane and instruction
-        const int nb = (i & 1) + 1, cpr = 4 * nb;  // blocks, 16-byte chunks per row
-        const int i0 = i - (i & 1);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (k * (64 / cpr) >= 64) break;  // nb == 1: four passes
-          const int row = lane / cpr + k * (64 / cpr), c = lane % cpr;
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kStagePitch + c * 16);
-          *reinterpret_cast<uint4*>(a.Y + (size_t)(tw0 + row) * N + nw0 + i0 * 32 + c * 8) = v;
-        }
-      }
+      if ((i & 1) || i == FNW - 1)
+        stage_flush(stage, (i & 1) + 1, lane, a.Y + (size_t)tw0 * N + nw0 + (i - (i & 1)) * 32, N);
       continue;
     }
 #pragma unroll

@@ -415,4 +415,29 @@ __device__ __forceinline__ void gemm_kloop_split(char* smem, __amdgpu_buffer_rsr
     for (int i = 0; i < FNW; ++i) acc[i][j] = Mma::run(fa[i], fb[j], acc[i][j]);
 }
 
+// Output staging for the GEMM epilogues. A wavefront's results for a pair of
+// 32-row blocks (i even, i + 1) and its 64 output rows are gathered in a
+// private LDS area as 64 rows of 128 bytes, then stored as whole 128-byte
+// lines (8 rows per instruction) instead of 16-byte pieces of 32 rows.
+constexpr int kStagePitch = 144;  // bytes per staged row: 128 + 16 (conflict-free writes)
+constexpr int kStageBytes = 64 * kStagePitch;
+
+// the 4 packed 16-bit values (columns 8q + 4fg .. +3 of block i, output row
+// 32j + fi) of one lane
+__device__ __forceinline__ void stage_put(char* stage, int i, int j, int q, int fi, int fg, uint2 p) {
+  *reinterpret_cast<uint2*>(stage + (j * 32 + fi) * kStagePitch + (i & 1) * 64 + 8 * fg + 16 * q) = p;
+}
+
+// the staged nb (1 or 2) blocks -> out[row * ld + 0 .. nb * 32), rows 0..63
+__device__ __forceinline__ void stage_flush(const char* stage, int nb, int lane, uint16_t* out, size_t ld) {
+  const int cpr = 4 * nb, rpp = 64 / cpr;  // 16-byte chunks per row, rows per pass
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k * rpp >= 64) break;
+    const int row = lane / cpr + k * rpp, c = lane % cpr;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kStagePitch + c * 16);
+    *reinterpret_cast<uint4*>(out + (size_t)row * ld + c * 8) = v;
+  }
+}
+
 }  // namespace llmint8

@@ -98,6 +98,17 @@ def committed_traffic(path=None, files=None, key="hbm_bytes_per_launch"):
     return float(m.group(1)) if m else None
 
 
+def committed_mfma_activity():
+    """(MFMA busy %, effective shader clock in GHz) of the prefill GEMM from the
+    committed counter summary, or (None, None) when absent or stale."""
+    if committed_traffic() is None:
+        return None, None
+    text = open(PROFILE_COUNTERS).read()
+    busy = re.search(r"=\s*([0-9.]+)% MFMA busy", text)
+    clock = re.search(r"=\s*([0-9.]+) GHz", text)
+    return (float(busy.group(1)) if busy else None, float(clock.group(1)) if clock else None)
+
+
 def graph_us_per_call(fn, n_calls, replays, stream):
     """fn(0) .. fn(n_calls - 1) captured once in a HIP graph and replayed: microseconds
     per call without the per-call host (Python) submission cost. The calls must
@@ -189,6 +200,7 @@ def main():
     gemm_ms = per_kernel[-1]
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     traffic = committed_traffic()
+    mfma_busy, sclk = committed_mfma_activity()
 
     result = {
         "metric": METRIC,
@@ -210,6 +222,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "int8 GEMM (kb_gemm_split for the 352x256 tile, "
                                                  "kb_gemm for the others)",
                      "gemm_tile": m8.llmint8_gemm_tile(T, N), "achieved": round(achieved, 2),
+                     "counters": {"mfma_busy_pct": mfma_busy, "effective_sclk_ghz": sclk,
+                                  "source": "profiles/kb_gemm_prefill_counters.txt"},
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "unit_note": "int8 tera-ops/s, 2 ops per multiply-add",
                      "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic,

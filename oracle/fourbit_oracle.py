@@ -22,8 +22,7 @@ Sources, by page title and section:
            scheme list: NF4 is an information-theoretically optimized
            non-uniform 4-bit format.
 
-Readings where the pages leave a step open (each also listed, with its reason,
-in the design notes):
+Readings where the pages leave a step open:
 
 * F1  code books (the pages give no values). NF4 follows the published
       NormalFloat construction: eight positive levels at standard-normal

@@ -27,8 +27,7 @@ are cited by page title and section:
            large *activation* values are kept in higher precision) and the
            introduction (weights are quantized when the model loads).
 
-Readings where the pages leave a step open (each one is also listed, with its
-reason, in the design notes):
+Readings where the pages leave a step open:
 
 * R1  an outlier is a whole *column* (feature dimension) of X, decided over all
       T rows of the call; the weight has no threshold.

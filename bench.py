@@ -135,7 +135,7 @@ def graph_us_per_call(fn, n_calls, replays, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 

@@ -4,7 +4,7 @@ row queries, code books) under AddressSanitizer and UndefinedBehaviorSanitizer.
 The library's sources are compiled as for the product (gfx950 device code
 included, though nothing here launches) with the sanitizers on the host pass
 only, linked with the C driver tests/host_check.c and run on the CPU. Any
-sanitizer report aborts the driver.
+sanitizer report aborts the C driver.
 """
 from __future__ import annotations
 

@@ -109,6 +109,28 @@ def committed_mfma_activity():
     return (float(busy.group(1)) if busy else None, float(clock.group(1)) if clock else None)
 
 
+def probe_mfma_i8(blocks, iters, out, stream):
+    """The matrix-core rate probe (libllmint8_probe.so, a measurement helper built beside
+    the product library): blocks x 4 wavefronts, each iters x 4 v_mfma_i32_32x32x32_i8.
+    Returns the int8 operation count of the call."""
+    import ctypes
+    global _PROBE
+    if _PROBE is None:
+        path = os.path.join(ROOT, "mixed_precision_int8_amd", "libllmint8_probe.so")
+        _PROBE = ctypes.CDLL(path)
+        _PROBE.llmint8_bench_probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                       ctypes.c_void_p]
+        _PROBE.llmint8_bench_probe_mfma_i8.restype = ctypes.c_int
+    st = _PROBE.llmint8_bench_probe_mfma_i8(int(blocks), int(iters), ctypes.c_void_p(out.data_ptr()),
+                                            ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise RuntimeError(f"probe launch failed ({st})")
+    return blocks * 4 * iters * 4 * 2 * 32 * 32 * 32
+
+
+_PROBE = None
+
+
 def graph_us_per_call(fn, n_calls, replays, stream):
     """fn(0) .. fn(n_calls - 1) captured once in a HIP graph and replayed: microseconds
     per call without the per-call host (Python) submission cost. The calls must
@@ -239,14 +261,14 @@ def main():
         pblocks, piters = 4 * cus, 2000
         pout = torch.empty((pblocks * 256,), dtype=torch.int32, device=dev)
         for _ in range(3):
-            pops = m8.llmint8_probe_mfma_i8(pblocks, piters, pout)
+            pops = probe_mfma_i8(pblocks, piters, pout, stream)
         torch.cuda.synchronize()
         pms = []
         for _ in range(5):
             p0 = torch.cuda.Event(enable_timing=True)
             p1 = torch.cuda.Event(enable_timing=True)
             p0.record(stream)
-            m8.llmint8_probe_mfma_i8(pblocks, piters, pout)
+            probe_mfma_i8(pblocks, piters, pout, stream)
             p1.record(stream)
             torch.cuda.synchronize()
             pms.append(p0.elapsed_time(p1))

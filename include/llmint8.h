@@ -62,7 +62,7 @@ typedef int llmint8_status;
 #define LLMINT8_OK               0
 #define LLMINT8_ERR_INVALID_ARG -1 /* null pointer, size <= 0 (T < 0), bad threshold, misaligned */
 #define LLMINT8_ERR_UNSUPPORTED -2 /* K % 16 != 0, K > 65536, N*K or T*K >= 2^31 (backward: N % 8 != 0 or N > 65536) */
-#define LLMINT8_ERR_WORKSPACE   -3 /* workspace smaller than llmint8_workspace_bytes(T,K,N) */
+#define LLMINT8_ERR_WORKSPACE   -3 /* workspace smaller than llmint8_workspace_bytes_path(T,K,N,path) */
 #define LLMINT8_ERR_HIP         -4 /* a HIP launch or runtime call failed */
 
 /* Kernel route for llmint8_linear_debug / llmint8_linear_timed. */
@@ -91,11 +91,25 @@ LLMINT8_API llmint8_status llmint8_quantize_weight(const void* W, int64_t N, int
                                        float* sW, void* stream);
 
 /*
- * Bytes of device workspace llmint8_linear needs for a call with these sizes.
- * The size covers the worst case of every column being an outlier; it does
- * not depend on the data. Returns 0 for invalid sizes.
+ * Bytes of device workspace llmint8_linear needs for a call with these sizes,
+ * which never depends on the data. It is 0 when the call takes the fused
+ * decode kernel (T <= llmint8_gemv_max_rows(K)), which keeps everything in
+ * LDS. On the GEMM route it is the int8 activations (T*K bytes) and a few
+ * small tables, plus room for the 16-bit operands of the first 512 outlier
+ * columns (2*(T+N) bytes per column, at most 2*(T+N)*K for K < 512). A larger
+ * workspace holds the operands of more outlier columns; the epilogue forms
+ * those of columns past what the workspace holds from X and Wq directly, with
+ * the same values, so any outlier count is handled. Returns 0 for invalid
+ * sizes.
  */
 LLMINT8_API size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N);
+
+/*
+ * llmint8_workspace_bytes for a debug or timed call with the given route
+ * (LLMINT8_PATH_*): 0 for the fused decode route, the GEMM route's size for
+ * the GEMM route at any T. Returns 0 for invalid sizes or an unknown path.
+ */
+LLMINT8_API size_t llmint8_workspace_bytes_path(int64_t T, int64_t K, int64_t N, int path);
 
 /*
  * The forward of the LLM.int8() linear layer ("Hugging Face Quantization with
@@ -106,7 +120,8 @@ LLMINT8_API size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N);
  *                   16-bit part; NaN or <= 0 is LLMINT8_ERR_INVALID_ARG
  *   Y         [out] fp16 [T, N], device
  *   workspace [tmp] device, >= llmint8_workspace_bytes(T, K, N) bytes,
- *                   256-byte aligned; contents on entry do not matter
+ *                   256-byte aligned; contents on entry do not matter. May be
+ *                   NULL (with any workspace_bytes) when that size is 0.
  * T == 0 is a valid no-op. The outlier set is decided over all T rows of the
  * call. Every stage runs on the GPU; the host never waits.
  */
@@ -285,17 +300,18 @@ LLMINT8_API llmint8_status llmint8_linear_debug_ex(const void* X, int dtype, int
                                                    int8_t* Xq, float* aX, int32_t* C);
 
 /*
- * 4-bit weights: NF4 and FP4 ("bitsandbytes: GPU-Accelerated Inference and
- * Training at Lower Bit Depths", introduction: the 4-bit layer supports FP4
- * and NF4, quantizes the weight in blocks that each carry a scaling factor and
- * computes in FP16 or BF16 with the weight dequantized per operation;
+ * 4-bit weights: NF4 and FP4 ("bitsandbytes" glossary, "What it provides":
+ * the 4-bit layer supports FP4 and NF4, quantizes the weight in blocks that
+ * each carry a scaling factor and computes in FP16 or BF16 with the weight
+ * dequantized per operation;
  * "Hugging Face Quantization with bitsandbytes ...", section 4: NF4 places its
  * levels where normally distributed weights concentrate, FP4 is a generic
  * 4-bit float).
  *
  * Code books (the pages name the types but print no values; this library
  * computes them on the host in binary64 and rounds once to fp32):
- *   NF4  the published NormalFloat construction: standard-normal quantiles at
+ *   NF4  the published NormalFloat construction (Dettmers et al., "QLoRA:
+ *        Efficient Finetuning of Quantized LLMs", 2023, section 3): standard-normal quantiles at
  *        probabilities p_max + i (0.5 - p_max) / 8 (i = 0..7) above zero and
  *        their mirror images at p_max + i (0.5 - p_max) / 7 (i = 0..6) below,
  *        plus an exact zero, divided by the quantile at p_max = 1 - (1/32 +
@@ -349,18 +365,6 @@ LLMINT8_API llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t
                                                const uint8_t* packed, const float* absmax,
                                                int64_t block, int quant_type, int64_t N,
                                                const void* bias, void* Y, void* stream);
-
-/*
- * Measurement helper, not part of the method: the rate of the matrix-core
- * instruction the int8 GEMM uses (v_mfma_i32_32x32x32_i8, 2 x 32 x 32 x 32
- * int8 operations each) with no memory traffic. Enqueues `blocks` workgroups
- * of 256 threads; each of their 4 wavefronts issues iters x 4 independent
- * MFMAs, then every thread writes one checksum to out (int32 [blocks * 256],
- * device) so that the work is kept. Operations per call:
- * blocks * 4 * iters * 4 * 65536. LLMINT8_ERR_INVALID_ARG for blocks <= 0,
- * iters <= 0 or out NULL.
- */
-LLMINT8_API llmint8_status llmint8_probe_mfma_i8(int blocks, int iters, int32_t* out, void* stream);
 
 /*
  * The GEMM tile the GEMM route picks for T rows and N output features on the

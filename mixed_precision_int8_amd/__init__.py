@@ -15,6 +15,7 @@ __all__ = [
     "LLMINT8_PATH_AUTO", "LLMINT8_PATH_GEMM", "LLMINT8_PATH_GEMV", "LLMINT8_PATH_GEMM_TILES",
     "Llmint8Error",
     "library_path", "load_library", "llmint8_quantize_weight", "llmint8_workspace_bytes",
+    "llmint8_workspace_bytes_path", "shared_workspace_bytes",
     "llmint8_linear", "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
     "llmint8_status_string", "llmint8_backward_workspace_bytes", "llmint8_dequantize_weight_t",
     "llmint8_linear_backward_input", "llmint8_linear_backward_input_timed", "Int8Linear",
@@ -23,7 +24,7 @@ __all__ = [
     "llmint8_quantize_weight_ex", "llmint8_linear_ex", "llmint8_linear_debug_ex",
     "LLMINT8_QUANT_NF4", "LLMINT8_QUANT_FP4", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit", "llmint8_linear_timed_ex",
-    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex", "llmint8_probe_mfma_i8",
+    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
     "llmint8_gemm_tile",
 ]
 
@@ -39,7 +40,8 @@ LLMINT8_QUANT_NF4 = 0
 LLMINT8_QUANT_FP4 = 1
 
 EXPORTED_SYMBOLS = (
-    "llmint8_quantize_weight", "llmint8_workspace_bytes", "llmint8_linear",
+    "llmint8_quantize_weight", "llmint8_workspace_bytes", "llmint8_workspace_bytes_path",
+    "llmint8_linear",
     "llmint8_linear_debug", "llmint8_linear_timed", "llmint8_gemv_max_rows",
     "llmint8_status_string", "llmint8_last_hip_error", "llmint8_backward_workspace_bytes",
     "llmint8_dequantize_weight_t", "llmint8_linear_backward_input",
@@ -47,7 +49,7 @@ EXPORTED_SYMBOLS = (
     "llmint8_dequantize_blockwise", "llmint8_quantize_weight_ex", "llmint8_linear_ex",
     "llmint8_linear_debug_ex", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "llmint8_linear_timed_ex",
-    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex", "llmint8_probe_mfma_i8",
+    "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
     "llmint8_gemm_tile",
 )
 
@@ -85,6 +87,8 @@ def load_library():
     lib.llmint8_quantize_weight.restype = ctypes.c_int
     lib.llmint8_workspace_bytes.argtypes = [_i64, _i64, _i64]
     lib.llmint8_workspace_bytes.restype = ctypes.c_size_t
+    lib.llmint8_workspace_bytes_path.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+    lib.llmint8_workspace_bytes_path.restype = ctypes.c_size_t
     lin = [_vp, _i64, _i64, _vp, _vp, _i64, ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
     lib.llmint8_linear.argtypes = lin
     lib.llmint8_linear.restype = ctypes.c_int
@@ -132,8 +136,6 @@ def load_library():
     lib.llmint8_linear_4bit.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64, ctypes.c_int,
                                         _i64, _vp, _vp, _vp]
     lib.llmint8_linear_4bit.restype = ctypes.c_int
-    lib.llmint8_probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
-    lib.llmint8_probe_mfma_i8.restype = ctypes.c_int
     lib.llmint8_gemm_tile.argtypes = [_i64, _i64]
     lib.llmint8_gemm_tile.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
@@ -183,16 +185,8 @@ def llmint8_workspace_bytes(T: int, K: int, N: int) -> int:
     return int(load_library().llmint8_workspace_bytes(T, K, N))
 
 
-def llmint8_probe_mfma_i8(blocks: int, iters: int, out, stream=None):
-    """Measurement helper: enqueue the matrix-core rate probe (blocks x 4 wavefronts, each
-    iters x 4 v_mfma_i32_32x32x32_i8); ``out`` int32 [blocks * 256] receives checksums.
-    Returns the int8 operation count of the call."""
-    import torch
-    lib = load_library()
-    _need(out, torch.int32, (blocks * 256,), "out")
-    _check(lib.llmint8_probe_mfma_i8(int(blocks), int(iters), _ptr(out), _stream(stream, out.device)),
-           "llmint8_probe_mfma_i8")
-    return blocks * 4 * iters * 4 * 2 * 32 * 32 * 32
+def llmint8_workspace_bytes_path(T: int, K: int, N: int, path: int = LLMINT8_PATH_AUTO) -> int:
+    return int(load_library().llmint8_workspace_bytes_path(T, K, N, int(path)))
 
 
 def llmint8_gemm_tile(T: int, N: int) -> str:
@@ -256,15 +250,22 @@ def llmint8_quantize_weight_ex(W, Wq=None, sW=None, stream=None):
     return Wq, sW
 
 
-def _workspace(T, K, N, device, workspace):
+def _workspace(T, K, N, device, workspace, path=LLMINT8_PATH_AUTO):
+    """The caller's workspace, or a new one of the size the route needs (None when the
+    route needs none: the fused decode kernel keeps everything in LDS)."""
     import torch
-    need = llmint8_workspace_bytes(T, K, N)
     if workspace is None:
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=device)
+        need = llmint8_workspace_bytes_path(T, K, N, path)
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=device)
     return workspace
 
 
-def _linear_args(X, Wq, sW, threshold, Y, workspace, dtype=None, bias=None):
+def _ws_bytes(ws):
+    return 0 if ws is None else _ws_bytes(ws)
+
+
+def _linear_args(X, Wq, sW, threshold, Y, workspace, dtype=None, bias=None, path=LLMINT8_PATH_AUTO):
     import torch
     T, K = X.shape
     N = Wq.shape[0]
@@ -277,7 +278,7 @@ def _linear_args(X, Wq, sW, threshold, Y, workspace, dtype=None, bias=None):
     if Y is None:
         Y = torch.empty((T, N), dtype=dtype, device=X.device)
     _need(Y, dtype, (T, N), "Y")
-    workspace = _workspace(T, K, N, X.device, workspace)
+    workspace = _workspace(T, K, N, X.device, workspace, path)
     thr = float(threshold)
     if thr == math.inf:
         thr = math.inf
@@ -289,7 +290,7 @@ def llmint8_linear(X, Wq, sW, threshold: float = 6.0, Y=None, workspace=None, st
     lib = load_library()
     T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
     _check(lib.llmint8_linear(_ptr(X), T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(Y), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(stream, X.device)),
+                              _ws_bytes(ws), _stream(stream, X.device)),
            "llmint8_linear")
     return Y
 
@@ -302,7 +303,7 @@ def llmint8_linear_ex(X, Wq, sW, threshold: float = 6.0, bias=None, Y=None, work
     code = _act_dtype(X.dtype)
     T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias)
     _check(lib.llmint8_linear_ex(_ptr(X), code, T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(bias),
-                                 _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _ptr(Y), _ptr(ws), _ws_bytes(ws),
                                  _stream(stream, X.device)),
            "llmint8_linear_ex")
     return Y
@@ -316,11 +317,11 @@ def llmint8_linear_timed_ex(X, Wq, sW, threshold, Y, workspace, events, bias=Non
     """
     lib = load_library()
     code = _act_dtype(X.dtype)
-    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias)
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias, path)
     handles = (_vp * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     nk = ctypes.c_int(0)
     _check(lib.llmint8_linear_timed_ex(_ptr(X), code, T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(bias),
-                                       _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _ptr(Y), _ptr(ws), _ws_bytes(ws),
                                        _stream(stream, X.device), int(path), handles, len(events),
                                        ctypes.byref(nk)),
            "llmint8_linear_timed_ex")
@@ -346,11 +347,11 @@ def llmint8_linear_debug_ex(X, Wq, sW, threshold: float = 6.0, bias=None,
     """llmint8_linear_ex plus the intermediates of the same kernels: dict of tensors."""
     lib = load_library()
     code = _act_dtype(X.dtype)
-    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias)
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, X.dtype, bias, path)
     dev = X.device
     out = _debug_outputs(T, K, N, dev, want_C)
     _check(lib.llmint8_linear_debug_ex(_ptr(X), code, T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(bias),
-                                       _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _ptr(Y), _ptr(ws), _ws_bytes(ws),
                                        _stream(stream, dev), int(path), _ptr(out["bitmap"]),
                                        _ptr(out["idx"]), _ptr(out["count"]), _ptr(out["Xq"]),
                                        _ptr(out["aX"]), _ptr(out["C"])),
@@ -363,11 +364,11 @@ def llmint8_linear_debug(X, Wq, sW, threshold: float = 6.0, path: int = LLMINT8_
                          Y=None, workspace=None, stream=None, want_C: bool = True):
     """Forward plus the intermediates of the same kernels: dict of tensors."""
     lib = load_library()
-    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, path=path)
     dev = X.device
     out = _debug_outputs(T, K, N, dev, want_C)
     _check(lib.llmint8_linear_debug(_ptr(X), T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(Y), _ptr(ws),
-                                    ws.numel() * ws.element_size(), _stream(stream, dev), int(path),
+                                    _ws_bytes(ws), _stream(stream, dev), int(path),
                                     _ptr(out["bitmap"]), _ptr(out["idx"]), _ptr(out["count"]),
                                     _ptr(out["Xq"]), _ptr(out["aX"]), _ptr(out["C"])),
            "llmint8_linear_debug")
@@ -382,11 +383,11 @@ def llmint8_linear_timed(X, Wq, sW, threshold, Y, workspace, events, path=LLMINT
     Returns the number of kernels launched.
     """
     lib = load_library()
-    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace)
+    T, K, N, Y, ws, thr = _linear_args(X, Wq, sW, threshold, Y, workspace, path=path)
     handles = (_vp * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     nk = ctypes.c_int(0)
     _check(lib.llmint8_linear_timed(_ptr(X), T, K, _ptr(Wq), _ptr(sW), N, thr, _ptr(Y), _ptr(ws),
-                                    ws.numel() * ws.element_size(), _stream(stream, X.device),
+                                    _ws_bytes(ws), _stream(stream, X.device),
                                     int(path), handles, len(events), ctypes.byref(nk)),
            "llmint8_linear_timed")
     return nk.value
@@ -434,7 +435,7 @@ def llmint8_linear_backward_input(dY, Wq, sW, dX=None, workspace=None, stream=No
     lib = load_library()
     T, K, N, dX, ws = _backward_args(dY, Wq, sW, dX, workspace)
     _check(lib.llmint8_linear_backward_input(_ptr(dY), T, K, _ptr(Wq), _ptr(sW), N, _ptr(dX),
-                                             _ptr(ws), ws.numel() * ws.element_size(),
+                                             _ptr(ws), _ws_bytes(ws),
                                              _stream(stream, dY.device)),
            "llmint8_linear_backward_input")
     return dX
@@ -446,7 +447,7 @@ def llmint8_linear_backward_input_ex(dY, Wq, sW, dX=None, workspace=None, stream
     code = _act_dtype(dY.dtype)
     T, K, N, dX, ws = _backward_args(dY, Wq, sW, dX, workspace, dY.dtype)
     _check(lib.llmint8_linear_backward_input_ex(_ptr(dY), code, T, K, _ptr(Wq), _ptr(sW), N,
-                                                _ptr(dX), _ptr(ws), ws.numel() * ws.element_size(),
+                                                _ptr(dX), _ptr(ws), _ws_bytes(ws),
                                                 _stream(stream, dY.device)),
            "llmint8_linear_backward_input_ex")
     return dX
@@ -476,7 +477,7 @@ def llmint8_linear_backward_input_timed(dY, Wq, sW, events, dX=None, workspace=N
     handles = (_vp * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     nk = ctypes.c_int(0)
     _check(lib.llmint8_linear_backward_input_timed(_ptr(dY), T, K, _ptr(Wq), _ptr(sW), N, _ptr(dX),
-                                                   _ptr(ws), ws.numel() * ws.element_size(),
+                                                   _ptr(ws), _ws_bytes(ws),
                                                    _stream(stream, dY.device), handles, len(events),
                                                    ctypes.byref(nk)),
            "llmint8_linear_backward_input_timed")
@@ -676,6 +677,29 @@ def _fp16():
     return torch.float16
 
 
+# One forward workspace per (device, stream), shared by every Int8Linear: calls on one
+# stream run one after another, so layers never use it at the same time.
+_SHARED_WS = {}
+
+
+def _shared_workspace(need, device):
+    import torch
+    if need == 0:
+        return None
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream(device).cuda_stream)
+    ws = _SHARED_WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty((need,), dtype=torch.uint8, device=device)
+        _SHARED_WS[key] = ws
+    return ws
+
+
+def shared_workspace_bytes() -> int:
+    """Device bytes held by the forward workspaces that Int8Linear layers share."""
+    return sum(ws.numel() for ws in _SHARED_WS.values())
+
+
 class Int8Linear:
     """Drop-in int8 replacement of an fp16 or bf16 linear layer, with or without bias.
 
@@ -696,25 +720,21 @@ class Int8Linear:
         self.dtype = weight.dtype
         self.Wq, self.sW = llmint8_quantize_weight_ex(weight.contiguous())
         self.bias = None if bias is None else bias.detach().to(weight.dtype).contiguous()
-        self._ws = None
 
     def memory_bytes(self) -> int:
+        """Device bytes this layer holds: the int8 weight, its scales and the bias. The
+        forward's scratch is not per layer: every Int8Linear on a device and stream shares
+        one workspace (``shared_workspace_bytes()``), and the fused decode route needs none."""
         extra = 0 if self.bias is None else self.bias.numel() * 2
         return self.Wq.numel() + self.sW.numel() * 4 + extra
 
     def _forward(self, X2):
-        ws = self._workspace(X2.shape[0], X2.device)
+        ws = _shared_workspace(llmint8_workspace_bytes(X2.shape[0], self.in_features,
+                                                       self.out_features), X2.device)
         if self.dtype == _fp16() and self.bias is None:
             return llmint8_linear(X2, self.Wq, self.sW, self.threshold, workspace=ws)
         return llmint8_linear_ex(X2, self.Wq, self.sW, self.threshold, bias=self.bias,
                                  workspace=ws)
-
-    def _workspace(self, T, device):
-        import torch
-        need = max(llmint8_workspace_bytes(T, self.in_features, self.out_features), 256)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty((need,), dtype=torch.uint8, device=device)
-        return self._ws
 
     def forward(self, X):
         """Y = the LLM.int8() forward of X. When X requires a gradient, the

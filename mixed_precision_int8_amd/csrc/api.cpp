@@ -25,15 +25,8 @@ llmint8_status hip_status(hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-constexpr double kTwo31 = 2147483648.0;
-
-llmint8_status check_sizes(int64_t T, int64_t K, int64_t N) {
-  if (T < 0 || K <= 0 || N <= 0) return LLMINT8_ERR_INVALID_ARG;
-  if (K % 16 != 0 || K > kMaxK) return LLMINT8_ERR_UNSUPPORTED;
-  if ((double)N * (double)K >= kTwo31 || (double)T * (double)K >= kTwo31) return LLMINT8_ERR_UNSUPPORTED;
-  if ((double)T * (double)N >= 16.0 * kTwo31) return LLMINT8_ERR_UNSUPPORTED;
-  return LLMINT8_OK;
-}
+// size limits: ranges.h (shared with the kernels' buffer windows)
+llmint8_status check_sizes(int64_t T, int64_t K, int64_t N) { return admit_linear(T, K, N); }
 
 int device_cu_count() {
   static std::mutex mu;
@@ -62,17 +55,22 @@ llmint8_status validate_linear(const void* X, int64_t T, int64_t K, const int8_t
   if (!Wq || !sW) return LLMINT8_ERR_INVALID_ARG;
   if (!aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
   if (T == 0) return LLMINT8_OK;
-  if (!X || !Y || !workspace) return LLMINT8_ERR_INVALID_ARG;
-  if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(workspace, kWsAlign)) return LLMINT8_ERR_INVALID_ARG;
-  if (workspace_bytes < ws_layout(T, K, N).total) return LLMINT8_ERR_WORKSPACE;
+  if (!X || !Y) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Y, 16)) return LLMINT8_ERR_INVALID_ARG;
+  return LLMINT8_OK;
+}
+
+// The GEMM route's workspace: present, aligned, and at least the standard size.
+llmint8_status validate_workspace(int64_t T, int64_t K, int64_t N, void* workspace,
+                                  size_t workspace_bytes) {
+  if (!workspace || !aligned(workspace, kWsAlign)) return LLMINT8_ERR_INVALID_ARG;
+  if (workspace_bytes < gemm_workspace_bytes(T, K, N)) return LLMINT8_ERR_WORKSPACE;
   return LLMINT8_OK;
 }
 
 LinearArgs make_args(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sW,
-                     int64_t N, float threshold, void* Y, void* workspace, int dtype,
-                     const void* bias) {
-  const WsLayout L = ws_layout(T, K, N);
-  char* ws = static_cast<char*>(workspace);
+                     int64_t N, float threshold, void* Y, void* workspace, size_t workspace_bytes,
+                     int dtype, const void* bias) {
   LinearArgs a{};
   a.X = static_cast<const uint16_t*>(X);
   a.Wq = Wq;
@@ -84,6 +82,9 @@ LinearArgs make_args(const void* X, int64_t T, int64_t K, const int8_t* Wq, cons
   a.thr = threshold;
   a.bf16 = dtype == LLMINT8_DTYPE_BF16 ? 1 : 0;
   a.bias = static_cast<const uint16_t*>(bias);
+  if (!workspace) return a;  // the fused decode route
+  const WsLayout L = ws_layout_for(T, K, N, workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
   a.parts = reinterpret_cast<uint32_t*>(ws + L.parts);
   a.bitmap = reinterpret_cast<uint32_t*>(ws + L.bitmap);
   a.count = reinterpret_cast<int32_t*>(ws + L.count);
@@ -92,6 +93,7 @@ LinearArgs make_args(const void* X, int64_t T, int64_t K, const int8_t* Wq, cons
   a.Xq = reinterpret_cast<int8_t*>(ws + L.Xq);
   a.Xo = reinterpret_cast<uint16_t*>(ws + L.Xo);
   a.Wd = reinterpret_cast<uint16_t*>(ws + L.Wd);
+  a.wchunks = L.chunks;
   return a;
 }
 
@@ -129,9 +131,16 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   const int nk = route == LLMINT8_PATH_GEMV ? 1 : 3;
   if (events && n_events < nk + 1) return LLMINT8_ERR_INVALID_ARG;
   if (T == 0) return LLMINT8_OK;
+  // the fused decode kernel keeps everything in LDS: no workspace
+  if (route == LLMINT8_PATH_GEMM) {
+    st = validate_workspace(T, K, N, workspace, workspace_bytes);
+    if (st != LLMINT8_OK) return st;
+  }
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  LinearArgs a = make_args(X, T, K, Wq, sW, N, threshold, Y, workspace, dtype, bias);
+  LinearArgs a = route == LLMINT8_PATH_GEMM
+                     ? make_args(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes, dtype, bias)
+                     : make_args(X, T, K, Wq, sW, N, threshold, Y, nullptr, 0, dtype, bias);
   a.dbg_C = dbg_C;
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
@@ -151,7 +160,7 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
     if (kernels_launched) *kernels_launched = 1;
     return LLMINT8_OK;
   }
-  const int groups = scan_row_groups((int)T, (int)K, cus);
+  const int groups = scan_row_groups((int)T);
   e = launch_scan(a, groups, stream);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_prepare(a, groups, cus, stream);
@@ -174,14 +183,9 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   return hip_status(e);
 }
 
-llmint8_status check_backward_sizes(int64_t T, int64_t K, int64_t N) {
-  llmint8_status st = check_sizes(T, K, N);
-  if (st != LLMINT8_OK) return st;
-  // WdT and dY rows (2N bytes) are copied in whole 16-byte pieces, and a tile's
-  // rows x 2N bytes must stay within 32-bit buffer offsets
-  if (N % 8 != 0 || N > kMaxK) return LLMINT8_ERR_UNSUPPORTED;
-  return LLMINT8_OK;
-}
+// WdT and dY rows (2N bytes) are copied in whole 16-byte pieces, and a tile's
+// rows x 2N bytes must stay within one buffer window
+llmint8_status check_backward_sizes(int64_t T, int64_t K, int64_t N) { return admit_backward(T, K, N); }
 
 size_t backward_workspace(int64_t K, int64_t N) { return align_up((size_t)2 * N * K, kWsAlign); }
 
@@ -245,9 +249,17 @@ llmint8_status llmint8_quantize_weight(const void* W, int64_t N, int64_t K, int8
   return llmint8_quantize_weight_ex(W, LLMINT8_DTYPE_F16, N, K, Wq, sW, stream);
 }
 
-size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+size_t llmint8_workspace_bytes_path(int64_t T, int64_t K, int64_t N, int path) {
   if (check_sizes(T, K, N) != LLMINT8_OK) return 0;
-  return ws_layout(T, K, N).total;
+  if (path != LLMINT8_PATH_AUTO && path != LLMINT8_PATH_GEMM && path != LLMINT8_PATH_GEMV &&
+      forced_tile(path) < 0)
+    return 0;
+  if (T == 0 || choose_path(path, T, K) == LLMINT8_PATH_GEMV) return 0;
+  return gemm_workspace_bytes(T, K, N);
+}
+
+size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+  return llmint8_workspace_bytes_path(T, K, N, LLMINT8_PATH_AUTO);
 }
 
 llmint8_status llmint8_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
@@ -371,10 +383,7 @@ llmint8_status llmint8_linear_backward_input_timed(const void* dY, int64_t T, in
 static llmint8_status check_blockwise(int dtype, int64_t n, int64_t block) {
   // the codec takes fp16 or fp32 tensors
   if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_F32) return LLMINT8_ERR_INVALID_ARG;
-  if (n < 0 || block <= 0) return LLMINT8_ERR_INVALID_ARG;
-  if (block > 4096 || !blockwise_supported((int)block) || n % 16 != 0 || n > (int64_t)1 << 30)
-    return LLMINT8_ERR_UNSUPPORTED;
-  return LLMINT8_OK;
+  return admit_blockwise(n, block);
 }
 
 llmint8_status llmint8_quantize_blockwise(const void* x, int dtype, int64_t n, int64_t block,
@@ -404,10 +413,7 @@ llmint8_status llmint8_dequantize_blockwise(const int8_t* q, const float* absmax
 static llmint8_status check_4bit(int dtype, int quant_type, int64_t n, int64_t block) {
   if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_BF16) return LLMINT8_ERR_INVALID_ARG;
   if (quant_type != LLMINT8_QUANT_NF4 && quant_type != LLMINT8_QUANT_FP4) return LLMINT8_ERR_INVALID_ARG;
-  if (n < 0 || block <= 0) return LLMINT8_ERR_INVALID_ARG;
-  if (block > 4096 || !blockwise_supported((int)block) || n % 16 != 0 || (double)n >= kTwo31)
-    return LLMINT8_ERR_UNSUPPORTED;
-  return LLMINT8_OK;
+  return admit_4bit(n, block);
 }
 
 llmint8_status llmint8_code_book_4bit(int quant_type, float* values) {
@@ -454,8 +460,8 @@ llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t T, int64_t 
   if (T < 0 || K <= 0 || N <= 0) return LLMINT8_ERR_INVALID_ARG;
   llmint8_status st = check_4bit(dtype, quant_type, 0, block);
   if (st != LLMINT8_OK) return st;
-  if (K % 128 != 0 || (double)N * (double)K >= kTwo31 || (double)T * (double)K >= kTwo31)
-    return LLMINT8_ERR_UNSUPPORTED;
+  st = admit_linear_4bit(T, K, N);
+  if (st != LLMINT8_OK) return st;
   if (T == 0) return LLMINT8_OK;
   if (!X || !packed || !absmax || !Y) return LLMINT8_ERR_INVALID_ARG;
   if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(Y, 2) ||
@@ -482,11 +488,6 @@ llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t T, int64_t 
 int llmint8_gemm_tile(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0) return LLMINT8_ERR_INVALID_ARG;
   return LLMINT8_PATH_GEMM_256x256 + choose_gemm_tile(T, N, device_cu_count());
-}
-
-llmint8_status llmint8_probe_mfma_i8(int blocks, int iters, int32_t* out, void* stream) {
-  if (blocks <= 0 || iters <= 0 || !out || !aligned(out, 4)) return LLMINT8_ERR_INVALID_ARG;
-  return hip_status(launch_probe_mfma_i8(blocks, iters, out, static_cast<hipStream_t>(stream)));
 }
 
 int llmint8_gemv_max_rows(int64_t K) {

@@ -11,8 +11,9 @@
 // HBM-bound. Quantization: a wavefront covers 64 / LPB blocks at a time with
 // LPB lanes per block and VPL 16-byte vectors per lane kept in registers: one
 // pass over the data, a segmented lane reduction of the block maximum, the
-// codes written as 8- or 4-byte pieces. Reads use buffer loads, so a ragged
-// last block reads zeros past the end without a branch. Dequantization is a
+// codes written as 8- or 4-byte pieces. Reads use buffer loads over a window
+// that ends with the tensor, so a ragged last block reads zeros past the end
+// without a branch. Dequantization is a
 // flat grid-stride loop over output vectors.
 #include "device_util.h"
 #include "internal.h"
@@ -44,20 +45,24 @@ __global__ __launch_bounds__(256) void kq_blockwise(const void* __restrict__ x, 
   constexpr int E = F32 ? 4 : 8;  // elements per 16-byte vector
   constexpr int VPB = LPB * VPL;  // vectors per block
   constexpr int BPI = 64 / LPB;   // blocks per wavefront iteration
+  static_assert(BPI * VPB * 16 == 1024 * VPL, "an iteration's window is codec_window_bytes(VPL)");
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPB, li = lane % LPB;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)n * (F32 ? 4 : 2)));
   const int nvec = n / E;
   for (int b0 = wave * BPI; b0 < nb; b0 += nwaves * BPI) {
     const int b = b0 + sub;
+    // one window per iteration: the BPI blocks from b0, cut at the end of the
+    // tensor (codec_window_bytes(VPL) bytes at most); vectors past it read as zero
+    const int v0 = b0 * VPB;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(
+        static_cast<const char*>(x) + (size_t)v0 * 16u, (uint32_t)min(BPI * VPB, nvec - v0) * 16u);
     uint4 v[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int vi = b * VPB + i * LPB + li;
-      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rx, vi < nvec ? (uint32_t)vi * 16u : kOobOffset, 0, 0));
+      const int vl = sub * VPB + i * LPB + li;  // vector within the window
+      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)vl * 16u, 0, 0));
     }
     uint32_t m = 0;
 #pragma unroll
@@ -143,11 +148,6 @@ int codec_grid(int nb, int blocks_per_wave_iter, int num_cus) {
   return max(1, min(wgs, num_cus * 16));
 }
 }  // namespace
-
-bool blockwise_supported(int block) {
-  const int l = log2_exact(block);
-  return l >= 6 && l <= 12;
-}
 
 #define LLMINT8_BW_CASES(F32, E)                                                           \
   switch (block) {                                                                         \

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ranges.h"
+
 namespace llmint8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -15,8 +17,6 @@ typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 // Buffer resource word 3 for raw (untyped) buffers on gfx9-family parts.
 constexpr int kRsrcWord3 = 0x00020000;
-// A buffer offset that is always out of range: loads from it return zero.
-constexpr uint32_t kOobOffset = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,

@@ -1,8 +1,8 @@
 // 4-bit weights on gfx950: NF4 / FP4 code books, blockwise 4-bit quantization
 // and dequantization, and the decode-shaped linear layer that dequantizes the
-// weight on the fly ("bitsandbytes: GPU-Accelerated Inference and Training at
-// Lower Bit Depths", introduction: FP4 and NF4 data types, blockwise scaling
-// factors, 16-bit compute with the weights dequantized per operation;
+// weight on the fly ("bitsandbytes" glossary, "What it provides": FP4 and NF4
+// data types, blockwise scaling factors, 16-bit compute with the weights
+// dequantized per operation;
 // "Hugging Face Quantization with bitsandbytes ...", section 4: NF4 is fitted to
 // normally distributed weights, FP4 is a generic 4-bit float).
 //
@@ -127,20 +127,23 @@ __global__ __launch_bounds__(256) void kq4_blockwise(const uint16_t* __restrict_
   using A16 = Act16<BF16>;
   constexpr int VPB = LPB * VPL;
   constexpr int BPI = 64 / LPB;
+  static_assert(BPI * VPB * 16 == 1024 * VPL, "an iteration's window is codec_window_bytes(VPL)");
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPB, li = lane % LPB;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((size_t)n * 2));
   const int nvec = n / 8;
   for (int b0 = wave * BPI; b0 < nb; b0 += nwaves * BPI) {
     const int b = b0 + sub;
+    // one window per iteration, cut at the end of the weight (vectors past it read as zero)
+    const int v0 = b0 * VPB;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(w + (size_t)v0 * 8u, (uint32_t)min(BPI * VPB, nvec - v0) * 16u);
     uint4 v[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int vi = b * VPB + i * LPB + li;
-      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rw, vi < nvec ? (uint32_t)vi * 16u : kOobOffset, 0, 0));
+      const int vl = sub * VPB + i * LPB + li;
+      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)vl * 16u, 0, 0));
     }
     uint32_t m = 0;
 #pragma unroll
@@ -282,14 +285,16 @@ __global__ __launch_bounds__(kN4Waves * 64) void kn_gemv(FourBitArgs a, Code4 bo
   const uint32_t nblocks = (uint32_t)(((size_t)a.N * K + (1u << a.block_shift) - 1) >> a.block_shift);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W4, (uint32_t)a.N * row_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.absmax, nblocks * 4u);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (uint32_t)a.T * (uint32_t)K * 2u);
+  // X: the workgroup's 16 rows only (linear4_x_window_bytes <= 2^31 for K <= kLinear4MaxK)
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(a.X + (size_t)t0 * K, (uint32_t)min(16, a.T - t0) * (uint32_t)K * 2u);
   const int n = n0 + r, t = t0 + r;
   const bool wvalid = n < a.N, xvalid = t < a.T;
   // lane (r, g) of step s holds row n's codes for columns 128 s + 32 g + [0, 32)
   // (word j: columns + 8 j + [0, 8), the k-slice of MFMA j) and row t's X there
   const uint32_t wbase = (uint32_t)n * row_bytes + 16u * g;
   const uint32_t ebase = (uint32_t)n * (uint32_t)K + 32u * g;
-  const uint32_t xbase = ((uint32_t)t * (uint32_t)K + 32u * g) * 2u;
+  const uint32_t xbase = ((uint32_t)r * (uint32_t)K + 32u * g) * 2u;
   const int steps = K / 128;
   const int per = (steps + kN4Waves - 1) / kN4Waves;
   const int s0 = min(steps, wave * per), s1 = min(steps, s0 + per);

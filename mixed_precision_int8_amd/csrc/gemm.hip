@@ -28,13 +28,35 @@
 
 namespace llmint8 {
 
+// 16-bit outlier operands of outliers j0 .. j0+7 (zero past |O|) for a chunk
+// the workspace does not hold: formed from Wq and X exactly as the prepare
+// kernel forms Wd and Xo, Wd[n,j] = r16(fl32(fl32(Wq[n,idx_j] * b_n) / 127)).
+template <bool BF16>
+__device__ __forceinline__ uint4 outlier_w8(const LinearArgs& a, int n, int j0, int count) {
+  const float b = a.sW[n];
+  const int8_t* wr = a.Wq + (size_t)n * a.K;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    v[e] = j0 + e < count ? Act16<BF16>::from_f32(((float)wr[a.idx[j0 + e]] * b) / 127.0f) : 0u;
+  return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+}
+__device__ __forceinline__ uint4 outlier_x8(const LinearArgs& a, int t, int j0, int count) {
+  const uint16_t* xr = a.X + (size_t)t * a.K;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = j0 + e < count ? (uint32_t)xr[a.idx[j0 + e]] : 0u;
+  return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+}
+
 // Epilogue of one wavefront: its FNW x FT accumulator blocks, weight rows
 // nw0.. and activation rows tw0.. of the output. sW_w / aX_w / bias_w point at
 // the wavefront's first entries of the tile's scales and bias in LDS (bias_w
 // null without bias). `wf(i, h)` / `xf(j, h)` give the 16-bit operands of the
 // first chunk of 32 outlier columns (k-step h of block i / j); later chunks
-// are read from memory here. Output layout of a 32x32 block: lane holds, for
-// column (t) lane&31, rows (n) 8*q + 4*(lane>>5) + r in register 4*q + r.
+// are read from the workspace here, or formed from Wq and X past the chunks
+// it holds. Output layout of a 32x32 block: lane holds, for column (t)
+// lane&31, rows (n) 8*q + 4*(lane>>5) + r in register 4*q + r.
 //
 // Y is written one of two ways. Directly, each lane stores its 4-value pieces
 // (16 contiguous bytes of an output row per instruction). Or, when `stage`
@@ -44,10 +66,11 @@ namespace llmint8 {
 template <bool BF16, int FNW, int FT, class WF, class XF>
 __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&acc)[FNW][FT], int nw0,
                                               int tw0, const float* sW_w, const float* aX_w,
-                                              const uint16_t* bias_w, int nch, int lane, WF&& wf,
+                                              const uint16_t* bias_w, int count, int lane, WF&& wf,
                                               XF&& xf, char* stage = nullptr) {
   using A16 = Act16<BF16>;
   const int N = a.N, T = a.T;
+  const int nch = (count + kOutChunk - 1) / kOutChunk;
   const int fi = lane & 31, fg = lane >> 5;
   const int nl = nw0 + 4 * fg;  // + i*32 + 8*q + r
   const int tl = tw0 + fi;      // + j*32
@@ -95,15 +118,22 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
     for (int c = 1; c < nch; ++c) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint4 w = *reinterpret_cast<const uint4*>(
-            a.Wd + ((size_t)c * N + nrow) * kOutChunk + h * 16 + fg * 8);
+        uint4 w, x[FT];
+        if (c < a.wchunks) {  // uniform
+          w = *reinterpret_cast<const uint4*>(a.Wd + ((size_t)c * N + nrow) * kOutChunk + h * 16 + fg * 8);
 #pragma unroll
-        for (int j = 0; j < FT; ++j) {
-          const int t = min(tl + j * 32, T - 1);
-          const uint4 x = *reinterpret_cast<const uint4*>(
-              a.Xo + ((size_t)c * T + t) * kOutChunk + h * 16 + fg * 8);
-          y[j] = A16::mma32(w, x, y[j]);
+          for (int j = 0; j < FT; ++j) {
+            const int t = min(tl + j * 32, T - 1);
+            x[j] = *reinterpret_cast<const uint4*>(a.Xo + ((size_t)c * T + t) * kOutChunk + h * 16 + fg * 8);
+          }
+        } else {
+          const int j0 = c * kOutChunk + h * 16 + fg * 8;
+          w = outlier_w8<BF16>(a, nrow, j0, count);
+#pragma unroll
+          for (int j = 0; j < FT; ++j) x[j] = outlier_x8(a, min(tl + j * 32, T - 1), j0, count);
         }
+#pragma unroll
+        for (int j = 0; j < FT; ++j) y[j] = A16::mma32(w, x[j], y[j]);
       }
     }
     if (bias_w) {
@@ -231,7 +261,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
   const bool staged = kCanStage && rows_n == G::BN && rows_t == G::BT && (N & 7) == 0;
   gemm_epilogue<BF16, G::FN, G::FT>(
       a, acc, nw0, tw0, sW_l + wn * G::WN, aX_l + wt * G::WT, a.bias ? bias_l + wn * G::WN : nullptr,
-      nch, lane, [&](int i, int h) { return wf0[i][h]; }, [&](int j, int h) { return xf0[j][h]; },
+      count, lane, [&](int i, int h) { return wf0[i][h]; }, [&](int j, int h) { return xf0[j][h]; },
       staged ? smem + wave * kStageBytes : nullptr);
 }
 
@@ -290,7 +320,7 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
   const bool staged = rows_n == G::BN && rows_t == G::BT && (a.N & 7) == 0;
   char* last_slot = epi == smem ? smem + G::STAGE : smem;  // the last stage's slot, free now
   gemm_epilogue<BF16, FNW, G::FT>(
-      a, acc, n0 + wrow, t0 + wcol, sW_l + wrow, aX_l + wcol, a.bias ? bias_l + wrow : nullptr, nch,
+      a, acc, n0 + wrow, t0 + wcol, sW_l + wrow, aX_l + wcol, a.bias ? bias_l + wrow : nullptr, count,
       lane,
       [&](int i, int h) {
         const int r = wrow + i * 32 + fi;

@@ -6,35 +6,42 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
+#include "ranges.h"
+
 namespace llmint8 {
 
-constexpr int kMaxK = 65536;        // bitmap prefix tables live in LDS
-constexpr int kScanMaxGroups = 8;   // row groups of the column scan (partial bitmaps)
 constexpr int kOutChunk = 32;       // outlier columns per fp16 MFMA k-step
+constexpr int kWsChunks = 16;       // outlier chunks a standard workspace materializes (512 columns)
 constexpr size_t kWsAlign = 256;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workspace regions (byte offsets from the workspace base), worst case |O| = K.
+// Workspace regions of the GEMM route (byte offsets from the workspace base).
 //   parts  uint32 [kScanMaxGroups][KW]      per-row-group column bitmaps
 //   bitmap uint32 [KW]                      final outlier bitmap
 //   count  int32  [1]                       |O|
 //   idx    int32  [K]                       ascending outlier columns
 //   aX     fp32   [T]                       row statistic
 //   Xq     int8   [T, K]                    quantized activations
-//   Xo     16-bit [KC][T][32]               outlier activations, chunk-major, zero padded
-//   Wd     16-bit [KC][N][32]               dequantized outlier weight columns, same layout
-// (16-bit: the activation type, fp16 or bf16)
-// with KW = ceil(K/32) words and KC = ceil(K/32) chunks of 32 outlier columns.
+//   Xo     16-bit [chunks][T][32]           outlier activations, chunk-major, zero padded
+//   Wd     16-bit [chunks][N][32]           dequantized outlier weight columns, same layout
+// (16-bit: the activation type, fp16 or bf16) with KW = ceil(K/32) words. Xo
+// and Wd hold the first `chunks` chunks of 32 outlier columns; the epilogue
+// forms any chunk past them from X and Wq directly (same values, fewer reuse).
+// The fixed part (up to Xq) does not depend on the data; a workspace of
+// gemm_workspace_bytes(T, K, N) materializes min(ceil(K/32), kWsChunks) chunks,
+// and a larger one as many more as fit.
 struct WsLayout {
   size_t parts, bitmap, count, idx, aX, Xq, Xo, Wd, total;
+  int chunks;
 };
 
-inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N) {
+inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N, int64_t chunks) {
   WsLayout L;
   const int64_t KW = ceil_div(K, 32);
-  const int64_t KC = ceil_div(K, kOutChunk);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -47,10 +54,30 @@ inline WsLayout ws_layout(int64_t T, int64_t K, int64_t N) {
   L.idx = take(sizeof(int32_t) * K);
   L.aX = take(sizeof(float) * (T > 0 ? T : 1));
   L.Xq = take((size_t)T * K);
-  L.Xo = take(sizeof(uint16_t) * KC * kOutChunk * (size_t)T);
-  L.Wd = take(sizeof(uint16_t) * KC * kOutChunk * (size_t)N);
+  L.Xo = take(sizeof(uint16_t) * chunks * kOutChunk * (size_t)T);
+  L.Wd = take(sizeof(uint16_t) * chunks * kOutChunk * (size_t)N);
   L.total = off;
+  L.chunks = (int)chunks;
   return L;
+}
+
+// bytes of one materialized chunk (Xo and Wd, each region rounded up)
+inline size_t ws_chunk_bytes(int64_t T, int64_t N) { return 2 * kOutChunk * (size_t)(T + N); }
+// the standard GEMM workspace: min(ceil(K/32), kWsChunks) chunks
+inline size_t gemm_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+  return ws_layout(T, K, N, std::min<int64_t>(ceil_div(K, kOutChunk), kWsChunks)).total;
+}
+// the layout of a workspace of `bytes` (>= the fixed part plus one chunk): as
+// many chunks as fit, up to ceil(K/32); chunks = 0 when not even one fits
+inline WsLayout ws_layout_for(int64_t T, int64_t K, int64_t N, size_t bytes) {
+  const int64_t KC = ceil_div(K, kOutChunk);
+  int64_t lo = 0, hi = KC;  // largest chunk count whose layout fits
+  if (ws_layout(T, K, N, 0).total > bytes) return ws_layout(T, K, N, 0);
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (ws_layout(T, K, N, mid).total <= bytes) lo = mid; else hi = mid - 1;
+  }
+  return ws_layout(T, K, N, lo);
 }
 
 // Pointers into a workspace, plus optional debug destinations.
@@ -72,6 +99,7 @@ struct LinearArgs {
   int8_t* Xq;
   uint16_t* Xo;
   uint16_t* Wd;
+  int wchunks;  // outlier chunks held in Xo / Wd (>= 1); later chunks are formed in the epilogue
   // debug outputs (nullable)
   uint32_t* dbg_bitmap;
   int32_t* dbg_idx;
@@ -94,7 +122,6 @@ struct BwdArgs {
 // Launchers (each enqueues exactly one kernel on `stream`).
 hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW, bool bf16,
                                   hipStream_t stream);
-int scan_row_groups(int T, int K, int num_cus);
 uint32_t threshold_code(float thr, bool bf16);  // smallest 16-bit |x| code whose value reaches thr
 hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream);
 hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStream_t stream);
@@ -103,14 +130,12 @@ hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStrea
 constexpr int kGemmTiles = 5;
 int choose_gemm_tile(int64_t T, int64_t N, int num_cus);  // host: the cost model's candidate
 hipError_t launch_gemm(const LinearArgs& a, int num_cus, hipStream_t stream, int tile = -1);
-hipError_t launch_probe_mfma_i8(int blocks, int iters, int32_t* out, hipStream_t stream);
 int gemv_max_rows(int K);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uint16_t* WdT,
                             bool bf16, hipStream_t stream);
 hipError_t launch_gemm_f16(const BwdArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_f16_variant(const BwdArgs& a, int variant, hipStream_t stream);
-bool blockwise_supported(int block);  // a power of two in [64, 4096]
 hipError_t launch_quantize_blockwise(const void* x, bool f32, int n, int block, int8_t* q,
                                      float* absmax, int num_cus, hipStream_t stream);
 hipError_t launch_dequantize_blockwise(const int8_t* q, const float* absmax, int n, int block,

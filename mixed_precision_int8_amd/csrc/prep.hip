@@ -79,19 +79,21 @@ __global__ __launch_bounds__(kScanThreads) void ka_scan(const uint16_t* __restri
   const int r = tid >> 3;
   const int col = blockIdx.x * 64 + c * 8;
   const int G = gridDim.y, g = blockIdx.y;
-  const int rows_per = (T + G - 1) / G;
+  const int rows_per = scan_rows_per_group(T, G);
   const int t0 = g * rows_per;
-  const int t1 = min(T, t0 + rows_per);
+  const int rows = min(T, t0 + rows_per) - t0;
   if (tid < 2) words[tid] = 0u;
   v2u16 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
-  if (col < K) {
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(X, (uint32_t)((size_t)T * K * 2));
-    for (int tb = t0 + r; tb < t1; tb += 64 * kScanLoads) {
+  if (col < K && rows > 0) {
+    // one window per row group, at most scan_window_bytes (< 2^31), so that
+    // kOobOffset lies past it
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + (size_t)t0 * K, (uint32_t)((size_t)rows * K * 2));
+    for (int tb = r; tb < rows; tb += 64 * kScanLoads) {
       uint4 v[kScanLoads];
 #pragma unroll
       for (int u = 0; u < kScanLoads; ++u) {  // rows past the group read as zero
         const int t = tb + 64 * u;
-        const uint32_t off = t < t1 ? (uint32_t)(((size_t)t * K + col) * 2) : kOobOffset;
+        const uint32_t off = t < rows ? (uint32_t)(((size_t)t * K + col) * 2) : kOobOffset;
         v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
       }
 #pragma unroll
@@ -118,13 +120,7 @@ __global__ __launch_bounds__(kScanThreads) void ka_scan(const uint16_t* __restri
   }
 }
 
-int scan_row_groups(int T, int K, int num_cus) {
-  (void)K;
-  (void)num_cus;
-  // one step of kScanLoads loads per thread covers 64 * kScanLoads rows
-  int g = (int)ceil_div(T, 64 * kScanLoads);
-  return g < 1 ? 1 : (g > kScanMaxGroups ? kScanMaxGroups : g);
-}
+static_assert(64 * kScanLoads == kScanRowsPerStep, "rows per scan step");
 
 uint32_t threshold_code(float thr, bool bf16) {
   // smallest 16-bit magnitude code h with value(h) >= thr; the infinity code
@@ -308,8 +304,9 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   }
   if (count == 0) return;
 
-  // one item = (row of Xo or Wd, group of 8 consecutive outliers)
-  const int ngrp = (count + kOutChunk - 1) / kOutChunk * (kOutChunk / 8);
+  // one item = (row of Xo or Wd, group of 8 consecutive outliers), for the
+  // chunks the workspace holds (the GEMM epilogue forms any later chunk itself)
+  const int ngrp = min((count + kOutChunk - 1) / kOutChunk, a.wchunks) * (kOutChunk / 8);
   const int items = (T + N) * ngrp;  // < 2^31: T, N < 2^31 / K and ngrp <= K / 8
   for (int it = gb * kPrepThreads + tid; it < items; it += ng * kPrepThreads) {
     const int row = it / ngrp;

@@ -8,12 +8,12 @@ code books on the host), and this file imports nothing from the product.
 
 Sources, by page title and section:
 
-* [HYS-4]  "bitsandbytes: GPU-Accelerated Inference and Training at Lower Bit
-           Depths", introduction: the 4-bit layer supports a generic 4-bit float
-           (FP4) and 4-bit NormalFloat (NF4), the latter fitted to the roughly
-           normal distribution of trained weights; weights are quantized in
-           blocks that each carry a scaling factor; the computation runs in a
-           16-bit type (FP16 or BF16) with the weights dequantized on the fly.
+* [DCT-4]  "bitsandbytes" (glossary), section "What it provides": the 4-bit
+           layer supports a generic 4-bit float (FP4) and 4-bit NormalFloat
+           (NF4), the latter fitted to the roughly normal distribution of
+           trained weights; weights are quantized in blocks that each carry a
+           scaling factor; the computation runs in a 16-bit type (FP16 or BF16)
+           with the weights dequantized on the fly.
 * [HFQ-4]  "Hugging Face Quantization with bitsandbytes ...", section 4
            "4-Bit Quantization: NF4, FP4, and Double Quantization": FP4 spreads
            its values like a generic float, NF4 puts them where normally
@@ -25,7 +25,9 @@ Sources, by page title and section:
 Readings where the pages leave a step open:
 
 * F1  code books (the pages give no values). NF4 follows the published
-      NormalFloat construction: eight positive levels at standard-normal
+      NormalFloat construction (Dettmers et al., "QLoRA: Efficient Finetuning
+      of Quantized LLMs", 2023, section 3, the technique the glossary page
+      names as the one built on the library): eight positive levels at standard-normal
       quantiles Phi^-1(p) for p = p_max + i * (0.5 - p_max) / 8, i = 0..7; seven
       negative levels at -Phi^-1(p) for p = p_max + i * (0.5 - p_max) / 7,
       i = 0..6; an exact zero; everything divided by Phi^-1(p_max), with

@@ -38,23 +38,33 @@ int main(void) {
   EXPECT(llmint8_quantize_weight_ex(p, 7, 16, 64, p, p, NULL) == INVALID);
 
   /* forward: validation and the T = 0 no-op */
-  const size_t need = llmint8_workspace_bytes(16, 1024, 1024);
-  EXPECT(need > 0);
-  EXPECT(llmint8_linear(NULL, 16, 1024, p, p, 1024, 6.0f, p, p, need, NULL) == INVALID);
-  EXPECT(llmint8_linear(p, 16, 1024, p, p, 1024, NAN, p, p, need, NULL) == INVALID);
-  EXPECT(llmint8_linear(p, 16, 1024, p, p, 1024, -1.0f, p, p, need, NULL) == INVALID);
-  EXPECT(llmint8_linear(p, 16, 1024, p, p, 1024, 6.0f, p, p, need - 256, NULL) == LLMINT8_ERR_WORKSPACE);
-  EXPECT(llmint8_linear(p, 16, 1000, p, p, 1024, 6.0f, p, p, need, NULL) == UNSUP);
+  EXPECT(llmint8_workspace_bytes(16, 1024, 1024) == 0); /* fused decode route: no workspace */
+  EXPECT(llmint8_workspace_bytes_path(16, 1024, 1024, LLMINT8_PATH_GEMV) == 0);
+  EXPECT(llmint8_workspace_bytes_path(16, 1024, 1024, LLMINT8_PATH_GEMM) > 16 * 1024);
+  EXPECT(llmint8_workspace_bytes_path(16, 1024, 1024, LLMINT8_PATH_GEMM) < llmint8_workspace_bytes(64, 1024, 1024));
+  EXPECT(llmint8_workspace_bytes_path(16, 1024, 1024, LLMINT8_PATH_GEMM_352x256) ==
+         llmint8_workspace_bytes_path(16, 1024, 1024, LLMINT8_PATH_GEMM));
+  EXPECT(llmint8_workspace_bytes_path(16, 1024, 1024, 3) == 0); /* unknown path */
+  const size_t need = llmint8_workspace_bytes(64, 1024, 1024);
+  EXPECT(need > 64 * 1024);
+  EXPECT(llmint8_linear(NULL, 64, 1024, p, p, 1024, 6.0f, p, p, need, NULL) == INVALID);
+  EXPECT(llmint8_linear(p, 64, 1024, p, p, 1024, NAN, p, p, need, NULL) == INVALID);
+  EXPECT(llmint8_linear(p, 64, 1024, p, p, 1024, -1.0f, p, p, need, NULL) == INVALID);
+  EXPECT(llmint8_linear(p, 64, 1024, p, p, 1024, 6.0f, p, p, need - 256, NULL) == LLMINT8_ERR_WORKSPACE);
+  EXPECT(llmint8_linear(p, 64, 1024, p, p, 1024, 6.0f, NULL, p, need, NULL) == INVALID);
+  EXPECT(llmint8_linear(p, 64, 1024, p, p, 1024, 6.0f, p, NULL, need, NULL) == INVALID);
+  EXPECT(llmint8_linear(p, 64, 1024, p, p, 1024, 6.0f, p, (char*)p + 16, need, NULL) == INVALID);
+  EXPECT(llmint8_linear(p, 64, 1000, p, p, 1024, 6.0f, p, p, need, NULL) == UNSUP);
   EXPECT(llmint8_linear(p, 0, 1024, p, p, 1024, 6.0f, p, p, need, NULL) == LLMINT8_OK);
-  EXPECT(llmint8_linear_ex(p, 9, 16, 1024, p, p, 1024, 6.0f, NULL, p, p, need, NULL) == INVALID);
-  EXPECT(llmint8_linear_ex(p, LLMINT8_DTYPE_BF16, 16, 1024, p, p, 1024, 6.0f, odd, p, p, need, NULL) ==
+  EXPECT(llmint8_linear_ex(p, 9, 64, 1024, p, p, 1024, 6.0f, NULL, p, p, need, NULL) == INVALID);
+  EXPECT(llmint8_linear_ex(p, LLMINT8_DTYPE_BF16, 64, 1024, p, p, 1024, 6.0f, odd, p, p, need, NULL) ==
          INVALID);
   for (int path = -1; path < 25; ++path) /* an unknown path, or else the misaligned Xq copy */
-    EXPECT(llmint8_linear_debug(p, 16, 1024, p, p, 1024, 6.0f, p, p, need, NULL, path, NULL, NULL, NULL,
+    EXPECT(llmint8_linear_debug(p, 64, 1024, p, p, 1024, 6.0f, p, p, need, NULL, path, NULL, NULL, NULL,
                                 mis, NULL, NULL) == INVALID);
   void* ev[4] = {p, p, p, p};
   int nk = -1;
-  EXPECT(llmint8_linear_timed(p, 16, 1024, p, p, 1024, 6.0f, p, p, need, NULL, LLMINT8_PATH_GEMM, ev, 2,
+  EXPECT(llmint8_linear_timed(p, 64, 1024, p, p, 1024, 6.0f, p, p, need, NULL, LLMINT8_PATH_GEMM, ev, 2,
                               &nk) == INVALID);
 
   /* workspace sizes grow with every dimension and cover the largest shapes */
@@ -62,6 +72,9 @@ int main(void) {
   EXPECT(llmint8_workspace_bytes(2048, 4096, 11008) < llmint8_workspace_bytes(2048, 8192, 11008));
   EXPECT(llmint8_workspace_bytes(2048, 4096, 11008) < llmint8_workspace_bytes(2048, 4096, 28672));
   EXPECT(llmint8_workspace_bytes(32767, 65536, 32767) > (size_t)32767 * 65536);
+  /* bounded: the int8 activations plus 512 outlier columns of 16-bit operands */
+  EXPECT(llmint8_workspace_bytes(2048, 4096, 11008) < (size_t)2048 * 4096 + (size_t)2 * 512 * (2048 + 11008) + (1 << 20));
+  EXPECT(llmint8_workspace_bytes(2048, 4096, 11008) > (size_t)2048 * 4096 + (size_t)2 * 512 * (2048 + 11008));
   EXPECT(llmint8_backward_workspace_bytes(2048, 4096, 11008) >= (size_t)2 * 4096 * 11008);
 
   /* backward, codecs, 4-bit */
@@ -74,7 +87,6 @@ int main(void) {
   EXPECT(llmint8_quantize_4bit(p, 0, 64, 64, 5, p, p, NULL) == INVALID);
   EXPECT(llmint8_linear_4bit(p, 0, 1, 100, p, p, 64, LLMINT8_QUANT_NF4, 8, NULL, p, NULL) == UNSUP);
   EXPECT(llmint8_linear_4bit(p, 0, 0, 128, p, p, 64, LLMINT8_QUANT_NF4, 8, NULL, p, NULL) == LLMINT8_OK);
-  EXPECT(llmint8_probe_mfma_i8(0, 1, p, NULL) == INVALID);
 
   /* 4-bit code books: 16 values in [-1, 1], both ends reached, repeatable */
   for (int q = 0; q < 2; ++q) {

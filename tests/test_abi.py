@@ -45,7 +45,9 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
-def _linear(lib, X=ALIGNED, T=16, K=1024, Wq=ALIGNED, sW=ALIGNED, N=1024, thr=6.0, Y=ALIGNED,
+# T = 64 takes the GEMM route (T > llmint8_gemv_max_rows(1024) = 16), which needs a
+# workspace; every call below fails validation, so nothing is ever launched
+def _linear(lib, X=ALIGNED, T=64, K=1024, Wq=ALIGNED, sW=ALIGNED, N=1024, thr=6.0, Y=ALIGNED,
             ws=ALIGNED, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = lib.llmint8_workspace_bytes(max(T, 0), K, N) if T >= 0 else 0
@@ -71,7 +73,7 @@ def test_linear_argument_errors(lib):
     assert _linear(lib, K=1000) == UNSUPPORTED                      # K % 16 != 0
     assert _linear(lib, K=65536 + 16) == UNSUPPORTED
     assert _linear(lib, N=1 << 20, K=4096) == UNSUPPORTED            # N*K >= 2^31
-    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    need = lib.llmint8_workspace_bytes(64, 1024, 1024)
     assert _linear(lib, ws_bytes=need - 1) == WORKSPACE
 
 
@@ -93,7 +95,7 @@ def test_quantize_weight_argument_errors(lib):
 
 
 def test_debug_and_timed_argument_errors(lib):
-    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    need = lib.llmint8_workspace_bytes_path(16, 1024, 1024, m8.LLMINT8_PATH_GEMM)
     d = lib.llmint8_linear_debug
     base = [ALIGNED, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, ALIGNED, ALIGNED, need, None]
     assert d(*base, 7, None, None, None, None, None, None) == INVALID        # unknown path
@@ -130,21 +132,26 @@ def test_gemm_tile_choice(lib):
     assert m8.llmint8_gemm_tile(2048, 11008) == "352x256"
 
 
-def test_probe_argument_errors(lib):
-    p = lib.llmint8_probe_mfma_i8
-    assert p(0, 10, ALIGNED, None) == INVALID
-    assert p(4, 0, ALIGNED, None) == INVALID
-    assert p(4, 10, None, None) == INVALID
-    assert p(4, 10, MISALIGNED, None) == INVALID
-
-
-def test_workspace_size_covers_worst_case(lib):
-    for T, K, N in [(1, 16, 1), (16, 1024, 1024), (2048, 4096, 11008), (4096, 8192, 28672)]:
+def test_workspace_size_is_route_aware_and_bounded(lib):
+    """The fused decode route needs no workspace; the GEMM route needs the int8
+    activations, small tables and the 16-bit operands of min(K, 512) outlier columns
+    (more outlier columns are formed in the epilogue), never the worst case |O| = K."""
+    for T, K, N in [(64, 16, 1), (17, 1024, 1024), (2048, 4096, 11008), (4096, 8192, 28672),
+                    (2048, 14336, 14336)]:
         ws = lib.llmint8_workspace_bytes(T, K, N)
-        kpad = (K + 31) // 32 * 32
-        # at least: Xq + aX + idx + outlier activations and weight columns for |O| = K
-        assert ws >= T * K + 4 * T + 4 * K + 2 * kpad * (T + N)
-        assert ws < T * K + 4 * T + 4 * K + 2 * kpad * (T + N) + 64 * 1024
+        cols = min((K + 31) // 32 * 32, 512)
+        assert ws >= T * K + 4 * T + 4 * K + 2 * cols * (T + N)
+        assert ws < T * K + 4 * T + 4 * K + 2 * cols * (T + N) + 64 * 1024
+        assert lib.llmint8_workspace_bytes_path(T, K, N, m8.LLMINT8_PATH_GEMM) == ws
+    for K in (1024, 4096, 8192):
+        r = lib.llmint8_gemv_max_rows(K)
+        assert lib.llmint8_workspace_bytes(r, K, 4096) == 0
+        assert lib.llmint8_workspace_bytes(r + 1, K, 4096) > 0
+        assert lib.llmint8_workspace_bytes_path(r, K, 4096, m8.LLMINT8_PATH_GEMM) > 0
+        assert lib.llmint8_workspace_bytes_path(r, K, 4096, m8.LLMINT8_PATH_GEMV) == 0
+        assert lib.llmint8_workspace_bytes_path(r, K, 4096, 3) == 0          # unknown path
+    # at the prefill shape: well under the int8 weight (the method's memory saving)
+    assert lib.llmint8_workspace_bytes(2048, 4096, 11008) < 4096 * 11008 // 2
     assert lib.llmint8_workspace_bytes(16, 1000, 16) == 0
     assert lib.llmint8_workspace_bytes(-1, 1024, 16) == 0
 
@@ -228,11 +235,11 @@ def test_blockwise_argument_errors(lib):
 
 def test_ex_entry_points_argument_errors(lib):
     F16, BF16, F32 = m8.LLMINT8_DTYPE_F16, m8.LLMINT8_DTYPE_BF16, m8.LLMINT8_DTYPE_F32
-    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    need = lib.llmint8_workspace_bytes(64, 1024, 1024)
     lx = lib.llmint8_linear_ex
 
-    def call(dtype=BF16, bias=None, X=ALIGNED, ws_bytes=need):
-        return lx(X, dtype, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, bias, ALIGNED, ALIGNED,
+    def call(dtype=BF16, bias=None, X=ALIGNED, ws_bytes=need):   # GEMM route (T = 64)
+        return lx(X, dtype, 64, 1024, ALIGNED, ALIGNED, 1024, 6.0, bias, ALIGNED, ALIGNED,
                   ws_bytes, None)
     assert call(dtype=F32) == INVALID                  # fp32 activations are not a forward type
     assert call(dtype=7) == INVALID
@@ -241,7 +248,7 @@ def test_ex_entry_points_argument_errors(lib):
     assert call(ws_bytes=need - 1) == WORKSPACE
     assert lx(None, F16, 0, 1024, ALIGNED, ALIGNED, 1024, 6.0, None, None, None, 0, None) == OK
     d = lib.llmint8_linear_debug_ex
-    base = [ALIGNED, BF16, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, ALIGNED, ALIGNED, ALIGNED, need,
+    base = [ALIGNED, BF16, 64, 1024, ALIGNED, ALIGNED, 1024, 6.0, ALIGNED, ALIGNED, ALIGNED, need,
             None]
     assert d(*base, 7, None, None, None, None, None, None) == INVALID
     assert d(*base, m8.LLMINT8_PATH_GEMM, None, None, None, MISALIGNED, None, None) == INVALID
@@ -296,11 +303,11 @@ def test_4bit_argument_errors(lib):
 
 
 def test_timed_ex_argument_errors(lib):
-    need = lib.llmint8_workspace_bytes(16, 1024, 1024)
+    need = lib.llmint8_workspace_bytes(64, 1024, 1024)
     t = lib.llmint8_linear_timed_ex
     ev = (ctypes.c_void_p * 4)(P, P, P, P)
     nk = ctypes.c_int(0)
-    base = [ALIGNED, m8.LLMINT8_DTYPE_BF16, 16, 1024, ALIGNED, ALIGNED, 1024, 6.0, None, ALIGNED,
+    base = [ALIGNED, m8.LLMINT8_DTYPE_BF16, 64, 1024, ALIGNED, ALIGNED, 1024, 6.0, None, ALIGNED,
             ALIGNED, need, None]
     assert t(*base, 0, None, 4, ctypes.byref(nk)) == INVALID
     assert t(*base, m8.LLMINT8_PATH_GEMM, ev, 2, ctypes.byref(nk)) == INVALID   # 3 kernels, 4 events

@@ -4,9 +4,9 @@ Bar: packed codes, block maxima and dequantized 16-bit weights bit-exact; Y of
 the 4-bit linear within the 16-bit output bar of ``parity_util`` (the kernel
 sums fp32 products in its own order, the oracle sums exactly).
 
-Sources (page title, section): "bitsandbytes: GPU-Accelerated Inference and
-Training at Lower Bit Depths", introduction (FP4 and NF4, blockwise scaling,
-16-bit compute with the weight dequantized per operation); "Hugging Face
+Sources (page title, section): "bitsandbytes" (glossary), "What it provides"
+(FP4 and NF4, blockwise scaling, 16-bit compute with the weight dequantized
+per operation); "Hugging Face
 Quantization with bitsandbytes ...", section 4.
 """
 from __future__ import annotations

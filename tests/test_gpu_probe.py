@@ -1,12 +1,12 @@
-"""The matrix-core rate probe (a measurement helper of the benchmark, not part of
-the method) runs through the C ABI and keeps its work: the checksums are
-deterministic and not all zero."""
+"""The benchmark's matrix-core rate probe (libllmint8_probe.so, a measurement
+helper built beside the product library, not part of it) keeps its work: the
+checksums are deterministic and not all zero."""
 from __future__ import annotations
 
 import pytest
 
 torch = pytest.importorskip("torch")
-import mixed_precision_int8_amd as m8  # noqa: E402
+import bench  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -15,10 +15,11 @@ def test_probe_runs_and_is_deterministic():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     print("[case] probe blocks=8 iters=50", flush=True)
+    stream = torch.cuda.current_stream()
     outs = []
     for _ in range(2):
         out = torch.zeros(8 * 256, dtype=torch.int32, device="cuda")
-        ops = m8.llmint8_probe_mfma_i8(8, 50, out)
+        ops = bench.probe_mfma_i8(8, 50, out, stream)
         torch.cuda.synchronize()
         outs.append(out.cpu())
     assert ops == 8 * 4 * 50 * 4 * 65536

@@ -273,3 +273,35 @@ def test_kernel_dequant_multiply_form_is_exact():
     div = (p / np.float32(127.0)).astype(np.float16)
     mul = (p * np.float32(1.0 / 127.0)).astype(np.float32).astype(np.float16)
     assert np.array_equal(div.view(np.uint16), mul.view(np.uint16))
+
+
+def _f32_to_bf16_bits_rne(x32):
+    """fp32 -> bf16 bit pattern, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_kernel_dequant_multiply_form_is_exact_bf16():
+    """bf16 compute type: for every positive finite bf16 scale and every code, rounding
+    fl32(fl32(q * b) * fl32(1/127)) to bf16 gives the bf16 rounding of the division."""
+    codes = np.arange(1, 0x7F80, dtype=np.uint32)
+    b = (codes << 16).view(np.float32)
+    q = np.arange(-127, 128, dtype=np.float32)
+    p = (q[None, :] * b[:, None]).astype(np.float32)      # exact: 8-bit times 8-bit significands
+    div = _f32_to_bf16_bits_rne((p / np.float32(127.0)).astype(np.float32))
+    mul = _f32_to_bf16_bits_rne((p * np.float32(1.0 / 127.0)).astype(np.float32))
+    assert np.array_equal(div, mul)
+
+
+def test_kernel_dequant_multiply_form_single_rounding_fp16():
+    """fp16 with the second product rounded to fp16 once (no fp32 rounding between, as a
+    fused mixed-precision multiply-add gives): still the fp16 rounding of the division,
+    for every positive fp16 scale and every code."""
+    codes = np.arange(1, 0x7C00, dtype=np.uint16)
+    b = codes.view(np.float16).astype(np.float32)
+    q = np.arange(-127, 128, dtype=np.float32)
+    p = (q[None, :] * b[:, None]).astype(np.float32)      # exact in fp32
+    div = (p / np.float32(127.0)).astype(np.float16)
+    # p (<= 19 significant bits) times fl32(1/127) (24 bits) is exact in binary64
+    once = (p.astype(np.float64) * np.float64(np.float32(1.0 / 127.0))).astype(np.float16)
+    assert np.array_equal(div.view(np.uint16), once.view(np.uint16))

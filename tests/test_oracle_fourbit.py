@@ -1,9 +1,9 @@
 """Pins for the oracle's 4-bit weight path (NF4 / FP4 code books, blockwise
 codes, dequantization, the decode-shaped linear).
 
-Sources (page title, section): "bitsandbytes: GPU-Accelerated Inference and
-Training at Lower Bit Depths", introduction (FP4 and NF4, blockwise scaling,
-16-bit compute with weights dequantized on the fly); "Hugging Face
+Sources (page title, section): "bitsandbytes" (glossary), "What it provides"
+(FP4 and NF4, blockwise scaling, 16-bit compute with weights dequantized on
+the fly); "Hugging Face
 Quantization with bitsandbytes ...", section 4 (NF4 fitted to normally
 distributed weights, FP4 a generic 4-bit float).
 

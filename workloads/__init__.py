@@ -171,3 +171,15 @@ def make(w: Workload, T: int | None = None, with_weight: bool = True):
 def random_fp16(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
     """Plain normal fp16 array (for edge-shape tests)."""
     return (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)).astype(np.float16)
+
+
+def random_fp16_large(rng: np.random.Generator, shape, scale: float = 1.0,
+                      chunk: int = 1 << 26) -> np.ndarray:
+    """Plain normal fp16 array drawn ``chunk`` elements at a time (inputs of several GB
+    without a float32 copy of the whole)."""
+    out = np.empty(shape, np.float16)
+    flat = out.reshape(-1)
+    for i in range(0, flat.size, chunk):
+        n = min(chunk, flat.size - i)
+        flat[i:i + n] = (rng.standard_normal(n, dtype=np.float32) * np.float32(scale)).astype(np.float16)
+    return out

@@ -262,7 +262,7 @@ def _workspace(T, K, N, device, workspace, path=LLMINT8_PATH_AUTO):
 
 
 def _ws_bytes(ws):
-    return 0 if ws is None else _ws_bytes(ws)
+    return 0 if ws is None else ws.numel() * ws.element_size()
 
 
 def _linear_args(X, Wq, sW, threshold, Y, workspace, dtype=None, bias=None, path=LLMINT8_PATH_AUTO):

@@ -367,6 +367,29 @@ LLMINT8_API llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t
                                                const void* bias, void* Y, void* stream);
 
 /*
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops): llmint8_linear_ex without a
+ * workspace argument, computing exactly what llmint8_linear_ex computes with
+ * the same kernels. Its scratch is a static device array inside the library,
+ * one per GPU, of llmint8_noalloc_scratch_bytes() bytes (64 MiB), held from
+ * the first call on that GPU until the process ends; the call allocates
+ * nothing. On the GEMM route it needs about T*K bytes plus 2*(T+N) bytes per
+ * 32 outlier columns it holds (one chunk at least); a call whose shapes need
+ * more returns LLMINT8_ERR_WORKSPACE before enqueuing anything. The fused
+ * decode route (T <= llmint8_gemv_max_rows(K)) uses no scratch. All calls on
+ * one GPU share its scratch: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give undefined results; calls in order on
+ * one stream are safe. Arguments and errors otherwise as for
+ * llmint8_linear_ex (HIP error of the one-time address lookup:
+ * LLMINT8_ERR_HIP).
+ */
+LLMINT8_API llmint8_status llmint8_linear_noalloc(const void* X, int dtype, int64_t T, int64_t K,
+                                                  const int8_t* Wq, const float* sW, int64_t N,
+                                                  float threshold, const void* bias, void* Y,
+                                                  void* stream);
+LLMINT8_API size_t llmint8_noalloc_scratch_bytes(void);
+
+/*
  * The GEMM tile the GEMM route picks for T rows and N output features on the
  * current device (its CU count; 256 when no device answers), as the
  * LLMINT8_PATH_GEMM_<tile> value that forces it; LLMINT8_ERR_INVALID_ARG for

@@ -25,7 +25,7 @@ __all__ = [
     "LLMINT8_QUANT_NF4", "LLMINT8_QUANT_FP4", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "Linear4bit", "llmint8_linear_timed_ex",
     "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
-    "llmint8_gemm_tile",
+    "llmint8_gemm_tile", "llmint8_linear_noalloc", "llmint8_noalloc_scratch_bytes",
 ]
 
 LLMINT8_PATH_AUTO = 0
@@ -50,7 +50,7 @@ EXPORTED_SYMBOLS = (
     "llmint8_linear_debug_ex", "llmint8_code_book_4bit", "llmint8_quantize_4bit",
     "llmint8_dequantize_4bit", "llmint8_linear_4bit", "llmint8_linear_timed_ex",
     "llmint8_linear_backward_input_ex", "llmint8_dequantize_weight_t_ex",
-    "llmint8_gemm_tile",
+    "llmint8_gemm_tile", "llmint8_linear_noalloc", "llmint8_noalloc_scratch_bytes",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -136,6 +136,11 @@ def load_library():
     lib.llmint8_linear_4bit.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64, ctypes.c_int,
                                         _i64, _vp, _vp, _vp]
     lib.llmint8_linear_4bit.restype = ctypes.c_int
+    lib.llmint8_linear_noalloc.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64,
+                                           ctypes.c_float, _vp, _vp, _vp]
+    lib.llmint8_linear_noalloc.restype = ctypes.c_int
+    lib.llmint8_noalloc_scratch_bytes.argtypes = []
+    lib.llmint8_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.llmint8_gemm_tile.argtypes = [_i64, _i64]
     lib.llmint8_gemm_tile.restype = ctypes.c_int
     lib.llmint8_gemv_max_rows.argtypes = [_i64]
@@ -307,6 +312,33 @@ def llmint8_linear_ex(X, Wq, sW, threshold: float = 6.0, bias=None, Y=None, work
                                  _stream(stream, X.device)),
            "llmint8_linear_ex")
     return Y
+
+
+def llmint8_linear_noalloc(X, Wq, sW, threshold: float = 6.0, bias=None, Y=None, stream=None):
+    """llmint8_linear_ex on the library's static scratch: no workspace and no allocation
+    inside the call (pass ``Y`` to allocate nothing at all). For callers that cannot
+    allocate; calls that overlap in time on one GPU race on the shared scratch."""
+    import torch
+    lib = load_library()
+    code = _act_dtype(X.dtype)
+    T, K = X.shape
+    N = Wq.shape[0]
+    _need(X, X.dtype, (T, K), "X")
+    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(sW, torch.float32, (N,), "sW")
+    if bias is not None:
+        _need(bias, X.dtype, (N,), "bias")
+    if Y is None:
+        Y = torch.empty((T, N), dtype=X.dtype, device=X.device)
+    _need(Y, X.dtype, (T, N), "Y")
+    _check(lib.llmint8_linear_noalloc(_ptr(X), code, T, K, _ptr(Wq), _ptr(sW), N, float(threshold),
+                                      _ptr(bias), _ptr(Y), _stream(stream, X.device)),
+           "llmint8_linear_noalloc")
+    return Y
+
+
+def llmint8_noalloc_scratch_bytes() -> int:
+    return int(load_library().llmint8_noalloc_scratch_bytes())
 
 
 def llmint8_linear_timed_ex(X, Wq, sW, threshold, Y, workspace, events, bias=None,

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libllmint8.so")
 
-SOURCES = ["prep.hip", "gemm.hip", "gemv.hip", "bwd.hip", "blockwise.hip", "fourbit.hip", "api.cpp"]
+SOURCES = ["prep.hip", "gemm.hip", "gemv.hip", "bwd.hip", "blockwise.hip", "fourbit.hip", "noalloc.hip",
+           "api.cpp"]
 # the benchmark's matrix-core rate probe: a library of its own, not part of libllmint8
 PROBE_SRC = os.path.join(HERE, "bench_probe", "probe.hip")
 PROBE_LIB = os.path.join(HERE, "libllmint8_probe.so")

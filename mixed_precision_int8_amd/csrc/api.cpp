@@ -118,7 +118,8 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
                           uint32_t* dbg_bitmap, int32_t* dbg_idx, int32_t* dbg_count,
                           int8_t* dbg_Xq, float* dbg_aX, int32_t* dbg_C,
                           void* const* events, int n_events, int* kernels_launched,
-                          int dtype = LLMINT8_DTYPE_F16, const void* bias = nullptr) {
+                          int dtype = LLMINT8_DTYPE_F16, const void* bias = nullptr,
+                          ScratchSource scratch = nullptr) {
   if (kernels_launched) *kernels_launched = 0;
   llmint8_status st = validate_linear(X, T, K, Wq, sW, N, threshold, Y, workspace, workspace_bytes,
                                       dtype, bias);
@@ -133,8 +134,15 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   if (T == 0) return LLMINT8_OK;
   // the fused decode kernel keeps everything in LDS: no workspace
   if (route == LLMINT8_PATH_GEMM) {
-    st = validate_workspace(T, K, N, workspace, workspace_bytes);
-    if (st != LLMINT8_OK) return st;
+    if (scratch) {
+      // the library's static scratch: the fixed part and one outlier chunk must fit
+      if (ws_layout(T, K, N, 1).total > workspace_bytes) return LLMINT8_ERR_WORKSPACE;
+      const hipError_t se = scratch(&workspace);
+      if (se != hipSuccess) return hip_status(se);
+    } else {
+      st = validate_workspace(T, K, N, workspace, workspace_bytes);
+      if (st != LLMINT8_OK) return st;
+    }
   }
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
@@ -230,6 +238,16 @@ llmint8_status run_backward_input(const void* dY, int64_t T, int64_t K, const in
 }
 
 }  // namespace
+
+namespace llmint8 {
+llmint8_status linear_static_scratch(const void* X, int dtype, int64_t T, int64_t K, const int8_t* Wq,
+                                     const float* sW, int64_t N, float threshold, const void* bias,
+                                     void* Y, ScratchSource scratch, size_t scratch_bytes, void* stream) {
+  return run_linear(X, T, K, Wq, sW, N, threshold, Y, nullptr, scratch_bytes, stream, LLMINT8_PATH_AUTO,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr, dtype,
+                    bias, scratch);
+}
+}  // namespace llmint8
 
 extern "C" {
 

@@ -119,6 +119,15 @@ struct BwdArgs {
   int bf16;            // 16-bit type: 0 fp16, 1 bf16
 };
 
+// The forward on the library's static scratch (no workspace argument): after
+// every argument check passes on the GEMM route, `scratch` gives the current
+// device's scratch address; the fixed part of the layout and one outlier chunk
+// must fit in scratch_bytes (LLMINT8_ERR_WORKSPACE otherwise).
+typedef hipError_t (*ScratchSource)(void** address);
+int linear_static_scratch(const void* X, int dtype, int64_t T, int64_t K, const int8_t* Wq,
+                          const float* sW, int64_t N, float threshold, const void* bias, void* Y,
+                          ScratchSource scratch, size_t scratch_bytes, void* stream);
+
 // Launchers (each enqueues exactly one kernel on `stream`).
 hipError_t launch_quantize_weight(const uint16_t* W, int N, int K, int8_t* Wq, float* sW, bool bf16,
                                   hipStream_t stream);

@@ -68,6 +68,10 @@ def parse():
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 + bias workload")
     p.add_argument("--no-fourbit", action="store_true", help="skip the 4-bit weight workload")
     p.add_argument("--no-probe", action="store_true", help="skip the matrix-core rate probe")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the tiny, large and outlier-sweep workloads")
+    p.add_argument("--config-steps", type=int, default=20,
+                   help="timed calls per tiny / large / sweep point")
     p.add_argument("--decode-copies", type=int, default=24,
                    help="distinct weight copies cycled in the decode timing (> last-level cache)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -152,6 +156,130 @@ def graph_us_per_call(fn, n_calls, replays, stream):
     us = e0.elapsed_time(e1) / (replays * n_calls) * 1e3
     del g
     return us
+
+
+# targets of the whole call at >= 60% of the int8 peak (us), per workload
+CALL_TARGET_US = {"large": 639.0, "sweep": 289.0}
+
+
+def time_linear(m8, torch, Xd, Wq, sW, thr, Y, ws, steps, warmup, stream):
+    """Whole calls between two events after a warm-up (at least 30 ms of calls), then
+    per-kernel times from events recorded between the kernels of the same call."""
+    import numpy as np
+    w0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - w0) < 0.03:
+        m8.llmint8_linear(Xd, Wq, sW, thr, Y=Y, workspace=ws)
+        n += 1
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        m8.llmint8_linear(Xd, Wq, sW, thr, Y=Y, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for row in evs:          # a torch event exists once it has been recorded
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    nk = 0
+    for row in evs:
+        nk = m8.llmint8_linear_timed(Xd, Wq, sW, thr, Y, ws, row)
+    torch.cuda.synchronize()
+    per = [float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs])) for i in range(nk)]
+    names = ["ka_scan", "ka_prepare", "kb_gemm"] if nk == 3 else ["kd_gemv"]
+    return call_ms, dict(zip(names, per))
+
+
+def graph_call_us(m8, torch, Xd, Wq, sW, thr, Y, ws, stream, calls=20, replays=10):
+    """Per-call time of `calls` calls captured in one HIP graph, replayed."""
+    return graph_us_per_call(lambda i: m8.llmint8_linear(Xd, Wq, sW, thr, Y=Y, workspace=ws),
+                             calls, replays, stream)
+
+
+def bench_configs(args, dev, stream):
+    """Tiny (CFG1), large (CFG4) and the outlier-fraction sweep (CFG5: n_out x threshold):
+    TOPS and % int8 peak of the whole call, per-kernel times, the GEMM's roofline, and
+    (sweep) the accuracy of Y against the fp32 product at both thresholds."""
+    import numpy as np
+    import torch
+
+    import mixed_precision_int8_amd as m8
+    import workloads
+
+    out = {}
+
+    def one(name, w, W_dev, Wq, sW, X, thr, target_us=None, accuracy=False):
+        T, K, N = X.shape[0], X.shape[1], Wq.shape[0]
+        Xd = torch.from_numpy(X).to(dev)
+        Y = torch.empty((T, N), dtype=torch.float16, device=dev)
+        need = m8.llmint8_workspace_bytes(T, K, N)
+        ws = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+        dbg = m8.llmint8_linear_debug(Xd, Wq, sW, thr, workspace=ws, want_C=False)
+        count = int(dbg["count"].cpu()[0])
+        del dbg
+        call_ms, kern = time_linear(m8, torch, Xd, Wq, sW, thr, Y, ws, args.config_steps,
+                                    args.warmup, stream)
+        ops = 2.0 * T * N * K
+        tops = ops / (call_ms * 1e-3) / 1e12
+        rec = {"T": T, "K": K, "N": N, "threshold": thr, "outliers": count,
+               "us_per_call": round(call_ms * 1e3, 2), "TOPS": round(tops, 1),
+               "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+               "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()}}
+        if "kb_gemm" in kern:
+            g = ops / (kern["kb_gemm"] * 1e-3) / 1e12
+            rec["gemm_tile"] = m8.llmint8_gemm_tile(T, N)
+            rec["roofline"] = roofline("mfma", "kb_gemm", g, PEAK_INT8_TOPS, "TFLOP/s", None,
+                                       unit_note="int8 tera-ops/s")
+        else:
+            rec["graph_us_per_call"] = round(graph_call_us(m8, torch, Xd, Wq, sW, thr, Y, ws, stream), 2)
+        if target_us:
+            rec["target_us"] = target_us
+            rec["meets_target"] = bool(rec["us_per_call"] <= target_us)
+        if accuracy:
+            # accuracy context (not parity): Y against the fp32 product X . W^T
+            Xf = Xd.float()
+            torch.backends.cuda.matmul.allow_tf32 = False
+            ref = Xf @ W_dev.float().t()
+            rec["rel_err_vs_fp32_product"] = float((Y.float() - ref).abs().max() / ref.abs().max())
+            del Xf, ref
+        del Xd, Y, ws
+        return rec
+
+    w1 = workloads.CONFIGS["tiny"]
+    W, X, _, _ = workloads.make(w1)
+    Wdv = torch.from_numpy(W).to(dev)
+    Wq, sW = m8.llmint8_quantize_weight(Wdv)
+    out["tiny"] = one("tiny", w1, Wdv, Wq, sW, X, w1.threshold)
+    out["tiny"]["workload"] = "tiny T=16 K=1024 N=1024, 4 outlier columns (latency-bound)"
+
+    w4 = workloads.CONFIGS["large"]
+    W, X, _, _ = workloads.make(w4)
+    Wdv = torch.from_numpy(W).to(dev)
+    Wq, sW = m8.llmint8_quantize_weight(Wdv)
+    del W
+    out["large"] = one("large", w4, Wdv, Wq, sW, X, w4.threshold, CALL_TARGET_US["large"])
+    out["large"]["workload"] = "large T=4096 K=8192 N=28672, 25 outlier columns, 41 rows zeroed"
+    del Wdv, Wq, sW
+
+    w5 = workloads.CONFIGS["sweep"]
+    W = workloads.make_weight(workloads.rng_for(w5.seed, 0), w5.N, w5.K, w5.sigma)
+    Wdv = torch.from_numpy(W).to(dev)
+    Wq, sW = m8.llmint8_quantize_weight(Wdv)
+    del W
+    sweep = {}
+    for n_out in workloads.SWEEP_N_OUT:
+        X = workloads.make(w5.with_(n_out=n_out), with_weight=False)[1]
+        for thr in workloads.SWEEP_THRESHOLDS:
+            key = f"n_out={n_out},thr={'inf' if thr == float('inf') else thr}"
+            sweep[key] = one(key, w5, Wdv, Wq, sW, X, thr, CALL_TARGET_US["sweep"], accuracy=True)
+    out["sweep"] = {"workload": "sweep T=2048 K=N=14336, n_out in {0, 8, 64, 512}, "
+                                "threshold in {6, inf}", "points": sweep}
+    del Wdv, Wq, sW
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -253,6 +381,11 @@ def main():
         "kernels_ms": {n: round(v, 5) for n, v in zip(names, per_kernel)},
         "wall_s_timed_region": round(wall, 4),
     }
+
+    # ---- the other workloads of the layer: tiny (latency), large hidden size and
+    # the outlier-fraction sweep (n_out x threshold), each timed like the headline
+    if not args.no_configs:
+        result["configs"] = bench_configs(args, dev, stream)
 
     # ---- the GEMM's MFMA instruction on its own (register operands, no memory
     # traffic): what the chip delivers at its running clock
@@ -629,11 +762,27 @@ def main():
         st = oracle.linear(X, Wq_ref, sW_ref, thr)
         c2 = time.perf_counter()
         cpu_tops = ops / (c2 - c1) / 1e12
+        # the same call stage by stage, with the oracle's own step functions
+        s0 = time.perf_counter()
+        mask = oracle.outlier_columns(X, thr)
+        Xq_o, aX_o = oracle.quantize_activations(X, mask)
+        s1 = time.perf_counter()
+        C_o = oracle.int8_matmul(Xq_o, Wq_ref)
+        s2 = time.perf_counter()
+        idx_o = np.flatnonzero(mask).astype(np.int32)
+        Xo_o, Wd_o = oracle.outlier_operands(X, Wq_ref, sW_ref, idx_o)
+        oracle.output(C_o, aX_o, sW_ref, Xo_o, Wd_o)
+        s3 = time.perf_counter()
+        del C_o, Xq_o
         result["cpu_baseline"] = {"value": round(cpu_tops, 5), "unit": "TOPS", "cores": threads,
                                   "kind": "oracle",
                                   "sample": f"one full prefill call (T={T},K={K},N={N}); "
                                             f"{c2 - c1:.2f} s, weight quantization "
-                                            f"{c1 - c0:.2f} s not counted"}
+                                            f"{c1 - c0:.2f} s not counted",
+                                  "stages_s": {"outlier_scan_and_quantize": round(s1 - s0, 4),
+                                               "int8_product_dgemm": round(s2 - s1, 4),
+                                               "outlier_product_and_epilogue": round(s3 - s2, 4),
+                                               "weight_quantize": round(c1 - c0, 4)}}
         result["parity"] = {"Y_max_abs_rel_err": oracle.parity_error(Yg, st.Y),
                             "outliers": st.count}
         if "bf16_bias" in result:

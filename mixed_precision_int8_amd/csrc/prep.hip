@@ -165,14 +165,20 @@ hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream) {
 //     Xo [KC][T][32] and the dequantized outlier weight columns Wd [KC][N][32]
 //     (zero past |O|), all gathers in flight together. Gather block 0
 //     publishes bitmap, idx and count.
-//   quantization blocks [ng, ng + nq): one wavefront per row of X; the row is
-//     read once into registers (up to kRegChunks 16-byte chunks per lane),
-//     reduced to its absmax over the kept columns, quantized and written as
-//     int8.
+//   quantization blocks [ng, ng + nq): one wavefront per row of X at a time;
+//     a row is held in registers (CPL 16-byte chunks per lane, the row's
+//     length rounded up to a template capacity), reduced to its absmax over
+//     the kept columns, quantized and written as int8. Each wavefront takes
+//     rows wave, wave + W, ... (W quantization wavefronts) with two register
+//     buffers: the next row's loads are in flight while the current row is
+//     reduced and its codes are stored, so stores and loads overlap when a
+//     wavefront has several rows (up to 8192 columns per row). Rows longer
+//     than the largest capacity (CPL = 0) are read twice from memory, which
+//     keeps the kernel's registers low enough for all its blocks to stay
+//     resident.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 256;
 constexpr int kMaxKW = kMaxK / 32;
-constexpr int kRegChunks = 16;
 constexpr int kIdxCap = 4096;  // outlier indices kept in LDS by the gather blocks
 
 __device__ __forceinline__ uint32_t chunk_skip_mask(const uint32_t* bm, int c) {
@@ -193,7 +199,61 @@ __device__ __forceinline__ uint32_t chunk_kept_max(const uint4& v, uint32_t skip
   return max((uint32_t)mx.x, (uint32_t)mx.y);
 }
 
+// One row of X held in registers: chunk lane + 64 u in v[u] (chunks past the row read as zero)
+template <int CPL>
+__device__ __forceinline__ void load_row_regs(const LinearArgs& a, int t, int lane, uint4 (&v)[CPL]) {
+  const int K = a.K, cpl = ((K >> 3) + 63) >> 6;
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X + (size_t)t * K, (uint32_t)(K * 2));
+#pragma unroll
+  for (int u = 0; u < CPL; ++u)
+    if (u < cpl) v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, (uint32_t)((lane + 64 * u) * 16), 0, 0));
+}
+
+// absmax over the kept columns, quantization and the stores of row t (held in v)
+template <bool BF16, int CPL>
+__device__ __forceinline__ void quantize_row_regs(const LinearArgs& a, const uint32_t* bm, int t, int lane,
+                                                  const uint4 (&v)[CPL]) {
+  const int K = a.K, KC = K >> 3, cpl = (KC + 63) >> 6;
+  uint32_t m = 0u;
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int c = lane + 64 * u;
+    if (u < cpl && c < KC) m = max(m, chunk_kept_max(v[u], chunk_skip_mask(bm, c)));
+  }
+  m = wave_max_u16x2(m) & 0xffffu;
+  const float ax = Act16<BF16>::to_f32(m);
+  const float s = m ? 127.0f / ax : 0.0f;
+  uint2* out = reinterpret_cast<uint2*>(a.Xq + (size_t)t * K);
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int c = lane + 64 * u;
+    if (u < cpl && c < KC) {
+      const uint32_t skip = chunk_skip_mask(bm, c);
+      out[c] = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+    }
+  }
+  if (lane == 0) a.aX[t] = ax;
+}
+
+// rows longer than any register capacity: read twice (maximum, then codes)
 template <bool BF16>
+__device__ __forceinline__ void quantize_row_mem(const LinearArgs& a, const uint32_t* bm, int t, int lane) {
+  const int K = a.K, KC = K >> 3;
+  const uint4* row = reinterpret_cast<const uint4*>(a.X + (size_t)t * K);
+  uint2* out = reinterpret_cast<uint2*>(a.Xq + (size_t)t * K);
+  uint32_t m = 0u;
+  for (int c = lane; c < KC; c += 64) m = max(m, chunk_kept_max(row[c], chunk_skip_mask(bm, c)));
+  m = wave_max_u16x2(m) & 0xffffu;
+  const float ax = Act16<BF16>::to_f32(m);
+  const float s = m ? 127.0f / ax : 0.0f;
+  for (int c = lane; c < KC; c += 64) {
+    const uint32_t skip = chunk_skip_mask(bm, c);
+    out[c] = Act16<BF16>::quantize8(row[c], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+  }
+  if (lane == 0) a.aX[t] = ax;
+}
+
+template <bool BF16, int CPL>
 __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int groups, int nq) {
   __shared__ uint32_t bm[kMaxKW];
   __shared__ int pre[kMaxKW];
@@ -202,64 +262,40 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, K = a.K, N = a.N;
   const int KW = (K + 31) >> 5;
-  const int KC = K >> 3;
   const int ng = gridDim.x - nq;  // gather blocks come first: their bitmap reads then
   const bool quant = (int)blockIdx.x >= ng;  // queue ahead of the quantization blocks' X loads
 
   // quantization blocks start their first row's loads before anything else
   const int row0 = (blockIdx.x - ng) * 4 + wave;
-  uint4 v[kRegChunks];
-  const bool in_regs = KC <= 64 * kRegChunks;
-  const int cpl = (KC + 63) >> 6;  // chunks per lane
-  auto load_row = [&](int t) {
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X + (size_t)t * K, (uint32_t)(K * 2));
-#pragma unroll
-    for (int u = 0; u < kRegChunks; ++u)  // chunks past the row read as zero
-      if (u < cpl) v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, (uint32_t)((lane + 64 * u) * 16), 0, 0));
-  };
-  if (quant && in_regs && row0 < T) load_row(row0);
+  const int W = nq * 4;  // quantization wavefronts
+  constexpr int CB = CPL > 0 ? CPL : 1;
+  uint4 v0[CB], v1[CB];
+  if (CPL > 0 && quant && row0 < T) load_row_regs<CB>(a, row0, lane, v0);
+  // the row groups' partial bitmaps, all loads in flight before the first OR
   for (int w = tid; w < KW; w += kPrepThreads) {
+    uint32_t p[kScanMaxGroups];
+#pragma unroll
+    for (int g = 0; g < kScanMaxGroups; ++g) p[g] = g < groups ? a.parts[(size_t)g * KW + w] : 0u;
     uint32_t x = 0u;
-    for (int g = 0; g < groups; ++g) x |= a.parts[(size_t)g * KW + w];
+#pragma unroll
+    for (int g = 0; g < kScanMaxGroups; ++g) x |= p[g];
     bm[w] = x;
   }
   __syncthreads();
 
   if (quant) {
-    // ---- activations: one wavefront per row
-    for (int t = row0; t < T; t += nq * 4) {
-      const uint4* row = reinterpret_cast<const uint4*>(a.X + (size_t)t * K);
-      uint2* out = reinterpret_cast<uint2*>(a.Xq + (size_t)t * K);
-      uint32_t m = 0u;
-      if (in_regs) {
-        if (t != row0) load_row(t);
-#pragma unroll
-        for (int u = 0; u < kRegChunks; ++u) {
-          const int c = lane + 64 * u;
-          if (u < cpl && c < KC) m = max(m, chunk_kept_max(v[u], chunk_skip_mask(bm, c)));
-        }
-      } else {
-        for (int c = lane; c < KC; c += 64) m = max(m, chunk_kept_max(row[c], chunk_skip_mask(bm, c)));
+    // ---- activations: rows row0, row0 + W, ...; two register buffers alternate
+    if constexpr (CPL > 0) {
+      for (int t = row0; t < T; t += 2 * W) {
+        const int t1 = t + W;
+        if (t1 < T) load_row_regs<CB>(a, t1, lane, v1);
+        quantize_row_regs<BF16, CB>(a, bm, t, lane, v0);
+        if (t1 >= T) break;
+        if (t1 + W < T) load_row_regs<CB>(a, t1 + W, lane, v0);
+        quantize_row_regs<BF16, CB>(a, bm, t1, lane, v1);
       }
-      m = wave_max_u16x2(m) & 0xffffu;
-      const float ax = Act16<BF16>::to_f32(m);
-      const float s = m ? 127.0f / ax : 0.0f;
-      if (in_regs) {
-#pragma unroll
-        for (int u = 0; u < kRegChunks; ++u) {
-          const int c = lane + 64 * u;
-          if (u < cpl && c < KC) {
-            const uint32_t skip = chunk_skip_mask(bm, c);
-            out[c] = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
-          }
-        }
-      } else {
-        for (int c = lane; c < KC; c += 64) {
-          const uint32_t skip = chunk_skip_mask(bm, c);
-          out[c] = Act16<BF16>::quantize8(row[c], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
-        }
-      }
-      if (lane == 0) a.aX[t] = ax;
+    } else {
+      for (int t = row0; t < T; t += W) quantize_row_mem<BF16>(a, bm, t, lane);
     }
     return;
   }
@@ -312,6 +348,12 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
     const int row = it / ngrp;
     const int jg = it - row * ngrp;
     const int j0 = jg * 8;
+    if (j0 >= count) {  // a group wholly past |O| (chunk padding): zeros, no loads
+      const size_t dst = row < T ? ((size_t)(j0 / kOutChunk) * T + row) * kOutChunk + (j0 % kOutChunk)
+                                 : ((size_t)(j0 / kOutChunk) * N + (row - T)) * kOutChunk + (j0 % kOutChunk);
+      *reinterpret_cast<uint4*>((row < T ? a.Xo : a.Wd) + dst) = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
     // column of each outlier j0 .. j0+7 (index 0 past |O|, masked later):
     // from the LDS table, or beyond it by a binary search for the word holding
     // it (last word with pre[w] <= j), all 8 searches advancing together,
@@ -376,19 +418,31 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   }
 }
 
+template <bool BF16>
+static hipError_t launch_prepare_dt(const LinearArgs& a, int groups, dim3 grid, int nq, hipStream_t stream) {
+  const int cpl = ((a.K >> 3) + 63) >> 6;  // 16-byte chunks per lane of one row
+  if (cpl <= 8)
+    hipLaunchKernelGGL((ka_prepare<BF16, 8>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
+  else if (cpl <= 16)
+    hipLaunchKernelGGL((ka_prepare<BF16, 16>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
+  else
+    hipLaunchKernelGGL((ka_prepare<BF16, 0>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
+  return hipGetLastError();
+}
+
 hipError_t launch_prepare(const LinearArgs& a, int groups, int num_cus, hipStream_t stream) {
-  int nq = (a.T + 3) / 4;
+  // quantization wavefronts: one row each (every row's loads in flight at
+  // once), at most 16 per CU
+  int nq = (int)ceil_div(a.T, 4);
   if (nq > 4 * num_cus) nq = 4 * num_cus;
   if (nq < 1) nq = 1;
   // gather work for up to 32 outliers; more are covered by the grid-stride loop
   int ng = (int)ceil_div((int64_t)(a.T + a.N) * (kOutChunk / 8), kPrepThreads);
   if (ng > 2 * num_cus) ng = 2 * num_cus;
   if (ng < 1) ng = 1;
-  if (a.bf16)
-    hipLaunchKernelGGL(ka_prepare<true>, dim3(nq + ng), dim3(kPrepThreads), 0, stream, a, groups, nq);
-  else
-    hipLaunchKernelGGL(ka_prepare<false>, dim3(nq + ng), dim3(kPrepThreads), 0, stream, a, groups, nq);
-  return hipGetLastError();
+  const dim3 grid(nq + ng);
+  return a.bf16 ? launch_prepare_dt<true>(a, groups, grid, nq, stream)
+                : launch_prepare_dt<false>(a, groups, grid, nq, stream);
 }
 
 }  // namespace llmint8

@@ -49,27 +49,75 @@ __device__ __forceinline__ uint4 outlier_x8(const LinearArgs& a, int t, int j0, 
   return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
 }
 
-// Epilogue of one wavefront: its FNW x FT accumulator blocks, weight rows
-// nw0.. and activation rows tw0.. of the output. sW_w / aX_w / bias_w point at
-// the wavefront's first entries of the tile's scales and bias in LDS (bias_w
-// null without bias). `wf(i, h)` / `xf(j, h)` give the 16-bit operands of the
-// first chunk of 32 outlier columns (k-step h of block i / j); later chunks
-// are read from the workspace here, or formed from Wq and X past the chunks
-// it holds. Output layout of a 32x32 block: lane holds, for column (t)
-// lane&31, rows (n) 8*q + 4*(lane>>5) + r in register 4*q + r.
+// The LDS layout of staged outlier operands: a chunk of 32 outlier columns is
+// BN rows of Wd then BT rows of Xo, 64 bytes each; row r keeps its 16-byte
+// piece c at position c ^ ((r >> 2) & 3), so that the epilogue's reads (32 rows
+// x 2 pieces per instruction) are free of bank conflicts.
+__device__ __forceinline__ uint4 staged_outlier_piece(const char* area, int r, int piece) {
+  return *reinterpret_cast<const uint4*>(area + r * 64 + ((piece ^ ((r >> 2) & 3)) * 16));
+}
+
+// Direct copies of chunk c's operands of the tile (rows past the matrix read
+// as zero) into `area`; every wavefront of the block takes pieces of 1 KB
+// (16 rows) in turn.
+template <int BN, int BT, int NWAVES>
+__device__ __forceinline__ void stage_outlier_chunk(const LinearArgs& a, int c, int n0, int t0, int rows_n,
+                                                    int rows_t, char* area, int wave, int lane) {
+  constexpr int CW = BN * 64 / 1024, CXO = BT * 64 / 1024;
+  static_assert(BN * 64 % 1024 == 0 && BT * 64 % 1024 == 0, "1 KB pieces");
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(a.Wd + ((size_t)c * a.N + n0) * kOutChunk, (uint32_t)(rows_n * 64));
+  const __amdgpu_buffer_rsrc_t rO =
+      make_rsrc(a.Xo + ((size_t)c * a.T + t0) * kOutChunk, (uint32_t)(rows_t * 64));
+  for (int p = wave; p < CW + CXO; p += NWAVES) {
+    const bool is_w = p < CW;  // wave-uniform
+    const int r = p * 16 + (lane >> 2);  // row of the staged area this lane fills
+    const uint32_t src = (uint32_t)((is_w ? p : p - CW) * 1024 + (lane >> 2) * 64 +
+                                    (((lane & 3) ^ ((r >> 2) & 3)) * 16));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_w ? rW : rO,
+                                             (__attribute__((address_space(3))) void*)(area + p * 1024),
+                                             16, src, 0, 0, 0);
+  }
+}
+
+// Where the epilogue may stage outlier chunks 1, 2, ... of a tile: `buf`, the
+// block's LDS ring (free once every wavefront is past the K loop; all copies
+// landed), of `bytes`; wavefront `wave` of NWAVES; tile origin and extent.
+struct ChunkStaging {
+  char* buf;
+  int bytes, wave, n0, t0, rows_n, rows_t;
+};
+
+// Epilogue of one wavefront: its FNW x FT accumulator blocks, at rows wrow..
+// (weights) and wcol.. (activations) of a BN x BT tile at (n0, t0) of the
+// output. sW_w / aX_w / bias_w point at the wavefront's first entries of the
+// tile's scales and bias in LDS (bias_w null without bias). `wf(i, h)` /
+// `xf(j, h)` give the 16-bit operands of the first chunk of 32 outlier columns
+// (k-step h of block i / j). Output layout of a 32x32 block: lane holds, for
+// column (t) lane&31, rows (n) 8*q + 4*(lane>>5) + r in register 4*q + r.
+//
+// Three phases. (1) Every block is dequantized, C * a * b / 127^2, and takes
+// the first chunk's 16-bit product. (2) Chunks 1, 2, ... that the workspace
+// holds go through LDS: all wavefronts of the block copy as many chunks as
+// `cs.buf` holds, wait, multiply every block with them and wait again, so
+// each chunk costs one memory latency per tile. Chunks past those the
+// workspace holds are formed from X and Wq per block. (3) Bias, rounding and
+// the store of each block. Every wavefront of a block calls this with the
+// same |O| (the barriers of phase 2 are the block's).
 //
 // Y is written one of two ways. Directly, each lane stores its 4-value pieces
 // (16 contiguous bytes of an output row per instruction). Or, when `stage`
 // (a wavefront-private LDS area of kStageBytes) is given, the tile lies wholly
 // inside Y and rows are 16-byte aligned, through LDS: two 32-row blocks are
 // gathered as 64 output rows of 128 bytes and stored as whole 128-byte lines.
-template <bool BF16, int FNW, int FT, class WF, class XF>
-__device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&acc)[FNW][FT], int nw0,
-                                              int tw0, const float* sW_w, const float* aX_w,
+template <bool BF16, int FNW, int FT, int BN, int BT, int NWAVES, class WF, class XF>
+__device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&acc)[FNW][FT], int wrow,
+                                              int wcol, const float* sW_w, const float* aX_w,
                                               const uint16_t* bias_w, int count, int lane, WF&& wf,
-                                              XF&& xf, char* stage = nullptr) {
+                                              XF&& xf, const ChunkStaging& cs, char* stage = nullptr) {
   using A16 = Act16<BF16>;
   const int N = a.N, T = a.T;
+  const int nw0 = cs.n0 + wrow, tw0 = cs.t0 + wcol;
   const int nch = (count + kOutChunk - 1) / kOutChunk;
   const int fi = lane & 31, fg = lane >> 5;
   const int nl = nw0 + 4 * fg;  // + i*32 + 8*q + r
@@ -78,6 +126,9 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
 #pragma unroll
   for (int j = 0; j < FT; ++j) as[j] = aX_w[fi + j * 32];
   const bool vec_ok = (N & 3) == 0;
+
+  // ---- (1) dequantization and the first outlier chunk, every block
+  v16f y[FNW][FT];
 #pragma unroll
   for (int i = 0; i < FNW; ++i) {
     float bs[16];
@@ -99,11 +150,10 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
         }
       }
     }
-    v16f y[FT];
 #pragma unroll
     for (int j = 0; j < FT; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) y[j][v] = (float)acc[i][j][v] * (as[j] * bs[v]);
+      for (int v = 0; v < 16; ++v) y[i][j][v] = (float)acc[i][j][v] * (as[j] * bs[v]);
     // outlier columns: 16-bit operands (the activation type), fp32 accumulation
     // on top of the int8 part; a chunk of 32 outlier columns is two 32x32x16 steps.
     if (nch > 0) {
@@ -111,29 +161,56 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
       for (int h = 0; h < 2; ++h) {
         const uint4 w = wf(i, h);
 #pragma unroll
-        for (int j = 0; j < FT; ++j) y[j] = A16::mma32(w, xf(j, h), y[j]);
+        for (int j = 0; j < FT; ++j) y[i][j] = A16::mma32(w, xf(j, h), y[i][j]);
       }
     }
+  }
+
+  // ---- (2) chunks 1 .. held-1 through LDS, batches of as many as cs.buf holds
+  const int held = min(nch, a.wchunks);
+  if (held > 1) {  // uniform over the block
+    constexpr int kChunkBytes = (BN + BT) * 64;
+    const int per = cs.bytes / kChunkBytes;
+    for (int c0 = 1; c0 < held; c0 += per) {
+      const int cn = min(per, held - c0);
+      wait_vmcnt<0>();
+      __syncthreads();  // the ring (the K loop's, or the previous batch's) is free
+      for (int cc = 0; cc < cn; ++cc)
+        stage_outlier_chunk<BN, BT, NWAVES>(a, c0 + cc, cs.n0, cs.t0, cs.rows_n, cs.rows_t,
+                                            cs.buf + cc * kChunkBytes, cs.wave, lane);
+      wait_vmcnt<0>();
+      __syncthreads();
+      for (int cc = 0; cc < cn; ++cc) {
+        const char* area = cs.buf + cc * kChunkBytes;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint4 x[FT];
+#pragma unroll
+          for (int j = 0; j < FT; ++j) x[j] = staged_outlier_piece(area, BN + wcol + j * 32 + fi, 2 * h + fg);
+#pragma unroll
+          for (int i = 0; i < FNW; ++i) {
+            const uint4 w = staged_outlier_piece(area, wrow + i * 32 + fi, 2 * h + fg);
+#pragma unroll
+            for (int j = 0; j < FT; ++j) y[i][j] = A16::mma32(w, x[j], y[i][j]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // every wavefront's reads are done before the ring is reused
+  }
+
+  // ---- (3) chunks past the workspace (formed here), bias, rounding, stores
+#pragma unroll
+  for (int i = 0; i < FNW; ++i) {
     const int nrow = min(nw0 + i * 32 + fi, N - 1);
-    for (int c = 1; c < nch; ++c) {
+    for (int c = max(1, held); c < nch; ++c) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        uint4 w, x[FT];
-        if (c < a.wchunks) {  // uniform
-          w = *reinterpret_cast<const uint4*>(a.Wd + ((size_t)c * N + nrow) * kOutChunk + h * 16 + fg * 8);
+        const int j0 = c * kOutChunk + h * 16 + fg * 8;
+        const uint4 w = outlier_w8<BF16>(a, nrow, j0, count);
 #pragma unroll
-          for (int j = 0; j < FT; ++j) {
-            const int t = min(tl + j * 32, T - 1);
-            x[j] = *reinterpret_cast<const uint4*>(a.Xo + ((size_t)c * T + t) * kOutChunk + h * 16 + fg * 8);
-          }
-        } else {
-          const int j0 = c * kOutChunk + h * 16 + fg * 8;
-          w = outlier_w8<BF16>(a, nrow, j0, count);
-#pragma unroll
-          for (int j = 0; j < FT; ++j) x[j] = outlier_x8(a, min(tl + j * 32, T - 1), j0, count);
-        }
-#pragma unroll
-        for (int j = 0; j < FT; ++j) y[j] = A16::mma32(w, x[j], y[j]);
+        for (int j = 0; j < FT; ++j)
+          y[i][j] = A16::mma32(w, outlier_x8(a, min(tl + j * 32, T - 1), j0, count), y[i][j]);
       }
     }
     if (bias_w) {
@@ -141,7 +218,7 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
       for (int v = 0; v < 16; ++v) {
         const float bv = A16::to_f32(bias_w[4 * fg + i * 32 + 8 * (v >> 2) + (v & 3)]);
 #pragma unroll
-        for (int j = 0; j < FT; ++j) y[j][v] += bv;
+        for (int j = 0; j < FT; ++j) y[i][j][v] += bv;
       }
     }
     if constexpr (FT == 2) if (stage) {  // uniform; 64 staged rows
@@ -151,8 +228,8 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           uint2 p;
-          p.x = (uint32_t)A16::from_f32(y[j][4 * q]) | ((uint32_t)A16::from_f32(y[j][4 * q + 1]) << 16);
-          p.y = (uint32_t)A16::from_f32(y[j][4 * q + 2]) | ((uint32_t)A16::from_f32(y[j][4 * q + 3]) << 16);
+          p.x = (uint32_t)A16::from_f32(y[i][j][4 * q]) | ((uint32_t)A16::from_f32(y[i][j][4 * q + 1]) << 16);
+          p.y = (uint32_t)A16::from_f32(y[i][j][4 * q + 2]) | ((uint32_t)A16::from_f32(y[i][j][4 * q + 3]) << 16);
           stage_put(stage, i, j, q, fi, fg, p);
         }
       if ((i & 1) || i == FNW - 1)
@@ -169,12 +246,12 @@ __device__ __forceinline__ void gemm_epilogue(const LinearArgs& a, const v16i (&
         uint16_t* dst = a.Y + (size_t)t * N + n;
         if (vec_ok && n + 3 < N) {
           uint2 p;
-          p.x = (uint32_t)A16::from_f32(y[j][4 * q]) | ((uint32_t)A16::from_f32(y[j][4 * q + 1]) << 16);
-          p.y = (uint32_t)A16::from_f32(y[j][4 * q + 2]) | ((uint32_t)A16::from_f32(y[j][4 * q + 3]) << 16);
+          p.x = (uint32_t)A16::from_f32(y[i][j][4 * q]) | ((uint32_t)A16::from_f32(y[i][j][4 * q + 1]) << 16);
+          p.y = (uint32_t)A16::from_f32(y[i][j][4 * q + 2]) | ((uint32_t)A16::from_f32(y[i][j][4 * q + 3]) << 16);
           *reinterpret_cast<uint2*>(dst) = p;
         } else {
           for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = A16::from_f32(y[j][4 * q + r]);
+            if (n + r < N) dst[r] = A16::from_f32(y[i][j][4 * q + r]);
         }
       }
     }
@@ -259,9 +336,11 @@ __global__ __launch_bounds__(G::kThreads, 1) void kb_gemm(LinearArgs a, int tile
   // every copy landed, so the whole ring is free)
   constexpr bool kCanStage = G::NSTAGE == 2 && G::FT == 2 && G::NWAVES * kStageBytes <= G::LDS;
   const bool staged = kCanStage && rows_n == G::BN && rows_t == G::BT && (N & 7) == 0;
-  gemm_epilogue<BF16, G::FN, G::FT>(
-      a, acc, nw0, tw0, sW_l + wn * G::WN, aX_l + wt * G::WT, a.bias ? bias_l + wn * G::WN : nullptr,
-      count, lane, [&](int i, int h) { return wf0[i][h]; }, [&](int j, int h) { return xf0[j][h]; },
+  gemm_epilogue<BF16, G::FN, G::FT, G::BN, G::BT, G::NWAVES>(
+      a, acc, wn * G::WN, wt * G::WT, sW_l + wn * G::WN, aX_l + wt * G::WT,
+      a.bias ? bias_l + wn * G::WN : nullptr, count, lane, [&](int i, int h) { return wf0[i][h]; },
+      [&](int j, int h) { return xf0[j][h]; },
+      ChunkStaging{smem, G::LDS, wave, n0, t0, rows_n, rows_t},
       staged ? smem + wave * kStageBytes : nullptr);
 }
 
@@ -284,27 +363,14 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
   const int count = *a.count;
   const int nch = (count + kOutChunk - 1) / kOutChunk;
   // The first chunk of 32 outlier columns (the common case is a single chunk):
-  // the tile's BN rows of Wd and BT rows of Xo, 64 bytes each, are copied into
-  // the ring slot that the last K stage leaves free, while its MFMAs run. Row r
-  // of that area keeps its 16-byte chunk c at position c ^ ((r >> 2) & 3), so
-  // that the epilogue's reads (32 rows x 2 chunks per instruction) are free of
-  // bank conflicts.
+  // the tile's BN rows of Wd and BT rows of Xo are copied into the ring slot
+  // that the last K stage leaves free, while its MFMAs run (layout of
+  // staged_outlier_piece).
   const char* epi = nullptr;
   auto outliers_to_lds = [&](char* free_slot) {
     epi = free_slot;
-    if (nch == 0) return;
-    constexpr int CW = G::BN * 64 / 1024, CXO = G::BT * 64 / 1024;
-    static_assert(G::BN * 64 % 1024 == 0 && G::BT * 64 % 1024 == 0, "1 KB pieces");
     static_assert((G::BN + G::BT) * 64 <= G::STAGE, "fits a slot");
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.Wd + (size_t)n0 * kOutChunk, (uint32_t)(rows_n * 64));
-    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.Xo + (size_t)t0 * kOutChunk, (uint32_t)(rows_t * 64));
-    for (int c = wave; c < CW + CXO; c += G::NWAVES) {
-      const bool is_w = c < CW;  // wave-uniform
-      const int r = c * 16 + (lane >> 2);  // row of the staged area this lane fills
-      const uint32_t src = (uint32_t)((is_w ? c : c - CW) * 1024 + (lane >> 2) * 64 +
-                                      (((lane & 3) ^ ((r >> 2) & 3)) * 16));
-      lds_dma16(is_w ? rW : rO, free_slot + c * 1024, src);
-    }
+    if (nch > 0) stage_outlier_chunk<G::BN, G::BT, G::NWAVES>(a, 0, n0, t0, rows_n, rows_t, free_slot, wave, lane);
   };
   v16i acc[FNW][G::FT];
   gemm_kloop_split<G, MmaI8, FNW>(smem, rA, rB, K, wave, lane, wrow, wcol, acc, before_prologue,
@@ -319,17 +385,12 @@ __device__ __forceinline__ void split_column(const LinearArgs& a, char* smem, in
   static_assert(G::NWAVES * kStageBytes <= G::STAGE, "staging fits the last slot");
   const bool staged = rows_n == G::BN && rows_t == G::BT && (a.N & 7) == 0;
   char* last_slot = epi == smem ? smem + G::STAGE : smem;  // the last stage's slot, free now
-  gemm_epilogue<BF16, FNW, G::FT>(
-      a, acc, n0 + wrow, t0 + wcol, sW_l + wrow, aX_l + wcol, a.bias ? bias_l + wrow : nullptr, count,
+  gemm_epilogue<BF16, FNW, G::FT, G::BN, G::BT, G::NWAVES>(
+      a, acc, wrow, wcol, sW_l + wrow, aX_l + wcol, a.bias ? bias_l + wrow : nullptr, count,
       lane,
-      [&](int i, int h) {
-        const int r = wrow + i * 32 + fi;
-        return *reinterpret_cast<const uint4*>(epi + r * 64 + (((2 * h + fg) ^ ((r >> 2) & 3)) * 16));
-      },
-      [&](int j, int h) {
-        const int r = G::BN + wcol + j * 32 + fi;
-        return *reinterpret_cast<const uint4*>(epi + r * 64 + (((2 * h + fg) ^ ((r >> 2) & 3)) * 16));
-      },
+      [&](int i, int h) { return staged_outlier_piece(epi, wrow + i * 32 + fi, 2 * h + fg); },
+      [&](int j, int h) { return staged_outlier_piece(epi, G::BN + wcol + j * 32 + fi, 2 * h + fg); },
+      ChunkStaging{smem, G::LDS, wave, n0, t0, rows_n, rows_t},
       staged ? last_slot + wave * kStageBytes : nullptr);
 }
 

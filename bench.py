@@ -33,10 +33,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "kb_gemm_prefill_counters.txt")
 PROFILE_BWD_COUNTERS = os.path.join(ROOT, "profiles", "kg_backward_prefill_counters.txt")
-BWD_SOURCES = ("bwd.hip", "gemm_common.h", "device_util.h", "internal.h")
+BWD_SOURCES = ("bwd.hip", "gemm_common.h", "device_util.h", "internal.h", "ranges.h")
+PROFILE_DECODE_COUNTERS = os.path.join(ROOT, "profiles", "kd_gemv_decode_counters.txt")
+DECODE_SOURCES = ("gemv.hip", "device_util.h", "internal.h", "ranges.h")
 PROFILE_NEXT_COUNTERS = os.path.join(ROOT, "profiles", "bf16_codec_nf4_counters.txt")
 NEXT_SOURCES = ("gemm.hip", "gemm_common.h", "blockwise.hip", "fourbit.hip", "device_util.h",
-                "internal.h")
+                "internal.h", "ranges.h")
 
 
 def roofline(bound, kernel, achieved, peak, unit, traffic, **extra):
@@ -82,7 +84,7 @@ def parse():
 
 def kernel_source_hash(files=None) -> str:
     h = hashlib.sha256()
-    for f in files or ("gemm.hip", "gemm_common.h", "device_util.h", "internal.h"):
+    for f in files or ("gemm.hip", "gemm_common.h", "device_util.h", "internal.h", "ranges.h"):
         with open(os.path.join(ROOT, "mixed_precision_int8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -113,26 +115,61 @@ def committed_mfma_activity():
     return (float(busy.group(1)) if busy else None, float(clock.group(1)) if clock else None)
 
 
-def probe_mfma_i8(blocks, iters, out, stream):
-    """The matrix-core rate probe (libllmint8_probe.so, a measurement helper built beside
-    the product library): blocks x 4 wavefronts, each iters x 4 v_mfma_i32_32x32x32_i8.
-    Returns the int8 operation count of the call."""
+_PROBE = None
+
+
+def _probe_lib():
+    """libllmint8_probe.so: measurement helpers built beside the product library."""
     import ctypes
     global _PROBE
     if _PROBE is None:
-        path = os.path.join(ROOT, "mixed_precision_int8_amd", "libllmint8_probe.so")
-        _PROBE = ctypes.CDLL(path)
-        _PROBE.llmint8_bench_probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                                       ctypes.c_void_p]
-        _PROBE.llmint8_bench_probe_mfma_i8.restype = ctypes.c_int
-    st = _PROBE.llmint8_bench_probe_mfma_i8(int(blocks), int(iters), ctypes.c_void_p(out.data_ptr()),
-                                            ctypes.c_void_p(stream.cuda_stream))
+        lib = ctypes.CDLL(os.path.join(ROOT, "mixed_precision_int8_amd", "libllmint8_probe.so"))
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        for name, args in (("llmint8_bench_probe_mfma_i8", [i, i, vp, vp]),
+                           ("llmint8_bench_probe_mfma_i8_lds_random", [i, i, vp, vp]),
+                           ("llmint8_bench_probe_stream", [vp, ctypes.c_size_t, vp, vp]),
+                           ("llmint8_bench_probe_empty", [vp, vp])):
+            getattr(lib, name).argtypes = args
+            getattr(lib, name).restype = i
+        _PROBE = lib
+    return _PROBE
+
+
+def _probe_check(st, name):
     if st != 0:
-        raise RuntimeError(f"probe launch failed ({st})")
+        raise RuntimeError(f"{name} failed ({st})")
+
+
+def probe_mfma_i8(blocks, iters, out, stream):
+    """The matrix-core rate probe: blocks x 4 wavefronts, each iters x 4
+    v_mfma_i32_32x32x32_i8 from registers. Returns the int8 operation count."""
+    import ctypes
+    _probe_check(_probe_lib().llmint8_bench_probe_mfma_i8(int(blocks), int(iters), ctypes.c_void_p(out.data_ptr()),
+                                                          ctypes.c_void_p(stream.cuda_stream)), "probe")
     return blocks * 4 * iters * 4 * 2 * 32 * 32 * 32
 
 
-_PROBE = None
+def probe_mfma_i8_lds_random(blocks, iters, out, stream):
+    """The same MFMA, 8 wavefronts of 4 x 2 blocks with fragments re-read from LDS full
+    of pseudo-random bytes every k-step. Returns the int8 operation count."""
+    import ctypes
+    _probe_check(_probe_lib().llmint8_bench_probe_mfma_i8_lds_random(
+        int(blocks), int(iters), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)),
+        "probe_lds_random")
+    return blocks * 8 * iters * 4 * 8 * 2 * 32 * 32 * 32
+
+
+def probe_stream(buf, n16, out, stream):
+    import ctypes
+    _probe_check(_probe_lib().llmint8_bench_probe_stream(ctypes.c_void_p(buf.data_ptr()), int(n16),
+                                                         ctypes.c_void_p(out.data_ptr()),
+                                                         ctypes.c_void_p(stream.cuda_stream)), "probe_stream")
+
+
+def probe_empty(out, stream):
+    import ctypes
+    _probe_check(_probe_lib().llmint8_bench_probe_empty(ctypes.c_void_p(out.data_ptr()),
+                                                        ctypes.c_void_p(stream.cuda_stream)), "probe_empty")
 
 
 def graph_us_per_call(fn, n_calls, replays, stream):
@@ -412,6 +449,49 @@ def main():
             "TOPS": round(ptops, 1), "pct_int8_peak": round(100.0 * ptops / PEAK_INT8_TOPS, 2),
             "gemm_fraction_of_probe": round(gemm_tops / ptops, 4) if gemm_tops else None}
         del pout
+        # the same instruction on operands that change every instruction (fragments
+        # re-read from LDS full of pseudo-random bytes): int8 MFMA power grows with the
+        # operand bits that switch, and the chip lowers its clock
+        rout = torch.empty((cus * 512,), dtype=torch.int32, device=dev)
+        for _ in range(3):
+            rops = probe_mfma_i8_lds_random(cus, 400, rout, stream)
+        torch.cuda.synchronize()
+        rms = []
+        for _ in range(5):
+            p0 = torch.cuda.Event(enable_timing=True)
+            p1 = torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            probe_mfma_i8_lds_random(cus, 400, rout, stream)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            rms.append(p0.elapsed_time(p1))
+        rtops = rops / (sorted(rms)[2] * 1e-3) / 1e12
+        del rout
+        # the prefill GEMM itself on all-zero int8 codes (nothing switches) against
+        # the workload's codes, same kernel and shapes
+        Xz = torch.zeros((T, K), dtype=torch.float16, device=dev)
+        Xz[:, 0] = 1.0
+        Wz = torch.zeros((N, K), dtype=torch.float16, device=dev)
+        Wz[:, 0] = 0.02
+        Wqz, sWz = m8.llmint8_quantize_weight(Wz)
+        del Wz
+        Yz = torch.empty_like(Y)   # the headline's Y stays for the parity check
+        zkern = time_linear(m8, torch, Xz, Wqz, sWz, thr, Yz, ws, args.steps, args.warmup, stream)[1]
+        del Xz, Wqz, sWz, Yz
+        result["mfma_probe"]["random_operands"] = {
+            "kernel": "8 wavefronts x (4 x 2) 32x32 blocks, fragments re-read from LDS (random bytes) "
+                      "every k-step, no global memory", "TOPS": round(rtops, 1),
+            "pct_int8_peak": round(100.0 * rtops / PEAK_INT8_TOPS, 2),
+            "gemm_fraction": round(gemm_tops / rtops, 4) if gemm_tops else None}
+        if result.get("roofline"):
+            # context for the GEMM's fraction: what the same instruction sustains on
+            # operands that switch like real ones, with no memory traffic at all
+            result["roofline"]["random_operand_mfma_TOPS"] = round(rtops, 1)
+            result["roofline"]["frac_of_random_operand_mfma"] = round(gemm_tops / rtops, 4)
+        result["mfma_probe"]["gemm_on_zero_codes"] = {
+            "kb_gemm_us": round(zkern["kb_gemm"] * 1e3, 2),
+            "kb_gemm_us_workload": round(gemm_ms * 1e3, 2),
+            "TOPS": round(ops / (zkern["kb_gemm"] * 1e-3) / 1e12, 1)}
 
     # ---- decode-shaped workload: HBM-bound weight streaming
     if not args.no_decode:
@@ -447,13 +527,53 @@ def main():
             nbytes = wd.N * wd.K + 4 * wd.N + 2 * Td * wd.K + 2 * Td * wd.N
             gbs = nbytes / (us * 1e-6) / 1e9
             ggbs = nbytes / (gus * 1e-6) / 1e9
+            # the kernel alone: events recorded on the launch stream right around it
+            kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for row in kev:
+                for e in row:
+                    e.record(stream)
+            torch.cuda.synchronize()
+            for i, row in enumerate(kev):
+                q, s = copies[i % len(copies)]
+                m8.llmint8_linear_timed(Xt, q, s, wd.threshold, Yt, wst, row)
+            torch.cuda.synchronize()
+            kus = float(np.mean([row[0].elapsed_time(row[1]) for row in kev])) * 1e3
             dec[f"T{Td}"] = {"us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
                              "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
                              "graph_us_per_call": round(gus, 3), "graph_GB_per_s": round(ggbs, 1),
                              "graph_pct_hbm": round(100.0 * ggbs / PEAK_HBM_GBS, 2),
-                             "algorithmic_bytes": nbytes}
-        result["decode"] = {"workload": "decode_gemv K=4096 N=4096", "kernel": "kd_gemv",
-                            "weight_copies_cycled": len(copies), **dec}
+                             "kernel_us": round(kus, 3), "algorithmic_bytes": nbytes}
+        dtraffic = committed_traffic(PROFILE_DECODE_COUNTERS, DECODE_SOURCES)
+        k1 = dec["T1"]
+        result["decode"] = {
+            "workload": "decode_gemv K=4096 N=4096", "kernel": "kd_gemv",
+            "weight_copies_cycled": len(copies), **dec,
+            # per launch: the HIP-graph replay of back-to-back calls (events around the
+            # replays, on the launch stream) divided by the calls; events around a single
+            # kernel ("kernel_us") add their own ~2 us at this size
+            "roofline": roofline("hbm", "kd_gemv<1> (T = 1)",
+                                 k1["algorithmic_bytes"] / (k1["graph_us_per_call"] * 1e-6) / 1e9,
+                                 PEAK_HBM_GBS, "GB/s", dtraffic,
+                                 algorithmic_bytes_per_launch=k1["algorithmic_bytes"],
+                                 avg_launch_us=k1["graph_us_per_call"])}
+        if not args.no_probe:
+            # what one launch can do at this size: an empty kernel, and a plain read of
+            # the same weight bytes, both per call in a HIP graph, copies cycled the same way
+            out1 = torch.zeros(1, dtype=torch.int32, device=dev)
+            assert copies[0][0].numel() == wd.N * wd.K and (wd.N * wd.K) % 16 == 0
+            n16 = wd.N * wd.K // 16          # exactly the int8 weight's bytes
+            e_us = graph_us_per_call(lambda i: probe_empty(out1, torch.cuda.current_stream()),
+                                     len(copies), 10, stream)
+            s_us = graph_us_per_call(
+                lambda i: probe_stream(copies[i][0], n16, out1, torch.cuda.current_stream()),
+                len(copies), 10, stream)
+            result["decode"]["floor"] = {
+                "empty_kernel_graph_us_per_call": round(e_us, 3),
+                "plain_read_graph_us_per_call": round(s_us, 3),
+                "plain_read_GB_per_s": round(n16 * 16 / (s_us * 1e-6) / 1e9, 1),
+                "plain_read_pct_hbm": round(100.0 * n16 * 16 / (s_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+                "note": "a plain read of the int8 decode weight (16.78 MB), 256-thread workgroups, one "
+                        "16-byte load per thread, the fastest launch shape measured for this size"}
         del copies
 
     # ---- bf16 activations with a fused bias: the prefill and decode shapes again

@@ -1,4 +1,4 @@
-// Measurement helper of the benchmark, not part of the method and not part of
+// Measurement helpers of the benchmark, not part of the method and not part of
 // libllmint8: the peak rate of the matrix-core instruction the int8 GEMM is
 // built on (v_mfma_i32_32x32x32_i8), so that the GEMM's rate can be set against
 // what the chip delivers at its running clock as well as against the published
@@ -36,5 +36,113 @@ extern "C" __attribute__((visibility("default"))) int llmint8_bench_probe_mfma_i
   if (blocks <= 0 || iters <= 0 || !out || (reinterpret_cast<uintptr_t>(out) & 3u) != 0) return -1;
   hipLaunchKernelGGL(kp_mfma_i8, dim3(blocks), dim3(kProbeThreads), 0, static_cast<hipStream_t>(stream),
                      iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// ---------------------------------------------------------------------------
+// The same MFMA on operands that change every instruction: 8 wavefronts per
+// block, each with 4 x 2 accumulator blocks whose fragments are re-read from
+// LDS (pseudo-random bytes, 128-byte rows with the GEMM's XOR swizzle) every
+// k-step, like the GEMM's K loop without its global memory traffic. Int8 MFMA
+// power depends on how many operand bits switch; this gives the rate the chip
+// sustains on such operands.
+__global__ __launch_bounds__(512, 1) void kp_mfma_i8_lds_random(int iters, int32_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char smem[65536];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 65536 / 16; i += 512) {
+    uint32_t h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // an integer hash of the byte position
+      uint32_t x = (uint32_t)(i * 4 + q) * 2654435761u;
+      x ^= x >> 15;
+      x *= 2246822519u;
+      x ^= x >> 13;
+      h[q] = x;
+    }
+    reinterpret_cast<v4i*>(smem)[i] = v4i{(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
+  }
+  __syncthreads();
+  constexpr int FN = 4, FT = 2;
+  v16i acc[FN][FT];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) acc[i][j] = v16i{};
+  const int fi = lane & 31, fg = lane >> 5;
+  const int sw = (fi ^ (fi >> 3)) & 7;
+  // A rows (wave & 1) * 128 + i * 32 + fi, B rows (wave >> 1) * 64 + j * 32 + fi of
+  // 128-byte rows; k-step ks reads piece 2 ks + fg; + a multiple of 32 rows per
+  // k-step so that no read is loop-invariant (every address stays in its 32 KB half)
+  auto aoff = [&](int i, int ks, int sh) {
+    return ((((wave & 1) * 128 + i * 32 + fi) * 128 + (((ks * 2 + fg) ^ sw) * 16)) + sh) & 32767;
+  };
+  auto boff = [&](int j, int ks, int sh) {
+    return 32768 + (((((wave >> 1) * 64 + j * 32 + fi) * 128 + (((ks * 2 + fg) ^ sw) * 16)) + sh) & 32767);
+  };
+  v4i fa[FN], fb[FT];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) fa[i] = *reinterpret_cast<const v4i*>(smem + aoff(i, 0, 0));
+#pragma unroll
+  for (int j = 0; j < FT; ++j) fb[j] = *reinterpret_cast<const v4i*>(smem + boff(j, 0, 0));
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < FT; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      const int sh = ((it * 4 + ks) & 3) * 4096;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) fa[i] = *reinterpret_cast<const v4i*>(smem + aoff(i, (ks + 1) & 3, sh));
+#pragma unroll
+      for (int j = 0; j < FT; ++j) fb[j] = *reinterpret_cast<const v4i*>(smem + boff(j, (ks + 1) & 3, sh));
+    }
+  }
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) s += acc[i][j][0] + acc[i][j][15];
+  out[(size_t)blockIdx.x * 512 + tid] = s;
+}
+
+// blocks workgroups of 512 threads; each of their 8 wavefronts issues
+// iters x 4 x 8 MFMAs; out: int32 [blocks * 512]. Returns 0, -1 or -4 as above.
+extern "C" __attribute__((visibility("default"))) int llmint8_bench_probe_mfma_i8_lds_random(
+    int blocks, int iters, int32_t* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out || (reinterpret_cast<uintptr_t>(out) & 3u) != 0) return -1;
+  hipLaunchKernelGGL(kp_mfma_i8_lds_random, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// ---------------------------------------------------------------------------
+// Streaming floor: a plain read of n16 16-byte pieces by 256-thread workgroups,
+// one piece per thread (the fastest launch shape measured for a 16.8 MB read),
+// folded into a value that is stored only if it equals a constant, so that the
+// loads are kept. And an empty kernel: the cost of a launch in a graph.
+__global__ __launch_bounds__(256) void kp_stream(const uint4* __restrict__ p, size_t n16, int32_t* out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const uint4 v = i < n16 ? p[i] : uint4{0, 0, 0, 0};
+  const uint32_t s = v.x ^ v.y ^ v.z ^ v.w;
+  if (s == 0x9e3779b9u) out[0] = (int32_t)s;
+}
+__global__ void kp_empty(int32_t* out) {
+  if (threadIdx.x == 64) out[0] = 0;  // never true: 64 threads
+}
+
+// p: device, n16 * 16 bytes, 16-byte aligned; out: int32 [1]. Returns 0, -1 or -4.
+extern "C" __attribute__((visibility("default"))) int llmint8_bench_probe_stream(const void* p, size_t n16,
+                                                                               int32_t* out, void* stream) {
+  if (!p || !out || n16 == 0 || (reinterpret_cast<uintptr_t>(p) & 15u) != 0) return -1;
+  const size_t blocks = (n16 + 255) / 256;
+  if (blocks > 0x7fffffffu) return -1;
+  hipLaunchKernelGGL(kp_stream, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(p), n16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+extern "C" __attribute__((visibility("default"))) int llmint8_bench_probe_empty(int32_t* out, void* stream) {
+  if (!out) return -1;
+  hipLaunchKernelGGL(kp_empty, dim3(256), dim3(64), 0, static_cast<hipStream_t>(stream), out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -176,8 +176,10 @@ LLMINT8_API llmint8_status llmint8_linear_timed(const void* X, int64_t T, int64_
  *   dY        [in]  fp16 [T, N], device (gradient of the layer output)
  *   Wq, sW    [in]  from llmint8_quantize_weight (int8 [N, K], fp32 [N])
  *   dX        [out] fp16 [T, K], device
- *   workspace [tmp] device, >= llmint8_backward_workspace_bytes(T, K, N)
- *                   bytes, 256-byte aligned; it receives Wdeq transposed
+ *   workspace [tmp] not used: one kernel dequantizes Wq into the 16-bit
+ *                   operand on the fly and keeps no copy of the weight
+ *                   (llmint8_backward_workspace_bytes returns 0; any pointer,
+ *                   NULL included, and size are accepted)
  * Requires, besides the forward's size limits, N % 8 == 0 and N <= 65536
  * (LLMINT8_ERR_UNSUPPORTED otherwise). T == 0 is a valid no-op. Results are
  * exact for the dequantization and within fp32 summation order for dX.
@@ -190,9 +192,8 @@ LLMINT8_API llmint8_status llmint8_linear_backward_input(const void* dY, int64_t
 
 /*
  * llmint8_linear_backward_input recording caller-created HIP events on the
- * stream: events[0] before the dequantization kernel, events[1] between the
- * two kernels, events[2] after the GEMM (n_events >= 3). *kernels_launched
- * (host int, may be NULL) receives 2.
+ * stream: events[0] before its kernel, events[1] after it (n_events >= 2).
+ * *kernels_launched (host int, may be NULL) receives 1.
  */
 LLMINT8_API llmint8_status llmint8_linear_backward_input_timed(
     const void* dY, int64_t T, int64_t K, const int8_t* Wq, const float* sW, int64_t N, void* dX,

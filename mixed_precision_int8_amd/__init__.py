@@ -457,8 +457,9 @@ def _backward_args(dY, Wq, sW, dX, workspace, dtype=None):
         dX = torch.empty((T, K), dtype=dtype, device=dY.device)
     _need(dX, dtype, (T, K), "dX")
     if workspace is None:
-        need = llmint8_backward_workspace_bytes(T, K, N)
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dY.device)
+        need = llmint8_backward_workspace_bytes(T, K, N)   # 0: the weight is dequantized on the fly
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=dY.device)
     return T, K, N, dX, workspace
 
 

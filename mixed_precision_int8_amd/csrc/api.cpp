@@ -191,28 +191,24 @@ llmint8_status run_linear(const void* X, int64_t T, int64_t K, const int8_t* Wq,
   return hip_status(e);
 }
 
-// WdT and dY rows (2N bytes) are copied in whole 16-byte pieces, and a tile's
+// dY rows and WdT rows (2N bytes) are copied in whole 16-byte pieces, and a tile's
 // rows x 2N bytes must stay within one buffer window
 llmint8_status check_backward_sizes(int64_t T, int64_t K, int64_t N) { return admit_backward(T, K, N); }
 
-size_t backward_workspace(int64_t K, int64_t N) { return align_up((size_t)2 * N * K, kWsAlign); }
-
-// dX = dY . Wdeq: dequantize-transpose into the workspace, then the 16-bit GEMM.
+// dX = dY . Wdeq in one kernel (Wq dequantized on the fly); no workspace.
 llmint8_status run_backward_input(const void* dY, int64_t T, int64_t K, const int8_t* Wq,
-                                  const float* sW, int64_t N, void* dX, void* workspace,
-                                  size_t workspace_bytes, void* stream_ptr, void* const* events,
-                                  int n_events, int* kernels_launched,
+                                  const float* sW, int64_t N, void* dX, void* stream_ptr,
+                                  void* const* events, int n_events, int* kernels_launched,
                                   int dtype = LLMINT8_DTYPE_F16) {
   if (kernels_launched) *kernels_launched = 0;
   llmint8_status st = check_backward_sizes(T, K, N);
   if (st != LLMINT8_OK) return st;
   if (dtype != LLMINT8_DTYPE_F16 && dtype != LLMINT8_DTYPE_BF16) return LLMINT8_ERR_INVALID_ARG;
   if (!Wq || !sW || !aligned(Wq, 16) || !aligned(sW, 4)) return LLMINT8_ERR_INVALID_ARG;
-  if (events && n_events < 3) return LLMINT8_ERR_INVALID_ARG;
+  if (events && n_events < 2) return LLMINT8_ERR_INVALID_ARG;
   if (T == 0) return LLMINT8_OK;
-  if (!dY || !dX || !workspace) return LLMINT8_ERR_INVALID_ARG;
-  if (!aligned(dY, 16) || !aligned(dX, 16) || !aligned(workspace, kWsAlign)) return LLMINT8_ERR_INVALID_ARG;
-  if (workspace_bytes < backward_workspace(K, N)) return LLMINT8_ERR_WORKSPACE;
+  if (!dY || !dX) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned(dY, 16) || !aligned(dX, 16)) return LLMINT8_ERR_INVALID_ARG;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   auto mark = [&](int i) -> hipError_t {
@@ -220,20 +216,18 @@ llmint8_status run_backward_input(const void* dY, int64_t T, int64_t K, const in
   };
   BwdArgs a{};
   a.dY = static_cast<const uint16_t*>(dY);
-  a.WdT = static_cast<uint16_t*>(workspace);
+  a.Wq = Wq;
+  a.sW = sW;
   a.dX = static_cast<uint16_t*>(dX);
   a.T = (int)T;
   a.K = (int)K;
   a.N = (int)N;
   a.bf16 = dtype == LLMINT8_DTYPE_BF16 ? 1 : 0;
   hipError_t e = mark(0);
-  if (e == hipSuccess)
-    e = launch_dequant_t(Wq, sW, (int)N, (int)K, static_cast<uint16_t*>(workspace), a.bf16 != 0, stream);
+  if (e == hipSuccess) e = launch_backward_dq(a, device_cu_count(), stream);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) e = launch_gemm_f16(a, device_cu_count(), stream);
-  if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return hip_status(e);
-  if (kernels_launched) *kernels_launched = 2;
+  if (kernels_launched) *kernels_launched = 1;
   return LLMINT8_OK;
 }
 
@@ -351,8 +345,10 @@ llmint8_status llmint8_linear_timed(const void* X, int64_t T, int64_t K, const i
 }
 
 size_t llmint8_backward_workspace_bytes(int64_t T, int64_t K, int64_t N) {
-  if (check_backward_sizes(T, K, N) != LLMINT8_OK) return 0;
-  return backward_workspace(K, N);
+  (void)T;
+  (void)K;
+  (void)N;
+  return 0;  // the weight is dequantized on the fly; nothing is staged in memory
 }
 
 llmint8_status llmint8_dequantize_weight_t_ex(const int8_t* Wq, const float* sW, int64_t N,
@@ -375,15 +371,17 @@ llmint8_status llmint8_linear_backward_input_ex(const void* dY, int dtype, int64
                                                 const int8_t* Wq, const float* sW, int64_t N,
                                                 void* dX, void* workspace, size_t workspace_bytes,
                                                 void* stream) {
-  return run_backward_input(dY, T, K, Wq, sW, N, dX, workspace, workspace_bytes, stream, nullptr, 0,
-                            nullptr, dtype);
+  (void)workspace;
+  (void)workspace_bytes;
+  return run_backward_input(dY, T, K, Wq, sW, N, dX, stream, nullptr, 0, nullptr, dtype);
 }
 
 llmint8_status llmint8_linear_backward_input(const void* dY, int64_t T, int64_t K, const int8_t* Wq,
                                              const float* sW, int64_t N, void* dX, void* workspace,
                                              size_t workspace_bytes, void* stream) {
-  return run_backward_input(dY, T, K, Wq, sW, N, dX, workspace, workspace_bytes, stream, nullptr, 0,
-                            nullptr);
+  (void)workspace;
+  (void)workspace_bytes;
+  return run_backward_input(dY, T, K, Wq, sW, N, dX, stream, nullptr, 0, nullptr);
 }
 
 llmint8_status llmint8_linear_backward_input_timed(const void* dY, int64_t T, int64_t K,
@@ -391,11 +389,12 @@ llmint8_status llmint8_linear_backward_input_timed(const void* dY, int64_t T, in
                                                    void* dX, void* workspace, size_t workspace_bytes,
                                                    void* stream, void* const* events, int n_events,
                                                    int* kernels_launched) {
-  if (!events || n_events < 3) return LLMINT8_ERR_INVALID_ARG;
-  for (int i = 0; i < 3; ++i)
+  if (!events || n_events < 2) return LLMINT8_ERR_INVALID_ARG;
+  for (int i = 0; i < 2; ++i)
     if (!events[i]) return LLMINT8_ERR_INVALID_ARG;
-  return run_backward_input(dY, T, K, Wq, sW, N, dX, workspace, workspace_bytes, stream, events,
-                            n_events, kernels_launched);
+  (void)workspace;
+  (void)workspace_bytes;
+  return run_backward_input(dY, T, K, Wq, sW, N, dX, stream, events, n_events, kernels_launched);
 }
 
 static llmint8_status check_blockwise(int dtype, int64_t n, int64_t block) {

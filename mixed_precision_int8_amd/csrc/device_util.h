@@ -128,6 +128,16 @@ struct Act16 {
     if constexpr (BF16) return float_to_bf16_bits(f);
     else return float_to_half_bits(f);
   }
+  // two values rounded to the type and packed, x0 in the low half
+  static __device__ __forceinline__ uint32_t pack2(float x0, float x1) {
+    if constexpr (BF16) {
+      typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+      return __builtin_bit_cast(uint32_t, v2{(__bf16)x0, (__bf16)x1});
+    } else {
+      typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+      return __builtin_bit_cast(uint32_t, v2{(_Float16)x0, (_Float16)x1});
+    }
+  }
   static __device__ __forceinline__ uint2 quantize8(const uint4& v, float s, uint32_t m0, uint32_t m1) {
     if constexpr (BF16) return quantize8_masked_bf16(v, s, m0, m1);
     else return quantize8_masked(v, s, m0, m1);

@@ -109,11 +109,11 @@ struct LinearArgs {
   int32_t* dbg_C;
 };
 
-// Operands of the input gradient dX = dY . Wdeq (WdT: the dequantized weight,
-// transposed, in the workspace).
+// Operands of the input gradient dX = dY . Wdeq.
 struct BwdArgs {
   const uint16_t* dY;  // 16-bit [T, N]
-  const uint16_t* WdT; // 16-bit [K, N]
+  const int8_t* Wq;    // int8 [N, K] and its scales [N] (dequantized on the fly)
+  const float* sW;
   uint16_t* dX;        // 16-bit [T, K]
   int T, K, N;
   int bf16;            // 16-bit type: 0 fp16, 1 bf16
@@ -143,8 +143,8 @@ int gemv_max_rows(int K);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uint16_t* WdT,
                             bool bf16, hipStream_t stream);
-hipError_t launch_gemm_f16(const BwdArgs& a, int num_cus, hipStream_t stream);
-hipError_t launch_gemm_f16_variant(const BwdArgs& a, int variant, hipStream_t stream);
+// dX = dY . Wdeq in one kernel, Wq dequantized into the 16-bit operand on the fly
+hipError_t launch_backward_dq(const BwdArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_quantize_blockwise(const void* x, bool f32, int n, int block, int8_t* q,
                                      float* absmax, int num_cus, hipStream_t stream);
 hipError_t launch_dequantize_blockwise(const int8_t* q, const float* absmax, int n, int block,

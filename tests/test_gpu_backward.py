@@ -4,7 +4,11 @@ Called through the C ABI and compared with the CPU oracle on the same seeded
 inputs: the dequantized, transposed weight bit-exact; dX within
 max-abs-relative 1e-3 (fp32 summation order is not pinned). Small and ragged
 shapes compare every element; the prefill-sized backward compares a seeded
-sample of rows.
+sample of rows. The input gradient forms the dequantized weight on the fly,
+inside its GEMM; with a one-hot output gradient (dY[t, n] = 1 for one n per
+row) each row of dX is a row of that operand exactly (one product by 1, an
+exact fp32 sum and an exact rounding), which checks the on-the-fly
+dequantization bit for bit.
 """
 from __future__ import annotations
 
@@ -72,6 +76,25 @@ def test_dequantize_transposed_prefill_weight_bit_exact():
     assert np.array_equal(WdT.view(np.uint16), ref.view(np.uint16))
 
 
+@pytest.mark.parametrize("N,K,dtype", [(520, 272, "f16"), (1000, 1040, "f16"), (72, 16, "f16"),
+                                       (2056, 4112, "bf16"), (11008, 4096, "f16")])
+def test_on_the_fly_dequantization_bit_exact(N, K, dtype):
+    """dY one-hot over a permutation of the weight rows: dX row t = Wdeq row perm[t]."""
+    _say(f"backward one-hot N={N} K={K} {dtype}")
+    Wq, sW, Wq_ref, sW_ref = _weights(27, N, K)
+    rng = np.random.default_rng(N + K)
+    T = min(N, 2048)
+    perm = rng.permutation(N)[:T]
+    one = np.uint16(0x3C00 if dtype == "f16" else 0x3F80)      # 1.0 in fp16 / bf16
+    dY = np.zeros((T, N), np.uint16)
+    dY[np.arange(T), perm] = one
+    dYd = _dev(dY).view(torch.float16 if dtype == "f16" else torch.bfloat16)
+    dX = _host(m8.llmint8_linear_backward_input_ex(dYd, Wq, sW).view(torch.int16)).view(np.uint16)
+    ref = oracle.dequantize_weight(Wq_ref, sW_ref, dtype)
+    ref = ref.view(np.uint16) if ref.dtype != np.uint16 else ref
+    assert np.array_equal(dX, ref[perm]), "on-the-fly dequantized operand differs"
+
+
 @pytest.mark.parametrize("T,K,N", [(16, 1024, 1024), (37, 336, 200), (300, 512, 264),
                                    (1, 4096, 4096), (257, 144, 520), (5, 16, 8)])
 def test_backward_input_parity(T, K, N):
@@ -114,12 +137,12 @@ def test_backward_input_edge_cases():
     with pytest.raises(m8.Llmint8Error) as e:
         m8.llmint8_linear_backward_input(_dev(np.zeros((4, 60), np.float16)), Wq2, sW2)
     assert e.value.status == -2
-    # a workspace smaller than required
+    # no workspace is needed; one given is ignored
     small = torch.empty((256,), dtype=torch.uint8, device="cuda")
-    with pytest.raises(m8.Llmint8Error) as e:
-        m8.llmint8_linear_backward_input(_dev(np.zeros((4, 64), np.float16)), Wq, sW,
-                                         workspace=small)
-    assert e.value.status == -3
+    dY4 = _dev(workloads.make_output_grad(25, 4, 64))
+    a = _host(m8.llmint8_linear_backward_input(dY4, Wq, sW, workspace=small)).view(np.uint16)
+    b = _host(m8.llmint8_linear_backward_input(dY4, Wq, sW)).view(np.uint16)
+    assert np.array_equal(a, b)
     # a zero gradient gives an exact zero
     dX = _host(m8.llmint8_linear_backward_input(_dev(np.zeros((3, 64), np.float16)), Wq, sW))
     assert not np.any(dX.astype(np.float32))
@@ -165,6 +188,25 @@ def test_dequantize_transposed_bf16_bit_exact(N, K):
     WdT = _bf16_host(m8.llmint8_dequantize_weight_t_ex(Wq, sW, dtype=torch.bfloat16))
     ref = oracle.dequantize_weight(Wq_ref, sW_ref, "bf16").T
     assert np.array_equal(WdT, np.ascontiguousarray(ref))
+
+
+@pytest.mark.parametrize("N,K,dtype", [(520, 272, "f16"), (1000, 1040, "f16"), (72, 16, "f16"),
+                                       (2056, 4112, "bf16"), (11008, 4096, "f16")])
+def test_on_the_fly_dequantization_bit_exact(N, K, dtype):
+    """dY one-hot over a permutation of the weight rows: dX row t = Wdeq row perm[t]."""
+    _say(f"backward one-hot N={N} K={K} {dtype}")
+    Wq, sW, Wq_ref, sW_ref = _weights(27, N, K)
+    rng = np.random.default_rng(N + K)
+    T = min(N, 2048)
+    perm = rng.permutation(N)[:T]
+    one = np.uint16(0x3C00 if dtype == "f16" else 0x3F80)      # 1.0 in fp16 / bf16
+    dY = np.zeros((T, N), np.uint16)
+    dY[np.arange(T), perm] = one
+    dYd = _dev(dY).view(torch.float16 if dtype == "f16" else torch.bfloat16)
+    dX = _host(m8.llmint8_linear_backward_input_ex(dYd, Wq, sW).view(torch.int16)).view(np.uint16)
+    ref = oracle.dequantize_weight(Wq_ref, sW_ref, dtype)
+    ref = ref.view(np.uint16) if ref.dtype != np.uint16 else ref
+    assert np.array_equal(dX, ref[perm]), "on-the-fly dequantized operand differs"
 
 
 @pytest.mark.parametrize("T,K,N", [(16, 1024, 1024), (37, 336, 200), (300, 512, 264),

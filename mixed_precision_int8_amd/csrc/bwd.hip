@@ -96,18 +96,19 @@ hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uin
 //   Wdeq[n][k] = r16(fl32(fl32(Wq[n][k] * b[n]) * fl32(1/127)))
 //
 // A workgroup owns a 128 (k) x 256 (t) output tile; the reduction runs over n
-// in stages of 64 (128 bytes of 16-bit operand) through three LDS slots. Its
-// eight wavefronts have two roles, one of each on every SIMD:
-//   * four MFMA wavefronts (a 64 x 128 block each) read the operands of slot
-//     s % 3 and multiply on v_mfma_f32_32x32x16_{f16,bf16};
+// in stages of 64 (128 bytes of 16-bit operand). Stage s's dY rows sit in LDS
+// slot s % 4 of B, its dequantized weight in slot s % 2 of A (160 KB in all).
+// The eight wavefronts have two roles, one of each on every SIMD:
+//   * four MFMA wavefronts (a 64 x 128 block each) read stage s's operands and
+//     multiply on v_mfma_f32_32x32x16_{f16,bf16};
 //   * four producer wavefronts fill the slots: producer p copies 64 of the
-//     stage's dY rows (n contiguous) global -> LDS directly, two stages ahead,
-//     and loads weight rows n = 64 s + 16 p + r (r = 0..15), two columns per
-//     lane (the tile's 128 contiguous bytes of each row per instruction), with
-//     their scales, three stages ahead; one stage ahead of the MFMAs it
-//     dequantizes them and writes, for each column, 8 consecutive n as one
-//     16-byte piece of that column's LDS row (the transposition the MFMA
-//     operand needs, under the same XOR swizzle as the copied operand).
+//     stage's dY rows (n contiguous) global -> LDS directly, and loads weight
+//     rows n = 64 s + 16 p + r (r = 0..15), two columns per lane (the tile's
+//     128 contiguous bytes of each row per instruction), with their scales,
+//     both three stages ahead; one stage ahead of the MFMAs it dequantizes the
+//     rows and writes, for each column, 8 consecutive n as one 16-byte piece
+//     of that column's LDS row (the transposition the MFMA operand needs,
+//     under the same XOR swizzle as the copied operand).
 // On a SIMD the producer's VALU work thus runs beside the MFMA wavefront's
 // matrix instructions with no scheduling by the compiler. Every stage ends
 // with one workgroup barrier, the same number (1 + stages) in both roles.
@@ -120,9 +121,10 @@ hipError_t launch_dequant_t(const int8_t* Wq, const float* sW, int N, int K, uin
 struct DqTile {
   static constexpr int BN = 128, BT = 256;  // output tile: k columns x t rows
   static constexpr int BK = 128;            // bytes of the reduction per stage (64 n)
-  static constexpr int NSTAGE = 3;
-  static constexpr int A_BYTES = BN * BK, B_BYTES = BT * BK, STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = STAGE * NSTAGE;
+  static constexpr int A_SLOTS = 2, B_SLOTS = 4;
+  static constexpr int A_BYTES = BN * BK, B_BYTES = BT * BK;
+  static constexpr int B_BASE = A_SLOTS * A_BYTES;  // LDS: the A slots, then the B slots
+  static constexpr int LDS = B_BASE + B_SLOTS * B_BYTES;
   static constexpr int kThreads = 512;      // 4 MFMA + 4 producer wavefronts
   static constexpr int WN = 64, WT = 128;   // MFMA wavefront block
   static constexpr int FN = WN / 32, FT = WT / 32, KS = BK / 32;
@@ -130,7 +132,7 @@ struct DqTile {
   static constexpr int B_ISSUES = BT / RPB / 4;        // 1 KB copies per producer per stage
   static constexpr int ROWS_P = 16;                    // weight rows per producer per stage
   static constexpr int LOADS = ROWS_P + 1 + B_ISSUES;  // producer memory instructions per stage
-  static_assert(LDS <= 160 * 1024 && 2 * LOADS < 64, "LDS, vmcnt range");
+  static_assert(LDS <= 160 * 1024 && 2 * LOADS + 8 < 64, "LDS, vmcnt range");
   static_assert(4 * ROWS_P * 2 == BK && BN == 128, "4 producers x 16 rows = 64 n; 2 columns per lane");
 };
 
@@ -180,9 +182,9 @@ __global__ __launch_bounds__(DqTile::kThreads, 1) void kg_backward_dq(BwdArgs a,
     uint32_t offB[G::B_ISSUES];
 #pragma unroll
     for (int i = 0; i < G::B_ISSUES; ++i) offB[i] = (uint32_t)(((i * 4 + p) * G::RPB + pr) * Kb + kcB);
-    auto issue_b = [&](int slot, int kt) {
+    auto issue_b = [&](int kt) {
       const int kb = kt * G::BK;
-      char* sB = smem + slot * G::STAGE + G::A_BYTES;
+      char* sB = smem + G::B_BASE + (kt & (G::B_SLOTS - 1)) * G::B_BYTES;
       const bool in = kcB < Kb - kb;
 #pragma unroll
       for (int i = 0; i < G::B_ISSUES; ++i)
@@ -214,14 +216,14 @@ __global__ __launch_bounds__(DqTile::kThreads, 1) void kg_backward_dq(BwdArgs a,
       R.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, voffS, 0, 0));
     };
     // dequantize a set and write its 4 pieces (2 columns x 2 groups of 8 rows)
-    // into the A operand of slot `slot`: column c of lane l is LDS row 2 l + c,
+    // into the A operand of stage kt's slot: column c of lane l is LDS row 2 l + c,
     // rows 8 h .. 8 h + 7 of producer p are the logical chunk 2 p + h
-    auto convert_store = [&](const ARegs& R, int slot) {
+    auto convert_store = [&](const ARegs& R, int kt) {
       float b[G::ROWS_P];
 #pragma unroll
       for (int r = 0; r < G::ROWS_P; ++r)
         b[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R.b), r));
-      char* sA = smem + slot * G::STAGE;
+      char* sA = smem + (kt & (G::A_SLOTS - 1)) * G::A_BYTES;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int kr = 2 * lane + c;
@@ -239,43 +241,46 @@ __global__ __launch_bounds__(DqTile::kThreads, 1) void kg_backward_dq(BwdArgs a,
         }
       }
     };
-    // prologue: stage 0 complete in slot 0; stage 1's weight rows landed in S1;
-    // stage 1's dY rows and stage 2's weight rows in flight (the scheduling
-    // barriers keep the requests in this order, which the wait counts)
+    // prologue: stages 0..2 requested (weight rows, dY rows, in that order per
+    // stage; the scheduling barriers keep this order, which the wait counts),
+    // stage 0's weight operand formed once its rows and dY rows have landed
     load_a(S0, 0);
+    issue_b(0);
+    __builtin_amdgcn_sched_barrier(0);
     load_a(S1, 1);
-    issue_b(0, 0);
+    issue_b(1);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b(1, 1);
     load_a(S2, 2);
+    issue_b(2);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<G::LOADS>();  // all but issue_b(1, 1) and load_a(S2, 2)
+    wait_vmcnt<2 * G::LOADS>();  // stage 0's requests have landed
     convert_store(S0, 0);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     barrier_no_fence();
-    // Stage kt: slot (kt + 2) % 3 was last read in stage kt - 1 and the set
-    // `load` was converted in stage kt - 1. Request stage kt + 3's weight rows
-    // and stage kt + 2's dY rows, form stage kt + 1's weight operand from
-    // `conv` into slot (kt + 1) % 3, then wait for every request made before
-    // this stage (this stage's LOADS may stay in flight) and for the LDS writes.
-    auto stage = [&](int kt, int slot, const ARegs& conv, ARegs& load) {
-      const int slot1 = slot == 2 ? 0 : slot + 1, slot2 = slot == 0 ? 2 : slot - 1;
+    // Stage kt: on entry the MFMA wavefronts have finished stage kt - 1, so B
+    // slot (kt + 3) % 4 and A slot (kt + 1) % 2 are free, and the set `load`
+    // (stage kt's rows) was converted during stage kt - 1. Request stage
+    // kt + 3's weight rows (into `load`) and dY rows, form stage kt + 1's
+    // weight operand from `conv` (requested in stage kt - 2), then wait until
+    // stage kt + 1's dY rows have landed (every request before stage kt - 1:
+    // the LOADS of stages kt - 1 and kt may stay in flight) and for the LDS writes.
+    auto stage = [&](int kt, const ARegs& conv, ARegs& load) {
       load_a(load, kt + 3);
-      issue_b(slot2, kt + 2);
-      convert_store(conv, slot1);
+      issue_b(kt + 3);
+      convert_store(conv, kt + 1);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<G::LOADS>();
+      wait_vmcnt<2 * G::LOADS>();
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       barrier_no_fence();
     };
     int kt = 0;
     for (; kt + 3 <= KT; kt += 3) {
-      stage(kt, 0, S1, S0);
-      stage(kt + 1, 1, S2, S1);
-      stage(kt + 2, 2, S0, S2);
+      stage(kt, S1, S0);
+      stage(kt + 1, S2, S1);
+      stage(kt + 2, S0, S2);
     }
-    if (kt < KT) stage(kt, 0, S1, S0);
-    if (kt + 1 < KT) stage(kt + 1, 1, S2, S1);
+    if (kt < KT) stage(kt, S1, S0);
+    if (kt + 1 < KT) stage(kt + 1, S2, S1);
     wait_vmcnt<0>();  // the requests past the end (zeros into unused slots) have landed
     return;
   }
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(DqTile::kThreads, 1) void kg_backward_dq(BwdArgs a,
   for (int ks = 0; ks < G::KS; ++ks) {
     const int phys = (ks * 2 + fg) ^ fswz;
     aoff[ks] = (wn * G::WN + fi) * G::BK + phys * 16;
-    boff[ks] = G::A_BYTES + (wt * G::WT + fi) * G::BK + phys * 16;
+    boff[ks] = (wt * G::WT + fi) * G::BK + phys * 16;
   }
   typename Mma::acc_t acc[G::FN][G::FT];
 #pragma unroll
@@ -297,11 +302,11 @@ __global__ __launch_bounds__(DqTile::kThreads, 1) void kg_backward_dq(BwdArgs a,
 #pragma unroll
     for (int j = 0; j < G::FT; ++j) acc[i][j] = Mma::zero();
   struct Frags { v4i a[G::FN], b[G::FT]; };
-  auto read_frags = [&](Frags& f, const char* st, int ks) {
+  auto read_frags = [&](Frags& f, const char* sa, const char* sb, int ks) {
 #pragma unroll
-    for (int j = 0; j < G::FT; ++j) f.b[j] = *reinterpret_cast<const v4i*>(st + boff[ks] + j * 32 * G::BK);
+    for (int j = 0; j < G::FT; ++j) f.b[j] = *reinterpret_cast<const v4i*>(sb + boff[ks] + j * 32 * G::BK);
 #pragma unroll
-    for (int i = 0; i < G::FN; ++i) f.a[i] = *reinterpret_cast<const v4i*>(st + aoff[ks] + i * 32 * G::BK);
+    for (int i = 0; i < G::FN; ++i) f.a[i] = *reinterpret_cast<const v4i*>(sa + aoff[ks] + i * 32 * G::BK);
   };
   auto mfma = [&](const Frags& f) {
 #pragma unroll
@@ -309,22 +314,31 @@ __global__ __launch_bounds__(DqTile::kThreads, 1) void kg_backward_dq(BwdArgs a,
 #pragma unroll
       for (int j = 0; j < G::FT; ++j) acc[i][j] = Mma::run(f.a[i], f.b[j], acc[i][j]);
   };
-  barrier_no_fence();  // the producers' prologue: stage 0 in slot 0
-  int slot = 0;
+  barrier_no_fence();  // the producers' prologue: stage 0's operands
   for (int kt = 0; kt < KT; ++kt) {
-    const char* st = smem + slot * G::STAGE;
+    const char* sa = smem + (kt & (G::A_SLOTS - 1)) * G::A_BYTES;
+    const char* sb = smem + G::B_BASE + (kt & (G::B_SLOTS - 1)) * G::B_BYTES;
     Frags f0, f1;
-    read_frags(f0, st, 0);
-    read_frags(f1, st, 1);
+    read_frags(f0, sa, sb, 0);
+    read_frags(f1, sa, sb, 1);
     mfma(f0);
-    read_frags(f0, st, 2);
+    read_frags(f0, sa, sb, 2);
     mfma(f1);
-    read_frags(f1, st, 3);
+    read_frags(f1, sa, sb, 3);
     mfma(f0);
     mfma(f1);
+    // one k-step of fragments ahead: each k-step's reads follow the first two
+    // MFMAs of the k-step before
+    constexpr int FR = G::FN + G::FT, MF = G::FN * G::FT;
+    __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (ks + 1 < G::KS) __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MF - 2, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    barrier_no_fence();  // the MFMAs have their operands: every read of the slot is done
-    slot = slot == 2 ? 0 : slot + 1;
+    barrier_no_fence();  // the MFMAs have their operands: every read of the slots is done
   }
 
   // ---- epilogue: lane holds, for row t = lane&31, columns k = 8*q + 4*(lane>>5) + r

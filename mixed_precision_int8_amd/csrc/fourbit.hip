@@ -204,6 +204,52 @@ __device__ __forceinline__ uint32_t byte_x4(uint32_t w) {
   return r;
 }
 
+// byte SEL of w times 8 (one SDWA shift): the address of a pair table entry
+template <int SEL>
+__device__ __forceinline__ uint32_t byte_x8(uint32_t w) {
+  uint32_t r;
+  if constexpr (SEL == 0)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if constexpr (SEL == 1)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if constexpr (SEL == 2)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+
+// 8 codes (one word, two per byte, the even element in the low nibble) -> 8
+// 16-bit weights r16(fl32(value[code] * a)), as dequant8, with one lookup per
+// byte in the pair table: entry b holds value[b & 15] and value[b >> 4]
+template <bool BF16>
+__device__ __forceinline__ uint4 dequant8_pairs(uint32_t cw, float a, const v2f* lut2) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const uint32_t ad[4] = {byte_x8<0>(cw), byte_x8<1>(cw), byte_x8<2>(cw), byte_x8<3>(cw)};
+  const char* base = reinterpret_cast<const char*>(lut2);
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const v2f e = *reinterpret_cast<const v2f*>(base + ad[p]);
+    float lo = e.x * a;
+    float hi = e.y * a;
+    asm volatile("" : "+v"(lo), "+v"(hi));  // the fp32 products, then one rounding each
+    if constexpr (BF16) {
+      b2 v;
+      v.x = (__bf16)lo;
+      v.y = (__bf16)hi;
+      o[p] = __builtin_bit_cast(uint32_t, v);
+    } else {
+      h2 v;
+      v.x = (_Float16)lo;
+      v.y = (_Float16)hi;
+      o[p] = __builtin_bit_cast(uint32_t, v);
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint4 dequant8(uint32_t cw, float a, const float* lut) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -264,15 +310,13 @@ constexpr int kN4Unroll = 2;  // 128-column steps in flight per wavefront
 template <bool BF16>
 __global__ __launch_bounds__(kN4Waves * 64) void kn_gemv(FourBitArgs a, Code4 book) {
   using A16 = Act16<BF16>;
-  __shared__ float lut[16];
+  __shared__ v2f lut2[256];  // pair table: the two codes of a byte
   __shared__ float bias_l[16];
   __shared__ v4f part[kN4Waves][64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
-  if (tid == 0) {
-#pragma unroll
-    for (int c = 0; c < 16; ++c) lut[c] = book.value[c];
-  }
+  static_assert(kN4Waves * 64 >= 256, "one pair table entry per thread");
+  if (tid < 256) lut2[tid] = v2f{book.value[tid & 15], book.value[tid >> 4]};
   // the block's 16 bias values, staged before the main loop (read in the
   // epilogue they would hold registers through it)
   if (tid >= 64 && tid < 80) {
@@ -327,7 +371,7 @@ __global__ __launch_bounds__(kN4Waves * 64) void kn_gemv(FourBitArgs a, Code4 bo
     for (int u = 0; u < kN4Unroll; ++u) {
       const uint32_t c[4] = {b.cw[u].x, b.cw[u].y, b.cw[u].z, b.cw[u].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8<BF16>(c[j], b.sc[u], lut), b.xb[u][j], acc);
+      for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8_pairs<BF16>(c[j], b.sc[u], lut2), b.xb[u][j], acc);
     }
   };
   // written as load + compute per iteration; the compiler rotates the loop so

@@ -817,7 +817,7 @@ def main():
                          "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(flops / (gf_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
                          "traffic": committed_traffic(PROFILE_BWD_COUNTERS, BWD_SOURCES,
-                                                      "gemm_hbm_bytes_per_launch"),
+                                                      "backward_hbm_bytes_per_launch"),
                          "algorithmic_ops_per_launch": flops,
                          "algorithmic_bytes_per_launch": N * K + 4 * N + 2 * T * N + 2 * T * K,
                          "avg_launch_ms": round(gf_ms, 5)},

@@ -234,7 +234,10 @@ __device__ __forceinline__ uint4 dequant8_pairs(uint32_t cw, float a, const v2f*
     const v2f e = *reinterpret_cast<const v2f*>(base + ad[p]);
     float lo = e.x * a;
     float hi = e.y * a;
-    asm volatile("" : "+v"(lo), "+v"(hi));  // the fp32 products, then one rounding each
+    // the fp32 products, then one rounding each: the empty asm hides each product
+    // from the compiler, which would otherwise fold multiply and conversion into
+    // one singly-rounded instruction; not volatile, so the lookups still overlap
+    asm("" : "+v"(lo), "+v"(hi));
     if constexpr (BF16) {
       b2 v;
       v.x = (__bf16)lo;
@@ -265,7 +268,7 @@ __device__ __forceinline__ uint4 dequant8(uint32_t cw, float a, const float* lut
   for (int p = 0; p < 4; ++p) {
     float lo = *reinterpret_cast<const float*>(base + ae[p]) * a;
     float hi = *reinterpret_cast<const float*>(base + ao[p]) * a;
-    asm volatile("" : "+v"(lo), "+v"(hi));
+    asm("" : "+v"(lo), "+v"(hi));  // as in dequant8_pairs: keeps the fp32 product, schedules freely
     if constexpr (BF16) {
       b2 v;
       v.x = (__bf16)lo;
@@ -396,6 +399,124 @@ __global__ __launch_bounds__(kN4Waves * 64) void kn_gemv(FourBitArgs a, Code4 bo
   }
 }
 
+// The same linear with the workgroup's rows of X staged in LDS, for calls whose
+// X rows fit (min(T, 16) rows of K values in at most XLDS bytes). A wavefront
+// then holds only its weight codes across the memory latency, DEPTH steps of
+// them, and reads each step's X fragments from LDS just before its MFMAs;
+// holding X fragments in registers across the latency (kn_gemv) limits it to
+// two steps in flight. Eight wavefronts split K; two workgroups fit a CU. (A
+// 20 KB variant with six steps in flight and three workgroups per CU measured
+// no faster on one-row calls.)
+constexpr int kN4XWaves = 8;
+constexpr int kN4XLdsLarge = 64 * 1024;
+__host__ __device__ constexpr uint32_t n4x_pitch(int K) { return 2u * (uint32_t)K + 16u; }  // bytes per X row in LDS
+
+template <bool BF16, int XLDS, int DEPTH>
+__global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4 book) {
+  using A16 = Act16<BF16>;
+  constexpr int kN4Depth = DEPTH;      // 128-column steps of codes in flight per wavefront
+  constexpr int kN4XLds = XLDS;
+  __shared__ __attribute__((aligned(16))) char xs[kN4XLds];  // X rows, pitch n4x_pitch(K)
+  __shared__ v2f lut2[256];
+  __shared__ float bias_l[16];
+  __shared__ v4f part[kN4XWaves][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int K = a.K;
+  const int rows_t = min(16, a.T - t0);
+  const uint32_t pitch = n4x_pitch(K);
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t row_bytes = (uint32_t)K / 2;
+  const uint32_t nblocks = (uint32_t)(((size_t)a.N * K + (1u << a.block_shift) - 1) >> a.block_shift);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W4, (uint32_t)a.N * row_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.absmax, nblocks * 4u);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + (size_t)t0 * K, (uint32_t)rows_t * (uint32_t)K * 2u);
+  const int n = n0 + r;
+  const bool wvalid = n < a.N;
+  const uint32_t wbase = (uint32_t)n * row_bytes + 16u * g;
+  const uint32_t ebase = (uint32_t)n * (uint32_t)K + 32u * g;
+  const int steps = K / 128;
+  const int per = (steps + kN4XWaves - 1) / kN4XWaves;
+  const int s0 = min(steps, wave * per), s1 = min(steps, s0 + per);
+
+  // 1. X rows: 16-byte pieces, loaded before the codes so that writing them to
+  // LDS waits for these loads only
+  const int xpieces = rows_t * (K / 8);  // K % 16 == 0
+  constexpr int kXPer = (kN4XLds / 16 + kN4XWaves * 64 - 1) / (kN4XWaves * 64);  // pieces per thread at most
+  uint4 xv[kXPer];
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int e = i * kN4XWaves * 64 + tid;
+    const int tr = e / (K / 8), c = e - tr * (K / 8);
+    xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rx, e < xpieces ? (uint32_t)(tr * K + 8 * c) * 2u : kOobOffset, 0, 0));
+  }
+  // 2. the first kN4Depth steps of codes and block maxima (past s1: zeros)
+  uint4 cw[kN4Depth];
+  float sc[kN4Depth];
+  auto load_codes = [&](int u, int si) {
+    const bool ok = si < s1 && wvalid;
+    cw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wbase + 64u * si : kOobOffset, 0, 0));
+    sc[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                          ra, ok ? ((ebase + 128u * si) >> a.block_shift) * 4u : kOobOffset, 0, 0));
+  };
+#pragma unroll
+  for (int u = 0; u < kN4Depth; ++u) load_codes(u, s0 + u);
+  // 3. pair table, bias
+  if (tid < 256) lut2[tid] = v2f{book.value[tid & 15], book.value[tid >> 4]};
+  if (tid >= 256 && tid < 272) {
+    const int nb = n0 + tid - 256;
+    bias_l[tid - 256] = a.bias && nb < a.N ? A16::to_f32(a.bias[nb]) : 0.0f;
+  }
+  // 4. X into LDS (waits for the X loads; the code loads issued after them stay in flight)
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int e = i * kN4XWaves * 64 + tid;
+    if (e < xpieces) {
+      const int tr = e / (K / 8), c = e - tr * (K / 8);
+      *reinterpret_cast<uint4*>(xs + tr * pitch + 16u * c) = xv[i];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): this thread's LDS writes
+  asm volatile("s_barrier" ::: "memory");  // no vmcnt wait: the code loads stay in flight
+
+  // 5. steps: lane (r, g) multiplies row n's codes for columns 128 s + 32 g + [0, 32)
+  // (word j: the k-slice of MFMA j) with row t0 + r of X there. Lanes of rows past
+  // T read the last row instead: output column r of the MFMA depends on that B
+  // row only, and columns past T are never stored.
+  const char* xl = xs + min(r, rows_t - 1) * pitch + 64u * g;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int base = s0; base < s1; base += kN4Depth) {
+#pragma unroll
+    for (int u = 0; u < kN4Depth; ++u) {
+      const int si = base + u;
+      if (si < s1) {  // uniform
+        uint4 xf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xf[j] = *reinterpret_cast<const uint4*>(xl + 256u * si + 16u * j);
+        const uint32_t c[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8_pairs<BF16>(c[j], sc[u], lut2), xf[j], acc);
+      }
+      load_codes(u, si + kN4Depth);
+    }
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  // threads 0..255: output element (row 4 (l / 16) + v, column l % 16) of the
+  // 16 x 16 block, l = tid % 64, v = tid / 64; partial sums added in wave order
+  if (tid < 256) {
+    const int l = tid & 63, v = tid >> 6;
+    float y = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kN4XWaves; ++w) y += part[w][l][v];
+    const int nl = 4 * (l >> 4) + v;
+    const int nn = n0 + nl, tt = t0 + (l & 15);
+    if (nn < a.N && tt < a.T) a.Y[(size_t)tt * a.N + nn] = A16::from_f32(y + bias_l[nl]);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 namespace {
@@ -456,6 +577,14 @@ hipError_t launch_dequantize_4bit(const uint8_t* packed, const float* absmax, in
 
 hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, hipStream_t stream) {
   const dim3 grid((a.N + 15) / 16, (a.T + 15) / 16);
+  const size_t xbytes = (size_t)std::min(a.T, 16) * n4x_pitch(a.K);
+  if (xbytes <= (size_t)kN4XLdsLarge) {
+    if (bf16)
+      hipLaunchKernelGGL((kn_gemv_x<true, kN4XLdsLarge, 4>), grid, dim3(kN4XWaves * 64), 0, stream, a, book);
+    else
+      hipLaunchKernelGGL((kn_gemv_x<false, kN4XLdsLarge, 4>), grid, dim3(kN4XWaves * 64), 0, stream, a, book);
+    return hipGetLastError();
+  }
   if (bf16) {
     hipLaunchKernelGGL(kn_gemv<true>, grid, dim3(kN4Waves * 64), 0, stream, a, book);
   } else {

@@ -744,13 +744,13 @@ def main():
         big = fb.get("large_layer_T1")
         rl = None
         if big:
-            rl = roofline("hbm", "kn_gemv (large layer, T = 1)", big["GB_per_s"], PEAK_HBM_GBS, "GB/s",
+            rl = roofline("hbm", "kn_gemv_x (large layer, T = 1; X rows in LDS)", big["GB_per_s"], PEAK_HBM_GBS, "GB/s",
                           committed_traffic(PROFILE_NEXT_COUNTERS, NEXT_SOURCES,
                                             "nf4_large_hbm_bytes_per_launch"),
                           algorithmic_bytes_per_launch=big["algorithmic_bytes"],
                           avg_launch_us=big["us_per_call"])
         result["fourbit_nf4"] = {"workload": "NF4 weights, block 64, fp16 activations; the decode "
-                                             "and large layers", "kernel": "kn_gemv",
+                                             "and large layers", "kernel": "kn_gemv_x (X rows in LDS; kn_gemv where they do not fit)",
                                  "bound": "hbm", "peak_GB_per_s": PEAK_HBM_GBS,
                                  "timing": "whole calls (one kernel each) between two events",
                                  "roofline": rl, **fb}

@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kN4Waves * 64) void kn_gemv(FourBitArgs a, Code4 bo
 // 20 KB variant with six steps in flight and three workgroups per CU measured
 // no faster on one-row calls.)
 constexpr int kN4XWaves = 8;
-constexpr int kN4XLdsLarge = 64 * 1024;
+constexpr int kN4XLdsLarge = 64 * 1024 + 16 * 16;  // 64 KB of X values plus 16 rows of padding
 __host__ __device__ constexpr uint32_t n4x_pitch(int K) { return 2u * (uint32_t)K + 16u; }  // bytes per X row in LDS
 
 template <bool BF16, int XLDS, int DEPTH>

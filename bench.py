@@ -750,7 +750,7 @@ def main():
                           algorithmic_bytes_per_launch=big["algorithmic_bytes"],
                           avg_launch_us=big["us_per_call"])
         result["fourbit_nf4"] = {"workload": "NF4 weights, block 64, fp16 activations; the decode "
-                                             "and large layers", "kernel": "kn_gemv_x (X rows in LDS; kn_gemv where they do not fit)",
+                                             "and large layers", "kernel": "kn_gemv_x (X rows staged in LDS by chunks of K)",
                                  "bound": "hbm", "peak_GB_per_s": PEAK_HBM_GBS,
                                  "timing": "whole calls (one kernel each) between two events",
                                  "roofline": rl, **fb}

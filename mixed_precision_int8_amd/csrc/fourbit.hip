@@ -22,10 +22,10 @@
 // nibble. Dequantization: r16(fl32(value[code] * a)) in the 16-bit compute type.
 //
 // The linear Y = X . Wdeq^T (+ bias) streams the codes once: a workgroup owns
-// 16 weight rows and its 16 wavefronts split K. Each lane loads 16 bytes of codes
+// 16 weight rows and its 8 wavefronts split K. Each lane loads 16 bytes of codes
 // (32 codes of one row, one block) per 128-column step, dequantizes them through
-// a 16-entry table in LDS and feeds v_mfma_f32_16x16x32_{f16,bf16} with the
-// weight rows as A and up to 16 rows of X (read straight from L2) as B. The
+// a pair table in LDS and feeds v_mfma_f32_16x16x32_{f16,bf16} with the weight
+// rows as A and up to 16 rows of X (staged in LDS by chunks of K) as B. The
 // partial sums are added in a fixed order through LDS, the bias is added and Y
 // is rounded once.
 #include <algorithm>
@@ -305,201 +305,114 @@ __global__ __launch_bounds__(256) void kdq4_blockwise(const uint8_t* __restrict_
 
 // ------------------------------------------------------------------ the 4-bit linear
 
-constexpr int kN4Waves = 16;  // wavefronts per workgroup, splitting K
-constexpr int kN4Unroll = 2;  // 128-column steps in flight per wavefront
-// Two 1024-thread workgroups per CU need at most 64 VGPRs per lane (8 waves
-// per SIMD); at 65 or more only one fits and the kernel runs ~40% slower.
+// The 4-bit linear. A workgroup of 8 wavefronts owns 16 weight rows and up to
+// 16 rows of X; K is walked in chunks whose X rows fit in LDS (kN4XLds bytes:
+// K = 32768 at T = 1, 4096 at T = 8, 2048 at T = 16 per chunk). Per chunk the
+// workgroup loads the chunk's X rows, then each wavefront its first DEPTH steps
+// of codes, and writes X into LDS; the wavefronts split the chunk's 128-column
+// steps, read each step's X fragments from LDS just before its MFMAs and keep
+// DEPTH steps of codes in flight. Only codes are held across the memory
+// latency (5 registers per step), which is what allows DEPTH steps in flight;
+// X fragments held in registers (21 per step) would allow two.
+constexpr int kN4XWaves = 8;
+constexpr int kN4XLds = 64 * 1024 + 16 * 16;  // 64 KB of X values plus 16 rows of padding
+constexpr int kN4Depth = 4;                   // 128-column steps of codes in flight per wavefront
+// columns of X per chunk for `rows` rows: a multiple of 128 with rows x (2 KC + 16) bytes in LDS
+__host__ __device__ constexpr int n4x_chunk_cols(int rows) { return ((kN4XLds / rows - 16) / 2) / 128 * 128; }
 
 template <bool BF16>
-__global__ __launch_bounds__(kN4Waves * 64) void kn_gemv(FourBitArgs a, Code4 book) {
+__global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4 book, int KC) {
   using A16 = Act16<BF16>;
-  __shared__ v2f lut2[256];  // pair table: the two codes of a byte
-  __shared__ float bias_l[16];
-  __shared__ v4f part[kN4Waves][64];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
-  static_assert(kN4Waves * 64 >= 256, "one pair table entry per thread");
-  if (tid < 256) lut2[tid] = v2f{book.value[tid & 15], book.value[tid >> 4]};
-  // the block's 16 bias values, staged before the main loop (read in the
-  // epilogue they would hold registers through it)
-  if (tid >= 64 && tid < 80) {
-    const int nb = n0 + tid - 64;
-    bias_l[tid - 64] = a.bias && nb < a.N ? A16::to_f32(a.bias[nb]) : 0.0f;
-  }
-  const int r = lane & 15, g = lane >> 4;
-  const int K = a.K;
-  const uint32_t row_bytes = (uint32_t)K / 2;
-  const uint32_t nblocks = (uint32_t)(((size_t)a.N * K + (1u << a.block_shift) - 1) >> a.block_shift);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W4, (uint32_t)a.N * row_bytes);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.absmax, nblocks * 4u);
-  // X: the workgroup's 16 rows only (linear4_x_window_bytes <= 2^31 for K <= kLinear4MaxK)
-  const __amdgpu_buffer_rsrc_t rx =
-      make_rsrc(a.X + (size_t)t0 * K, (uint32_t)min(16, a.T - t0) * (uint32_t)K * 2u);
-  const int n = n0 + r, t = t0 + r;
-  const bool wvalid = n < a.N, xvalid = t < a.T;
-  // lane (r, g) of step s holds row n's codes for columns 128 s + 32 g + [0, 32)
-  // (word j: columns + 8 j + [0, 8), the k-slice of MFMA j) and row t's X there
-  const uint32_t wbase = (uint32_t)n * row_bytes + 16u * g;
-  const uint32_t ebase = (uint32_t)n * (uint32_t)K + 32u * g;
-  const uint32_t xbase = ((uint32_t)r * (uint32_t)K + 32u * g) * 2u;
-  const int steps = K / 128;
-  const int per = (steps + kN4Waves - 1) / kN4Waves;
-  const int s0 = min(steps, wave * per), s1 = min(steps, s0 + per);
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  __syncthreads();
-  struct Steps {
-    uint4 cw[kN4Unroll];     // codes
-    float sc[kN4Unroll];     // block maxima
-    uint4 xb[kN4Unroll][4];  // X fragments
-  };
-  auto load = [&](Steps& b, int s) {
-#pragma unroll
-    for (int u = 0; u < kN4Unroll; ++u) {
-      const int si = s + u;
-      const bool ok = si < s1;
-      b.cw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rw, ok && wvalid ? wbase + 64u * si : kOobOffset, 0, 0));
-      b.sc[u] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(
-                     ra, ok && wvalid ? ((ebase + 128u * si) >> a.block_shift) * 4u : kOobOffset, 0, 0));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b.xb[u][j] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rx, ok && xvalid ? xbase + 256u * si + 16u * j : kOobOffset, 0, 0));
-    }
-  };
-  auto compute = [&](const Steps& b) {
-#pragma unroll
-    for (int u = 0; u < kN4Unroll; ++u) {
-      const uint32_t c[4] = {b.cw[u].x, b.cw[u].y, b.cw[u].z, b.cw[u].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8_pairs<BF16>(c[j], b.sc[u], lut2), b.xb[u][j], acc);
-    }
-  };
-  // written as load + compute per iteration; the compiler rotates the loop so
-  // that the next iteration's loads are issued before this one's arithmetic
-  for (int s = s0; s < s1; s += kN4Unroll) {
-    Steps b;
-    load(b, s);
-    compute(b);
-  }
-  part[wave][lane] = acc;
-  __syncthreads();
-  // threads 0..255: output element (row 4 (l / 16) + v, column l % 16) of the
-  // 16 x 16 block, l = tid % 64, v = tid / 64; partial sums added in wave order
-  for (int e = tid; e < 256; e += kN4Waves * 64) {
-    const int l = e & 63, v = e >> 6;
-    float y = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kN4Waves; ++w) y += part[w][l][v];
-    const int nl = 4 * (l >> 4) + v;
-    const int nn = n0 + nl, tt = t0 + (l & 15);
-    if (nn < a.N && tt < a.T) a.Y[(size_t)tt * a.N + nn] = A16::from_f32(y + bias_l[nl]);
-  }
-}
-
-// The same linear with the workgroup's rows of X staged in LDS, for calls whose
-// X rows fit (min(T, 16) rows of K values in at most XLDS bytes). A wavefront
-// then holds only its weight codes across the memory latency, DEPTH steps of
-// them, and reads each step's X fragments from LDS just before its MFMAs;
-// holding X fragments in registers across the latency (kn_gemv) limits it to
-// two steps in flight. Eight wavefronts split K; two workgroups fit a CU. (A
-// 20 KB variant with six steps in flight and three workgroups per CU measured
-// no faster on one-row calls.)
-constexpr int kN4XWaves = 8;
-constexpr int kN4XLdsLarge = 64 * 1024 + 16 * 16;  // 64 KB of X values plus 16 rows of padding
-__host__ __device__ constexpr uint32_t n4x_pitch(int K) { return 2u * (uint32_t)K + 16u; }  // bytes per X row in LDS
-
-template <bool BF16, int XLDS, int DEPTH>
-__global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4 book) {
-  using A16 = Act16<BF16>;
-  constexpr int kN4Depth = DEPTH;      // 128-column steps of codes in flight per wavefront
-  constexpr int kN4XLds = XLDS;
-  __shared__ __attribute__((aligned(16))) char xs[kN4XLds];  // X rows, pitch n4x_pitch(K)
-  __shared__ v2f lut2[256];
+  __shared__ __attribute__((aligned(16))) char xs[kN4XLds];  // a chunk of X rows, pitch 2 KC + 16 bytes
+  __shared__ v2f lut2[256];                                   // pair table: the two codes of a byte
   __shared__ float bias_l[16];
   __shared__ v4f part[kN4XWaves][64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
   const int K = a.K;
   const int rows_t = min(16, a.T - t0);
-  const uint32_t pitch = n4x_pitch(K);
+  const uint32_t pitch = 2u * (uint32_t)KC + 16u;  // rows on different banks
   const int r = lane & 15, g = lane >> 4;
   const uint32_t row_bytes = (uint32_t)K / 2;
   const uint32_t nblocks = (uint32_t)(((size_t)a.N * K + (1u << a.block_shift) - 1) >> a.block_shift);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W4, (uint32_t)a.N * row_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.absmax, nblocks * 4u);
+  // X: the workgroup's 16 rows only (linear4_x_window_bytes <= 2^31 for K <= kLinear4MaxK)
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + (size_t)t0 * K, (uint32_t)rows_t * (uint32_t)K * 2u);
   const int n = n0 + r;
   const bool wvalid = n < a.N;
+  // lane (r, g) of step s holds row n's codes for columns 128 s + 32 g + [0, 32)
+  // (word j: columns + 8 j + [0, 8), the k-slice of MFMA j) and row t0 + r of X there
   const uint32_t wbase = (uint32_t)n * row_bytes + 16u * g;
   const uint32_t ebase = (uint32_t)n * (uint32_t)K + 32u * g;
-  const int steps = K / 128;
-  const int per = (steps + kN4XWaves - 1) / kN4XWaves;
-  const int s0 = min(steps, wave * per), s1 = min(steps, s0 + per);
+  constexpr int kXPer = (kN4XLds / 16 + kN4XWaves * 64 - 1) / (kN4XWaves * 64);  // X pieces per thread at most
 
-  // 1. X rows: 16-byte pieces, loaded before the codes so that writing them to
-  // LDS waits for these loads only
-  const int xpieces = rows_t * (K / 8);  // K % 16 == 0
-  constexpr int kXPer = (kN4XLds / 16 + kN4XWaves * 64 - 1) / (kN4XWaves * 64);  // pieces per thread at most
-  uint4 xv[kXPer];
-#pragma unroll
-  for (int i = 0; i < kXPer; ++i) {
-    const int e = i * kN4XWaves * 64 + tid;
-    const int tr = e / (K / 8), c = e - tr * (K / 8);
-    xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rx, e < xpieces ? (uint32_t)(tr * K + 8 * c) * 2u : kOobOffset, 0, 0));
-  }
-  // 2. the first kN4Depth steps of codes and block maxima (past s1: zeros)
-  uint4 cw[kN4Depth];
-  float sc[kN4Depth];
-  auto load_codes = [&](int u, int si) {
-    const bool ok = si < s1 && wvalid;
-    cw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wbase + 64u * si : kOobOffset, 0, 0));
-    sc[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                          ra, ok ? ((ebase + 128u * si) >> a.block_shift) * 4u : kOobOffset, 0, 0));
-  };
-#pragma unroll
-  for (int u = 0; u < kN4Depth; ++u) load_codes(u, s0 + u);
-  // 3. pair table, bias
   if (tid < 256) lut2[tid] = v2f{book.value[tid & 15], book.value[tid >> 4]};
   if (tid >= 256 && tid < 272) {
     const int nb = n0 + tid - 256;
     bias_l[tid - 256] = a.bias && nb < a.N ? A16::to_f32(a.bias[nb]) : 0.0f;
   }
-  // 4. X into LDS (waits for the X loads; the code loads issued after them stay in flight)
-#pragma unroll
-  for (int i = 0; i < kXPer; ++i) {
-    const int e = i * kN4XWaves * 64 + tid;
-    if (e < xpieces) {
-      const int tr = e / (K / 8), c = e - tr * (K / 8);
-      *reinterpret_cast<uint4*>(xs + tr * pitch + 16u * c) = xv[i];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): this thread's LDS writes
-  asm volatile("s_barrier" ::: "memory");  // no vmcnt wait: the code loads stay in flight
-
-  // 5. steps: lane (r, g) multiplies row n's codes for columns 128 s + 32 g + [0, 32)
-  // (word j: the k-slice of MFMA j) with row t0 + r of X there. Lanes of rows past
-  // T read the last row instead: output column r of the MFMA depends on that B
-  // row only, and columns past T are never stored.
+  uint4 cw[kN4Depth];
+  float sc[kN4Depth];
+  // Lanes of rows past T read the last row of X instead: output column r of the
+  // MFMA depends on that B row only, and columns past T are never stored.
   const char* xl = xs + min(r, rows_t - 1) * pitch + 64u * g;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int base = s0; base < s1; base += kN4Depth) {
+  const int nck = (K + KC - 1) / KC;
+  for (int ck = 0; ck < nck; ++ck) {  // uniform
+    const int kc0 = ck * KC, cols = min(KC, K - kc0);
+    const int gs = kc0 / 128, nsc = cols / 128;  // first step of the chunk, its steps
+    const int per = (nsc + kN4XWaves - 1) / kN4XWaves;
+    const int s0 = min(nsc, wave * per), s1 = min(nsc, s0 + per);  // this wavefront's steps of the chunk
+    // (1) the chunk's X rows in 16-byte pieces, loaded before the codes so that
+    // writing them to LDS waits for these loads only
+    const int cpr = cols / 8, xpieces = rows_t * cpr;
+    uint4 xv[kXPer];
 #pragma unroll
-    for (int u = 0; u < kN4Depth; ++u) {
-      const int si = base + u;
-      if (si < s1) {  // uniform
-        uint4 xf[4];
+    for (int i = 0; i < kXPer; ++i) {
+      const int e = i * kN4XWaves * 64 + tid;
+      const int tr = e / cpr, c = e - tr * cpr;
+      xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rx, e < xpieces ? (uint32_t)(tr * K + kc0 + 8 * c) * 2u : kOobOffset, 0, 0));
+    }
+    // (2) the wavefront's first kN4Depth steps of codes and block maxima (past s1: zeros)
+    auto load_codes = [&](int u, int si) {
+      const bool ok = si < s1 && wvalid;
+      const uint32_t sg = (uint32_t)(gs + si);
+      cw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wbase + 64u * sg : kOobOffset, 0, 0));
+      sc[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            ra, ok ? ((ebase + 128u * sg) >> a.block_shift) * 4u : kOobOffset, 0, 0));
+    };
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xf[j] = *reinterpret_cast<const uint4*>(xl + 256u * si + 16u * j);
-        const uint32_t c[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+    for (int u = 0; u < kN4Depth; ++u) load_codes(u, s0 + u);
+    // (3) X into LDS once every wavefront has read the previous chunk's; the
+    // barriers wait for LDS only, so the code loads stay in flight
+    if (ck > 0) asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8_pairs<BF16>(c[j], sc[u], lut2), xf[j], acc);
+    for (int i = 0; i < kXPer; ++i) {
+      const int e = i * kN4XWaves * 64 + tid;
+      if (e < xpieces) {
+        const int tr = e / cpr, c = e - tr * cpr;
+        *reinterpret_cast<uint4*>(xs + tr * pitch + 16u * c) = xv[i];
       }
-      load_codes(u, si + kN4Depth);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's LDS writes
+    asm volatile("s_barrier" ::: "memory");
+    // (4) the steps, kN4Depth steps of codes in flight
+    for (int base = s0; base < s1; base += kN4Depth) {
+#pragma unroll
+      for (int u = 0; u < kN4Depth; ++u) {
+        const int si = base + u;
+        if (si < s1) {  // uniform
+          uint4 xf[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const uint4*>(xl + 256u * si + 16u * j);
+          const uint32_t c[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8_pairs<BF16>(c[j], sc[u], lut2), xf[j], acc);
+        }
+        load_codes(u, si + kN4Depth);
+      }
     }
   }
   part[wave][lane] = acc;
@@ -577,19 +490,11 @@ hipError_t launch_dequantize_4bit(const uint8_t* packed, const float* absmax, in
 
 hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, hipStream_t stream) {
   const dim3 grid((a.N + 15) / 16, (a.T + 15) / 16);
-  const size_t xbytes = (size_t)std::min(a.T, 16) * n4x_pitch(a.K);
-  if (xbytes <= (size_t)kN4XLdsLarge) {
-    if (bf16)
-      hipLaunchKernelGGL((kn_gemv_x<true, kN4XLdsLarge, 4>), grid, dim3(kN4XWaves * 64), 0, stream, a, book);
-    else
-      hipLaunchKernelGGL((kn_gemv_x<false, kN4XLdsLarge, 4>), grid, dim3(kN4XWaves * 64), 0, stream, a, book);
-    return hipGetLastError();
-  }
-  if (bf16) {
-    hipLaunchKernelGGL(kn_gemv<true>, grid, dim3(kN4Waves * 64), 0, stream, a, book);
-  } else {
-    hipLaunchKernelGGL(kn_gemv<false>, grid, dim3(kN4Waves * 64), 0, stream, a, book);
-  }
+  const int KC = std::min(a.K, n4x_chunk_cols(std::min(a.T, 16)));
+  if (bf16)
+    hipLaunchKernelGGL(kn_gemv_x<true>, grid, dim3(kN4XWaves * 64), 0, stream, a, book, KC);
+  else
+    hipLaunchKernelGGL(kn_gemv_x<false>, grid, dim3(kN4XWaves * 64), 0, stream, a, book, KC);
   return hipGetLastError();
 }
 

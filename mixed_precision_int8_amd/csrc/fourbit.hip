@@ -323,10 +323,19 @@ __host__ __device__ constexpr int n4x_chunk_cols(int rows) { return ((kN4XLds / 
 template <bool BF16>
 __global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4 book, int KC) {
   using A16 = Act16<BF16>;
-  __shared__ __attribute__((aligned(16))) char xs[kN4XLds];  // a chunk of X rows, pitch 2 KC + 16 bytes
-  __shared__ v2f lut2[256];                                   // pair table: the two codes of a byte
-  __shared__ float bias_l[16];
-  __shared__ v4f part[kN4XWaves][64];
+  // one LDS block with the pair table at offset 0: a lookup's address (byte x 8)
+  // is then the table entry's, with no add per lookup
+  struct Lds {
+    v2f lut2[256];                               // pair table: the two codes of a byte
+    float bias_l[16];
+    v4f part[kN4XWaves][64];
+    __attribute__((aligned(16))) char xs[kN4XLds];  // a chunk of X rows, pitch 2 KC + 16 bytes
+  };
+  __shared__ Lds lds;
+  v2f* const lut2 = lds.lut2;
+  float* const bias_l = lds.bias_l;
+  v4f (*const part)[64] = lds.part;
+  char* const xs = lds.xs;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
   const int K = a.K;

@@ -208,6 +208,96 @@ def test_repeat_calls_bit_identical():
     assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
 
 
+# --------------------------------------------------------------------------- workspace reuse
+
+def _check_stages(out, st, name):
+    count = int(_host(out["count"])[0])
+    assert count == st.count, (name, count, st.count)
+    assert np.array_equal(_host(out["bitmap"]).view(np.uint32), st.bitmap), name
+    assert np.array_equal(_host(out["idx"])[:count], st.idx), name
+    assert np.array_equal(_host(out["Xq"]), st.Xq), f"{name}: Xq differs"
+    assert np.array_equal(_host(out["aX"]).view(np.uint32), st.aX.view(np.uint32)), f"{name}: aX differs"
+    err = oracle.parity_error(_host(out["Y"]), st.Y)
+    assert err <= Y_TOL, f"{name}: Y parity error {err}"
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_forward_any_workspace_contents(fill):
+    """Whatever the workspace holds on entry, the stages are the oracle's: every
+    region a call reads (the scan's partial bitmaps included) is written by that
+    call first."""
+    T, K, N = 520, 2048, 300
+    W, X = _small(T, K, N, seed=61, n_out=5)
+    _say(f"workspace filled with {fill}: T={T} K={K} N={N}")
+    Wq, sW, Wq_ref, sW_ref = quantize_weight_checked(W)
+    st = oracle.linear(X, Wq_ref, sW_ref, 6.0)
+    nb = m8.llmint8_workspace_bytes(T, K, N)
+    if fill == "zeros":
+        ws = torch.zeros((nb,), dtype=torch.uint8, device="cuda")
+    elif fill == "ones":
+        ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    else:
+        ws = _dev(_rng(62).integers(0, 256, size=nb, dtype=np.uint8))
+    for rep in range(2):
+        out = m8.llmint8_linear_debug(_dev(X), Wq, sW, 6.0, path=GEMM, workspace=ws, want_C=False)
+        _check_stages(out, st, f"{fill} call {rep}")
+
+
+def test_forward_alternating_inputs_one_workspace():
+    """Calls in order on one workspace with inputs whose outlier columns differ:
+    no call takes anything (partial bitmaps, outlier operands) from an earlier one."""
+    T, K, N = 700, 1024, 200
+    W, X0 = _small(T, K, N, seed=71, n_out=4)
+    Xs = [X0] + [_small(T, K, N, seed=sd, n_out=4)[1] for sd in (72, 73)]
+    _say(f"alternating inputs: T={T} K={K} N={N}")
+    Wq, sW, Wq_ref, sW_ref = quantize_weight_checked(W)
+    sts = [oracle.linear(X, Wq_ref, sW_ref, 6.0) for X in Xs]
+    assert len({tuple(st.idx) for st in sts}) == 3
+    ws = torch.empty((m8.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        for i, (X, st) in enumerate(zip(Xs, sts)):
+            out = m8.llmint8_linear_debug(_dev(X), Wq, sW, 6.0, path=GEMM, workspace=ws, want_C=False)
+            _check_stages(out, st, f"input {i}, round {rep}")
+
+
+def test_forward_graph_replays_new_inputs():
+    """One call captured in a HIP graph and replayed with new data in the same X
+    buffer (copied in by eager work between replays): every replay decides the
+    outlier set of its own X, bit-identical to an eager call."""
+    T, K, N = 520, 2048, 300
+    W, X0 = _small(T, K, N, seed=81, n_out=5)
+    Xs = [X0] + [_small(T, K, N, seed=sd, n_out=5)[1] for sd in (82, 83)]
+    _say(f"graph replays: T={T} K={K} N={N}")
+    Wq, sW, Wq_ref, sW_ref = quantize_weight_checked(W)
+    sts = [oracle.linear(X, Wq_ref, sW_ref, 6.0) for X in Xs]
+    nb = m8.llmint8_workspace_bytes(T, K, N)
+    Xd = _dev(X0)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+    ws = torch.empty((nb,), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty((nb,), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m8.llmint8_linear(Xd, Wq, sW, 6.0, Y=Y, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        m8.llmint8_linear(Xd, Wq, sW, 6.0, Y=Y, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, (X, st) in enumerate(zip(Xs, sts)):
+            Xd.copy_(torch.from_numpy(X))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            Yg = _host(Y).copy()
+            Ye = _host(m8.llmint8_linear(Xd, Wq, sW, 6.0, workspace=ws2))
+            assert np.array_equal(Yg.view(np.uint16), Ye.view(np.uint16)), f"replay {rep}/{i} differs"
+            err = oracle.parity_error(Yg, st.Y)
+            assert err <= Y_TOL, f"replay {rep}/{i}: Y parity error {err}"
+    del g
+
+
 def test_int8linear_module_and_memory():
     """The layer holds its int8 weight and scales only; layers share one forward
     workspace per device and stream, and the fused decode route needs none."""

@@ -498,7 +498,7 @@ llmint8_status llmint8_linear_4bit(const void* X, int dtype, int64_t T, int64_t 
   a.K = (int)K;
   a.N = (int)N;
   a.block_shift = shift;
-  return hip_status(launch_linear_4bit(a, book, dtype == LLMINT8_DTYPE_BF16,
+  return hip_status(launch_linear_4bit(a, book, dtype == LLMINT8_DTYPE_BF16, device_cu_count(),
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -320,24 +320,25 @@ constexpr int kN4Depth = 4;                   // 128-column steps of codes in fl
 // columns of X per chunk for `rows` rows: a multiple of 128 with rows x (2 KC + 16) bytes in LDS
 __host__ __device__ constexpr int n4x_chunk_cols(int rows) { return ((kN4XLds / rows - 16) / 2) / 128 * 128; }
 
-template <bool BF16>
+template <bool BF16, int RB>
 __global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4 book, int KC) {
   using A16 = Act16<BF16>;
   // one LDS block with the pair table at offset 0: a lookup's address (byte x 8)
-  // is then the table entry's, with no add per lookup
+  // is then the table entry's, with no add per lookup. The partial sums reuse
+  // the X area once the last chunk's steps are done.
   struct Lds {
-    v2f lut2[256];                               // pair table: the two codes of a byte
-    float bias_l[16];
-    v4f part[kN4XWaves][64];
+    v2f lut2[256];                                  // pair table: the two codes of a byte
+    float bias_l[16 * RB];
     __attribute__((aligned(16))) char xs[kN4XLds];  // a chunk of X rows, pitch 2 KC + 16 bytes
   };
+  static_assert(kN4XWaves * RB * 64 * 16 <= kN4XLds, "partial sums fit the X area");
   __shared__ Lds lds;
   v2f* const lut2 = lds.lut2;
   float* const bias_l = lds.bias_l;
-  v4f (*const part)[64] = lds.part;
   char* const xs = lds.xs;
+  v4f (*const part)[RB][64] = reinterpret_cast<v4f (*)[RB][64]>(lds.xs);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int n0 = blockIdx.x * 16 * RB, t0 = blockIdx.y * 16;
   const int K = a.K;
   const int rows_t = min(16, a.T - t0);
   const uint32_t pitch = 2u * (uint32_t)KC + 16u;  // rows on different banks
@@ -348,25 +349,33 @@ __global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.absmax, nblocks * 4u);
   // X: the workgroup's 16 rows only (linear4_x_window_bytes <= 2^31 for K <= kLinear4MaxK)
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + (size_t)t0 * K, (uint32_t)rows_t * (uint32_t)K * 2u);
-  const int n = n0 + r;
-  const bool wvalid = n < a.N;
-  // lane (r, g) of step s holds row n's codes for columns 128 s + 32 g + [0, 32)
-  // (word j: columns + 8 j + [0, 8), the k-slice of MFMA j) and row t0 + r of X there
-  const uint32_t wbase = (uint32_t)n * row_bytes + 16u * g;
-  const uint32_t ebase = (uint32_t)n * (uint32_t)K + 32u * g;
+  // lane (r, g) of step s holds, for row block b, row n0 + 16 b + r's codes for
+  // columns 128 s + 32 g + [0, 32) (word j: columns + 8 j + [0, 8), the k-slice
+  // of MFMA j) and row t0 + r of X there; the X fragments serve all RB blocks
+  bool wvalid[RB];
+  uint32_t wbase[RB], ebase[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int n = n0 + 16 * b + r;
+    wvalid[b] = n < a.N;
+    wbase[b] = (uint32_t)n * row_bytes + 16u * g;
+    ebase[b] = (uint32_t)n * (uint32_t)K + 32u * g;
+  }
   constexpr int kXPer = (kN4XLds / 16 + kN4XWaves * 64 - 1) / (kN4XWaves * 64);  // X pieces per thread at most
 
   if (tid < 256) lut2[tid] = v2f{book.value[tid & 15], book.value[tid >> 4]};
-  if (tid >= 256 && tid < 272) {
+  if (tid >= 256 && tid < 256 + 16 * RB) {
     const int nb = n0 + tid - 256;
     bias_l[tid - 256] = a.bias && nb < a.N ? A16::to_f32(a.bias[nb]) : 0.0f;
   }
-  uint4 cw[kN4Depth];
-  float sc[kN4Depth];
+  uint4 cw[kN4Depth][RB];
+  float sc[kN4Depth][RB];
   // Lanes of rows past T read the last row of X instead: output column r of the
   // MFMA depends on that B row only, and columns past T are never stored.
   const char* xl = xs + min(r, rows_t - 1) * pitch + 64u * g;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f acc[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) acc[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const int nck = (K + KC - 1) / KC;
   for (int ck = 0; ck < nck; ++ck) {  // uniform
     const int kc0 = ck * KC, cols = min(KC, K - kc0);
@@ -386,11 +395,14 @@ __global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4
     }
     // (2) the wavefront's first kN4Depth steps of codes and block maxima (past s1: zeros)
     auto load_codes = [&](int u, int si) {
-      const bool ok = si < s1 && wvalid;
       const uint32_t sg = (uint32_t)(gs + si);
-      cw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wbase + 64u * sg : kOobOffset, 0, 0));
-      sc[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            ra, ok ? ((ebase + 128u * sg) >> a.block_shift) * 4u : kOobOffset, 0, 0));
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const bool ok = si < s1 && wvalid[b];
+        cw[u][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wbase[b] + 64u * sg : kOobOffset, 0, 0));
+        sc[u][b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 ra, ok ? ((ebase[b] + 128u * sg) >> a.block_shift) * 4u : kOobOffset, 0, 0));
+      }
     };
 #pragma unroll
     for (int u = 0; u < kN4Depth; ++u) load_codes(u, s0 + u);
@@ -416,24 +428,30 @@ __global__ __launch_bounds__(kN4XWaves * 64) void kn_gemv_x(FourBitArgs a, Code4
           uint4 xf[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const uint4*>(xl + 256u * si + 16u * j);
-          const uint32_t c[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc = A16::mma16(dequant8_pairs<BF16>(c[j], sc[u], lut2), xf[j], acc);
+          for (int b = 0; b < RB; ++b) {
+            const uint32_t c[4] = {cw[u][b].x, cw[u][b].y, cw[u][b].z, cw[u][b].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[b] = A16::mma16(dequant8_pairs<BF16>(c[j], sc[u][b], lut2), xf[j], acc[b]);
+          }
         }
         load_codes(u, si + kN4Depth);
       }
     }
   }
-  part[wave][lane] = acc;
+  __syncthreads();  // every wavefront is done with X: the partial sums take its area
+#pragma unroll
+  for (int b = 0; b < RB; ++b) part[wave][b][lane] = acc[b];
   __syncthreads();
-  // threads 0..255: output element (row 4 (l / 16) + v, column l % 16) of the
-  // 16 x 16 block, l = tid % 64, v = tid / 64; partial sums added in wave order
-  if (tid < 256) {
-    const int l = tid & 63, v = tid >> 6;
+  // thread -> output element (row 16 b + 4 (l / 16) + v, column l % 16) of the
+  // 16 RB x 16 block, l = tid % 64, v = (tid / 64) % 4, b = tid / 256; partial
+  // sums added in wave order
+  if (tid < 256 * RB) {
+    const int l = tid & 63, v = (tid >> 6) & 3, b = tid >> 8;
     float y = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kN4XWaves; ++w) y += part[w][l][v];
-    const int nl = 4 * (l >> 4) + v;
+    for (int w = 0; w < kN4XWaves; ++w) y += part[w][b][l][v];
+    const int nl = 16 * b + 4 * (l >> 4) + v;
     const int nn = n0 + nl, tt = t0 + (l & 15);
     if (nn < a.N && tt < a.T) a.Y[(size_t)tt * a.N + nn] = A16::from_f32(y + bias_l[nl]);
   }
@@ -497,13 +515,28 @@ hipError_t launch_dequantize_4bit(const uint8_t* packed, const float* absmax, in
   return hipGetLastError();
 }
 
-hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, hipStream_t stream) {
-  const dim3 grid((a.N + 15) / 16, (a.T + 15) / 16);
+hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, int num_cus,
+                              hipStream_t stream) {
   const int KC = std::min(a.K, n4x_chunk_cols(std::min(a.T, 16)));
-  if (bf16)
-    hipLaunchKernelGGL(kn_gemv_x<true>, grid, dim3(kN4XWaves * 64), 0, stream, a, book, KC);
-  else
-    hipLaunchKernelGGL(kn_gemv_x<false>, grid, dim3(kN4XWaves * 64), 0, stream, a, book, KC);
+  const dim3 block(kN4XWaves * 64);
+  // 32 weight rows per workgroup (each X fragment serves two MFMAs, each X chunk
+  // two row blocks) from 4 rows of X on, where the X staged per workgroup
+  // matters (at the 28672 x 8192 layer: T = 8 59.7-61.4 us against 63.3-63.9
+  // with 16 rows; T = 1 51-52 against 46-48, the wider workgroups filling the
+  // CUs in fewer, emptier rounds), if every CU still gets two workgroups
+  if (a.T >= 4 && (int64_t)ceil_div(a.N, 32) * ceil_div(a.T, 16) >= 2 * (int64_t)num_cus) {
+    const dim3 grid((a.N + 31) / 32, (a.T + 15) / 16);
+    if (bf16)
+      hipLaunchKernelGGL((kn_gemv_x<true, 2>), grid, block, 0, stream, a, book, KC);
+    else
+      hipLaunchKernelGGL((kn_gemv_x<false, 2>), grid, block, 0, stream, a, book, KC);
+  } else {
+    const dim3 grid((a.N + 15) / 16, (a.T + 15) / 16);
+    if (bf16)
+      hipLaunchKernelGGL((kn_gemv_x<true, 1>), grid, block, 0, stream, a, book, KC);
+    else
+      hipLaunchKernelGGL((kn_gemv_x<false, 1>), grid, block, 0, stream, a, book, KC);
+  }
   return hipGetLastError();
 }
 

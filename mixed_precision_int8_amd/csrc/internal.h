@@ -174,6 +174,7 @@ hipError_t launch_quantize_4bit(const uint16_t* w, bool bf16, int n, int block, 
 hipError_t launch_dequantize_4bit(const uint8_t* packed, const float* absmax, int n, int block,
                                   const Code4& book, uint16_t* out, bool bf16, int num_cus,
                                   hipStream_t stream);
-hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, hipStream_t stream);
+hipError_t launch_linear_4bit(const FourBitArgs& a, const Code4& book, bool bf16, int num_cus,
+                              hipStream_t stream);
 
 }  // namespace llmint8

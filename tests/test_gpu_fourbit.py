@@ -173,6 +173,20 @@ def test_linear_decode_workload(quant_type, dtype, T):
     linear_case("decode", _as(dtype, W), _as(dtype, X), 64, quant_type, dtype, bias=b)
 
 
+@pytest.mark.parametrize("quant_type", ["nf4", "fp4"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,N,block", [(20, 384, 8200, 64), (4, 1152, 16408, 128),
+                                         (17, 2048, 8232, 64), (17, 8320, 8200, 64)])
+def test_linear_two_row_blocks(quant_type, dtype, T, K, N, block):
+    """Shapes that take 32 weight rows per workgroup on a 256-CU device (T >= 4,
+    ceil(N/32) x ceil(T/16) >= 512): ragged N (a last workgroup with one row
+    block partly or wholly past N), T past 16, odd step counts and steps left
+    to some wavefronts only, with bias; every output against the oracle."""
+    W, X = _weights(T + K + N, N, K, 0.05), _acts(T + K + N + 1, T, K)
+    b = workloads.make_bias(N, N, bf16=dtype == "bf16")
+    linear_case("two row blocks", _as(dtype, W), _as(dtype, X), block, quant_type, dtype, bias=b)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_linear_large_layer_sampled_rows(dtype):
     w = workloads.CONFIGS["large"]

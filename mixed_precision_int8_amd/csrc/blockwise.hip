@@ -39,10 +39,20 @@ __device__ __forceinline__ uint32_t quantize4_f32(const uint4& v, float s) {
 // final rounding to fp32 is the correctly rounded quotient.
 __device__ __forceinline__ float div127(float p) { return (float)((double)p * (1.0 / 127.0)); }
 
+// Every code and every dequantized value is written once and not read again by
+// the kernel: the stores are non-temporal (their lines go to memory without
+// lingering in L2). Measured on 45 M elements, three copies cycled:
+// fp16 -> codes 26.7 -> 23.7 us, codes -> fp16 26.1 -> 20.7 us, codes -> fp32
+// 44.0 -> 34.8 us, fp32 -> codes 44.0 -> 40.8 us, and 38.5 us with the fp32
+// input read non-temporally as well (the same hint on the other loads was
+// slower).
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
 template <bool F32, int LPB, int VPL>
 __global__ __launch_bounds__(256) void kq_blockwise(const void* __restrict__ x, int n, int nb,
                                                     int8_t* __restrict__ q, float* __restrict__ absmax) {
   constexpr int E = F32 ? 4 : 8;  // elements per 16-byte vector
+  constexpr int kLoadPolicy = F32 ? 2 : 0;  // buffer cache policy: non-temporal reads of fp32 input
   constexpr int VPB = LPB * VPL;  // vectors per block
   constexpr int BPI = 64 / LPB;   // blocks per wavefront iteration
   static_assert(BPI * VPB * 16 == 1024 * VPL, "an iteration's window is codec_window_bytes(VPL)");
@@ -62,7 +72,7 @@ __global__ __launch_bounds__(256) void kq_blockwise(const void* __restrict__ x, 
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int vl = sub * VPB + i * LPB + li;  // vector within the window
-      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)vl * 16u, 0, 0));
+      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)vl * 16u, 0, kLoadPolicy));
     }
     uint32_t m = 0;
 #pragma unroll
@@ -87,9 +97,10 @@ __global__ __launch_bounds__(256) void kq_blockwise(const void* __restrict__ x, 
         const int vi = b * VPB + i * LPB + li;
         if (vi >= nvec) continue;
         if (F32) {
-          reinterpret_cast<uint32_t*>(q)[vi] = quantize4_f32(v[i], s);
+          __builtin_nontemporal_store(quantize4_f32(v[i], s), reinterpret_cast<uint32_t*>(q) + vi);
         } else {
-          reinterpret_cast<uint2*>(q)[vi] = quantize8_masked(v[i], s, 0xffffffffu, 0xffffffffu);
+          const uint2 c = quantize8_masked(v[i], s, 0xffffffffu, 0xffffffffu);
+          __builtin_nontemporal_store(v2u{c.x, c.y}, reinterpret_cast<v2u*>(q) + vi);
         }
       }
     }
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(256) void kdq_blockwise(const int8_t* __restrict__ 
         const float p = (float)(int)(int8_t)((c >> (8 * j)) & 0xffu) * a;
         po[j] = __builtin_bit_cast(uint32_t, div127(p));
       }
-      reinterpret_cast<uint4*>(out)[vi] = o;
+      __builtin_nontemporal_store(__builtin_bit_cast(v4i, o), reinterpret_cast<v4i*>(out) + vi);
     } else {
       const uint2 c = reinterpret_cast<const uint2*>(q)[vi];
       const uint32_t w[2] = {c.x, c.y};
@@ -131,7 +142,7 @@ __global__ __launch_bounds__(256) void kdq_blockwise(const int8_t* __restrict__ 
       o.y = h[2] | (h[3] << 16);
       o.z = h[4] | (h[5] << 16);
       o.w = h[6] | (h[7] << 16);
-      reinterpret_cast<uint4*>(out)[vi] = o;
+      __builtin_nontemporal_store(__builtin_bit_cast(v4i, o), reinterpret_cast<v4i*>(out) + vi);
     }
   }
 }

@@ -178,6 +178,7 @@ hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream) {
 //     resident.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 256;
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 constexpr int kMaxKW = kMaxK / 32;
 constexpr int kIdxCap = 4096;  // outlier indices kept in LDS by the gather blocks
 
@@ -229,7 +230,11 @@ __device__ __forceinline__ void quantize_row_regs(const LinearArgs& a, const uin
     const int c = lane + 64 * u;
     if (u < cpl && c < KC) {
       const uint32_t skip = chunk_skip_mask(bm, c);
-      out[c] = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+      // non-temporal: the codes are not read again by this kernel (ka_prepare
+      // 12.0 -> 11.4 us at the 2048 x 4096 prefill input; the whole call about
+      // 0.5 us faster, the GEMM that reads them next a little slower)
+      const uint2 q = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+      __builtin_nontemporal_store(v2u32{q.x, q.y}, reinterpret_cast<v2u32*>(out) + c);
     }
   }
   if (lane == 0) a.aX[t] = ax;

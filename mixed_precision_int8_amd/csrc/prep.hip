@@ -172,7 +172,8 @@ hipError_t launch_scan(const LinearArgs& a, int groups, hipStream_t stream) {
 //     rows wave, wave + W, ... (W quantization wavefronts) with two register
 //     buffers: the next row's loads are in flight while the current row is
 //     reduced and its codes are stored, so stores and loads overlap when a
-//     wavefront has several rows (up to 8192 columns per row). Rows longer
+//     wavefront has several rows (up to 8192 columns per row); rows of up to
+//     16384 columns have one buffer (CPL = 32, 128 registers). Rows longer
 //     than the largest capacity (CPL = 0) are read twice from memory, which
 //     keeps the kernel's registers low enough for all its blocks to stay
 //     resident.
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   const int row0 = (blockIdx.x - ng) * 4 + wave;
   const int W = nq * 4;  // quantization wavefronts
   constexpr int CB = CPL > 0 ? CPL : 1;
-  uint4 v0[CB], v1[CB];
+  uint4 v0[CB], v1[CPL > 16 ? 1 : CB];
   if (CPL > 0 && quant && row0 < T) load_row_regs<CB>(a, row0, lane, v0);
   // the row groups' partial bitmaps, all loads in flight before the first OR
   for (int w = tid; w < KW; w += kPrepThreads) {
@@ -290,7 +291,14 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
 
   if (quant) {
     // ---- activations: rows row0, row0 + W, ...; two register buffers alternate
-    if constexpr (CPL > 0) {
+    if constexpr (CPL > 16) {
+      // one register buffer (a second would not fit): the next row's loads
+      // follow the current row's stores
+      for (int t = row0; t < T; t += W) {
+        if (t != row0) load_row_regs<CB>(a, t, lane, v0);
+        quantize_row_regs<BF16, CB>(a, bm, t, lane, v0);
+      }
+    } else if constexpr (CPL > 0) {
       for (int t = row0; t < T; t += 2 * W) {
         const int t1 = t + W;
         if (t1 < T) load_row_regs<CB>(a, t1, lane, v1);
@@ -430,6 +438,8 @@ static hipError_t launch_prepare_dt(const LinearArgs& a, int groups, dim3 grid, 
     hipLaunchKernelGGL((ka_prepare<BF16, 8>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
   else if (cpl <= 16)
     hipLaunchKernelGGL((ka_prepare<BF16, 16>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
+  else if (cpl <= 32)
+    hipLaunchKernelGGL((ka_prepare<BF16, 32>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
   else
     hipLaunchKernelGGL((ka_prepare<BF16, 0>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
   return hipGetLastError();

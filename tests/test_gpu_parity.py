@@ -121,6 +121,15 @@ def test_ragged_k_and_n(K, N):
     run_case(f"ragged K={K} N={N} gemv", W, X[:5], 6.0, GEMV)
 
 
+@pytest.mark.parametrize("T,K,N", [(37, 8208, 40), (300, 12304, 96), (33, 16384, 33), (1, 14336, 17)])
+def test_long_rows_one_register_buffer(T, K, N):
+    """Rows of 8193 to 16384 columns: the activation quantization holds a row in
+    one register buffer of 32 chunks per lane (shorter rows take two buffers,
+    longer ones two passes over memory); every stage bit-exact."""
+    W, X = _small(T, K, N, seed=K + T, n_out=5)
+    run_case(f"long rows K={K}", W, X, 6.0, GEMM, check_auto=T > 16)
+
+
 @pytest.mark.parametrize("path", [GEMM, GEMV])
 def test_no_outliers_and_infinite_threshold(path):
     W, X = _small(12, 512, 96, seed=7)

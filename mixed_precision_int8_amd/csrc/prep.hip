@@ -259,7 +259,11 @@ __device__ __forceinline__ void quantize_row_mem(const LinearArgs& a, const uint
   if (lane == 0) a.aX[t] = ax;
 }
 
-template <bool BF16, int CPL>
+// ONE: a single register buffer, for rows of 32 chunks per lane (two would not
+// fit) and, with 16 chunks, for grids where every wavefront has at most one row
+// (the second buffer would never be used, and without it more workgroups stay
+// resident)
+template <bool BF16, int CPL, bool ONE>
 __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int groups, int nq) {
   __shared__ uint32_t bm[kMaxKW];
   __shared__ int pre[kMaxKW];
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   const int row0 = (blockIdx.x - ng) * 4 + wave;
   const int W = nq * 4;  // quantization wavefronts
   constexpr int CB = CPL > 0 ? CPL : 1;
-  uint4 v0[CB], v1[CPL > 16 ? 1 : CB];
+  uint4 v0[CB], v1[ONE ? 1 : CB];
   if (CPL > 0 && quant && row0 < T) load_row_regs<CB>(a, row0, lane, v0);
   // the row groups' partial bitmaps, all loads in flight before the first OR
   for (int w = tid; w < KW; w += kPrepThreads) {
@@ -291,9 +295,8 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
 
   if (quant) {
     // ---- activations: rows row0, row0 + W, ...; two register buffers alternate
-    if constexpr (CPL > 16) {
-      // one register buffer (a second would not fit): the next row's loads
-      // follow the current row's stores
+    if constexpr (CPL > 0 && ONE) {
+      // one register buffer: any next row's loads follow the current row's stores
       for (int t = row0; t < T; t += W) {
         if (t != row0) load_row_regs<CB>(a, t, lane, v0);
         quantize_row_regs<BF16, CB>(a, bm, t, lane, v0);
@@ -434,14 +437,22 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
 template <bool BF16>
 static hipError_t launch_prepare_dt(const LinearArgs& a, int groups, dim3 grid, int nq, hipStream_t stream) {
   const int cpl = ((a.K >> 3) + 63) >> 6;  // 16-byte chunks per lane of one row
-  if (cpl <= 8)
-    hipLaunchKernelGGL((ka_prepare<BF16, 8>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
-  else if (cpl <= 16)
-    hipLaunchKernelGGL((ka_prepare<BF16, 16>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
-  else if (cpl <= 32)
-    hipLaunchKernelGGL((ka_prepare<BF16, 32>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
-  else
-    hipLaunchKernelGGL((ka_prepare<BF16, 0>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq);
+  // every quantization wavefront has at most one row: the 16-chunk kernel then
+  // takes one buffer (127 registers, not 224: twice the resident workgroups;
+  // 39.3 -> 36.4 us at the 4096 x 8192 input). The 8-chunk kernel keeps two
+  // (119 registers; with one, 78, the 2048 x 4096 prefill call measured slower).
+  const bool one = a.T <= 4 * nq;
+#define PREP(C, O) hipLaunchKernelGGL((ka_prepare<BF16, C, O>), grid, dim3(kPrepThreads), 0, stream, a, groups, nq)
+  if (cpl <= 8) {
+    PREP(8, false);
+  } else if (cpl <= 16) {
+    if (one) PREP(16, true); else PREP(16, false);
+  } else if (cpl <= 32) {
+    PREP(32, true);
+  } else {
+    PREP(0, false);
+  }
+#undef PREP
   return hipGetLastError();
 }
 

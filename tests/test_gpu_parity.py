@@ -266,7 +266,7 @@ def test_forward_alternating_inputs_one_workspace():
     for rep in range(3):
         for i, (X, st) in enumerate(zip(Xs, sts)):
             out = m8.llmint8_linear_debug(_dev(X), Wq, sW, 6.0, path=GEMM, workspace=ws, want_C=False)
-            _check_stages(out, st, f"input {i}, round {rep}")
+            _check_stages(out, st, f"input {i}, pass {rep}")
 
 
 def test_forward_graph_replays_new_inputs():

@@ -130,6 +130,14 @@ def test_long_rows_one_register_buffer(T, K, N):
     run_case(f"long rows K={K}", W, X, 6.0, GEMM, check_auto=T > 16)
 
 
+def test_long_rows_several_per_wavefront():
+    """T past 4096 with rows of 8193 to 16384 columns: on a 256-CU device each
+    quantization wavefront takes two rows through its single register buffer,
+    loading the second after the first is stored; every stage bit-exact."""
+    W, X = _small(4500, 8320, 40, seed=4501, n_out=6)
+    run_case("long rows, several per wavefront", W, X, 6.0, GEMM, check_auto=True)
+
+
 @pytest.mark.parametrize("path", [GEMM, GEMV])
 def test_no_outliers_and_infinite_threshold(path):
     W, X = _small(12, 512, 96, seed=7)

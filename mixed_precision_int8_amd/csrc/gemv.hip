@@ -15,18 +15,22 @@
 //     once (16 x 16-byte loads per lane). Issuing that much stalls the issuing
 //     wavefront for about a microsecond, which is about when X has landed.
 //   * 4 X wavefronts copy X into LDS (buffer_load ... lds) meanwhile.
-//   * Then all 8 wavefronts work on X: a thread owns 8-column chunks across
-//     all T rows, decides their outlier flags on its own (column absmax >=
-//     threshold), takes the rows' maxima over its kept columns in the same
-//     pass (packed u16 arithmetic on 16-bit magnitude codes), and after one block-wide
-//     reduction quantizes its chunks into LDS.
+//   * The scan: a thread owns 8-column chunks across all T rows, decides
+//     their outlier flags on its own (column absmax >= threshold) and takes
+//     the rows' maxima over its kept columns in the same pass (packed u16
+//     arithmetic on 16-bit magnitude codes). At T = 1 the X wavefronts scan
+//     alone, each the chunks it copied, while the stream wavefronts are still
+//     issuing; for more rows all 8 wavefronts scan once those have issued.
+//   * After one block-wide reduction all 8 wavefronts quantize their chunks
+//     into LDS.
 //   * The stream wavefronts then multiply their quarter of K on
-//     v_mfma_i32_16x16x64_i8 (16 weight rows as A, int8 rows of X as B) and
-//     leave int32 partial sums in LDS. Meanwhile X wavefront 0, which has
-//     compacted the outlier indices and gathered the weight bytes of the
-//     first 32 outlier columns, computes the 16-bit outlier product on
-//     v_mfma_f32_16x16x32_f16; it finally sums the partials, dequantizes and
-//     stores Y in the activation type (fp16 or bf16).
+//     v_mfma_i32_16x16x64_i8 (16 weight rows as A, int8 rows of X as B, four
+//     independent accumulators) and leave int32 partial sums in LDS.
+//     Meanwhile X wavefront 0, which has compacted the outlier indices,
+//     gathers the weight bytes of the outlier columns and computes the 16-bit
+//     outlier product on v_mfma_f32_16x16x32_f16; it finally sums the
+//     partials, dequantizes and stores Y in the activation type (fp16 or
+//     bf16).
 // The kernel is instantiated per row capacity TB (1, 2, 4, 8, 16 >= T) so
 // that per-row loops are resolved at compile time.
 #include <atomic>
@@ -64,7 +68,7 @@ __host__ __device__ inline GemvLds gemv_lds(int T, int K) {
   off += kGemvRowsN * 4;
   L.rowred = off;  // [8 wavefronts][8 row pairs] packed u16 maxima
   off += 8 * 8 * 4;
-  L.cnt = off;
+  L.cnt = off;  // [0] outlier count, [1] X wavefronts' arrivals (T = 1)
   off += 16;
   L.total = off;
   return L;
@@ -101,6 +105,21 @@ __device__ __forceinline__ int byte_of(uint32_t word, int h) {
 }
 
 __device__ __forceinline__ v2u16 pk_max(v2u16 a, v2u16 b) { return __builtin_elementwise_max(a, b); }
+
+// Keep masks of 8 columns from their magnitude codes (packed u16 pairs):
+// cm - thr is negative (sign bit set) exactly where the column stays below the
+// threshold. Both codes are below 2^15, so the packed difference cannot wrap.
+__device__ __forceinline__ uint32_t keep_mask(v2u16 cm, v2u16 hthr2) {
+  const v2u16 d = cm - hthr2;
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, __builtin_bit_cast(short2, d) >> (short)15));
+}
+// Outlier bits (bit j: column j reaches the threshold) of 8 columns from their keep masks.
+__device__ __forceinline__ uint32_t outlier_bits(const uint32_t keep[4]) {
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bits |= (((~keep[i]) & 1u) | ((~keep[i] >> 15) & 2u)) << (2 * i);
+  return bits;
+}
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
 __device__ __forceinline__ uint32_t as_u32(v2u16 x) { return __builtin_bit_cast(uint32_t, x); }
 
@@ -118,6 +137,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   float* arow = reinterpret_cast<float*>(lds + L.arow);
   uint32_t* rowred = reinterpret_cast<uint32_t*>(lds + L.rowred);
   int* cnt = reinterpret_cast<int*>(lds + L.cnt);
+  int* xctr = cnt + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -131,6 +151,11 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.Wq + (size_t)n0 * K, (uint32_t)(rows_n * K));
   const uint32_t rowoff = (uint32_t)(fi * K);
   constexpr int NP = (TB + 1) / 2;  // row pairs packed as u16x2
+  // At T = 1 the X wavefronts scan (each its own copies of X) and quantize
+  // alone, so that work waits neither for the stream wavefronts to finish
+  // issuing nor for their loads.
+  constexpr bool kXScan = TB == 1;
+  constexpr int kScanWaves = kXScan ? 4 : 8;
 
   // stream wavefronts: their K range and the first batch of weight loads
   const int ww = wave & 3;
@@ -146,9 +171,141 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       w[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
     }
   };
+  // ---- 3. the scan: a thread takes 8-column chunks across all rows: column
+  // absmax -> outlier flags -> keep masks -> row maxima over the kept columns.
+  // All values are 16-bit codes with the sign cleared, compared as packed u16.
+  // Each scanning wavefront leaves its partial row maxima in rowred.
+  auto scan_chunks = [&](int first, int stride) {
+    const v2u16 hthr2 = {(uint16_t)hthr, (uint16_t)hthr};
+    v2u16 rmax[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) rmax[t] = v2u16{0, 0};
+    for (int c = first; c < KC; c += stride) {
+      v2u16 ab[TB][4];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const uint4 v = t < T ? *reinterpret_cast<const uint4*>(xs + t * K + c * 8) : uint4{0, 0, 0, 0};
+        ab[t][0] = as_u16x2(v.x & 0x7fff7fffu);
+        ab[t][1] = as_u16x2(v.y & 0x7fff7fffu);
+        ab[t][2] = as_u16x2(v.z & 0x7fff7fffu);
+        ab[t][3] = as_u16x2(v.w & 0x7fff7fffu);
+      }
+      uint32_t keep[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v2u16 cm = ab[0][i];
+#pragma unroll
+        for (int t = 1; t < TB; ++t) cm = pk_max(cm, ab[t][i]);
+        keep[i] = keep_mask(cm, hthr2);
+      }
+      if ((keep[0] & keep[1] & keep[2] & keep[3]) != 0xffffffffu)
+        atomicOr(&bm[c >> 2], outlier_bits(keep) << ((c & 3) * 8));
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        v2u16 m = rmax[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = pk_max(m, as_u16x2(as_u32(ab[t][i]) & keep[i]));
+        rmax[t] = m;
+      }
+    }
+    // fold the two halves, pack row pairs, reduce over the wavefront
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (2 * p < T) {
+        const uint32_t lo = max(rmax[2 * p].x, rmax[2 * p].y);
+        const uint32_t hi = 2 * p + 1 < TB ? max(rmax[2 * p + 1].x, rmax[2 * p + 1].y) : 0u;
+        const uint32_t r = wave_max_u16x2(lo | (hi << 16));
+        if (lane == 0) rowred[wave * 8 + p] = r;
+      }
+    }
+  };
+
+  // ---- 4. row scales from the scanning wavefronts' partial maxima, and the
+  // int8 codes of the chunks first, first + stride, ...
+  auto quantize_chunks = [&](int first, int stride) {
+    // lane t (< T) of every calling wavefront combines the partial maxima of
+    // row t; the scales then go to scalar registers
+    float srow = 0.0f;
+    if (lane < T) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int w = 0; w < kScanWaves; ++w) m = max(m, (rowred[w * 8 + (lane >> 1)] >> ((lane & 1) * 16)) & 0xffffu);
+      const float ax = A16::to_f32(m);
+      srow = m ? 127.0f / ax : 0.0f;
+      if (wave == 0) arow[lane] = ax;
+    }
+    float st[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+      st[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, srow), t));
+    // int8 codes of this thread's chunks
+    for (int c = first; c < KC; c += stride) {
+      uint4 v[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        if (t < T) v[t] = *reinterpret_cast<const uint4*>(xs + t * K + c * 8);
+      uint32_t skip;
+      if constexpr (TB == 1) {
+        // one row: a column's maximum is its only value, so the outlier
+        // flags follow from the chunk itself, as in the scan
+        const v2u16 hthr2 = {(uint16_t)hthr, (uint16_t)hthr};
+        const uint32_t keep[4] = {keep_mask(as_u16x2(v[0].x & 0x7fff7fffu), hthr2),
+                                  keep_mask(as_u16x2(v[0].y & 0x7fff7fffu), hthr2),
+                                  keep_mask(as_u16x2(v[0].z & 0x7fff7fffu), hthr2),
+                                  keep_mask(as_u16x2(v[0].w & 0x7fff7fffu), hthr2)};
+        skip = outlier_bits(keep);
+      } else {
+        skip = (bm[c >> 2] >> ((c & 3) * 8)) & 0xffu;
+      }
+      const uint32_t m0 = expand4(~skip & 0xfu), m1 = expand4((~skip >> 4) & 0xfu);
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(v[t], st[t], m0, m1);
+    }
+  };
+
+  // ---- 5b. wavefront 0: the outlier indices, ascending, compacted from the
+  // bitmap (the int8 product does not need them, so this runs after barrier
+  // C, beside the stream wavefronts' products); returns their count
+  auto compact = [&]() -> int {
+    const int per = (KW + 63) / 64;
+    const int w0i = min(KW, lane * per), w1i = min(KW, w0i + per);
+    int local = 0;
+    for (int w = w0i; w < w1i; ++w) local += __popc(bm[w]);
+    const int incl = wave_incl_sum(local);
+    const int count = __builtin_amdgcn_readlane(incl, 63);
+    if (count) {
+      int j = incl - local;
+      for (int w = w0i; w < w1i; ++w) {
+        uint32_t bits = bm[w];
+        while (bits) {
+          idxl[j++] = (uint16_t)(w * 32 + __builtin_ctz(bits));
+          bits &= bits - 1u;
+        }
+      }
+    }
+    if (lane == 0) *cnt = count;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the index writes precede the wavefront's reads
+    return count;
+  };
+
   v4i w0[kGemvBatch], w1[kGemvBatch];
   float bs4[4] = {0.f, 0.f, 0.f, 0.f}, brow = 0.f;
-  uint16_t bias4[4] = {0, 0, 0, 0};
+  uint32_t bias4[4] = {0, 0, 0, 0};  // 16-bit values kept in whole registers: no packing waits for the loads
+  // At T = 1 the X wavefronts synchronise among themselves through a counter
+  // in LDS; the stream wavefronts meet them only at barrier C. The counter
+  // is cleared before one block barrier at entry (E), which the X
+  // wavefronts reach once their copies of X are issued and the stream
+  // wavefronts before their first load: the copies of X enter the memory
+  // pipeline ahead of the weight stream. The wait is bounded, so it always ends.
+  auto x_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes are done
+    if (lane == 0) __hip_atomic_fetch_add(xctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(xctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
   if (xwave) {
     // ---- 1. X -> LDS (1 KB per wavefront issue); wavefront 0 also fetches
     // the scales of the 16 weight rows (rows past N read as zero)
@@ -169,138 +326,47 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
           bias4[v] = __builtin_amdgcn_raw_buffer_load_b16(rBias, (uint32_t)((4 * fg + v) * 2), 0, 0);
       }
     }
-    for (int w = xt; w < KW; w += 256) bm[w] = 0u;
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's part of X has landed
+    if constexpr (kXScan) {
+      if (tid == 0) *xctr = 0;
+      lds_barrier();  // E: the counter is clear; X and the scales are requested
+    }
+    if constexpr (kXScan) {
+      // X wavefront w copied the 1 KB pieces w, w + 4, ... of the row, i.e.
+      // chunks 64w + 256i + lane: it clears the bitmap words of those chunks
+      // and scans them as soon as its own copies have landed. The stream
+      // wavefronts, stalled issuing the weight loads, wait for none of it.
+      for (int c = xt; c < KC; c += 256)
+        if ((c & 3) == 0) bm[c >> 2] = 0u;
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's part of X has landed
+      scan_chunks(xt, 256);
+      x_sync();  // the 4 partial maxima and the whole bitmap are in LDS
+      quantize_chunks(xt, 256);
+    } else {
+      for (int w = xt; w < KW; w += 256) bm[w] = 0u;
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's part of X has landed
+    }
   } else {
     // ---- 2. the weight stream: 16 x 16-byte loads per lane, in flight while
     // the X wavefronts work (issuing them stalls only these wavefronts)
+    if constexpr (kXScan) lds_barrier();  // E
     load_batch(w0, 0);  // out-of-range steps read as zero
   }
-  lds_barrier();  // A: X is in LDS, the bitmap is clear
-
-  uint32_t g[8];
-  {
-    // ---- 3. all 8 wavefronts (the stream wavefronts have issued their loads
-    // by now): a thread takes 8-column chunks across all rows: column absmax
-    // -> outlier flags -> keep masks -> row maxima over the kept columns. All
-    // values are 16-bit codes with the sign cleared, compared as packed u16.
-    const v2u16 hthr2 = {(uint16_t)hthr, (uint16_t)hthr};
-    v2u16 rmax[TB];
-#pragma unroll
-    for (int t = 0; t < TB; ++t) rmax[t] = v2u16{0, 0};
-    for (int c = tid; c < KC; c += 512) {
-      v2u16 ab[TB][4];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        const uint4 v = t < T ? *reinterpret_cast<const uint4*>(xs + t * K + c * 8) : uint4{0, 0, 0, 0};
-        ab[t][0] = as_u16x2(v.x & 0x7fff7fffu);
-        ab[t][1] = as_u16x2(v.y & 0x7fff7fffu);
-        ab[t][2] = as_u16x2(v.z & 0x7fff7fffu);
-        ab[t][3] = as_u16x2(v.w & 0x7fff7fffu);
-      }
-      uint32_t keep[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v2u16 cm = ab[0][i];
-#pragma unroll
-        for (int t = 1; t < TB; ++t) cm = pk_max(cm, ab[t][i]);
-        // cm - thr is negative (sign bit set) exactly where the column is kept
-        const v2u16 d = cm - hthr2;
-        keep[i] = as_u32(__builtin_bit_cast(v2u16, __builtin_bit_cast(short2, d) >> (short)15));
-      }
-      if ((keep[0] & keep[1] & keep[2] & keep[3]) != 0xffffffffu) {
-        uint32_t bits = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bits |= (((~keep[i]) & 1u) | ((~keep[i] >> 15) & 2u)) << (2 * i);
-        atomicOr(&bm[c >> 2], bits << ((c & 3) * 8));
-      }
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        v2u16 m = rmax[t];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = pk_max(m, as_u16x2(as_u32(ab[t][i]) & keep[i]));
-        rmax[t] = m;
-      }
-    }
-    // fold the two halves, pack row pairs, reduce over the wavefront
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      if (2 * p < T) {
-        const uint32_t lo = max(rmax[2 * p].x, rmax[2 * p].y);
-        const uint32_t hi = 2 * p + 1 < TB ? max(rmax[2 * p + 1].x, rmax[2 * p + 1].y) : 0u;
-        const uint32_t r = wave_max_u16x2(lo | (hi << 16));
-        if (lane == 0) rowred[wave * 8 + p] = r;
-      }
-    }
+  if constexpr (!kXScan) {
+    lds_barrier();  // A: X is in LDS, the bitmap is clear
+    // all 8 wavefronts scan and quantize (the stream wavefronts have issued
+    // their loads by now)
+    scan_chunks(tid, 512);
+    lds_barrier();  // B: bitmap and partial row maxima complete
+    quantize_chunks(tid, 512);
   }
-  lds_barrier();  // B: bitmap and partial row maxima complete
-
-  {
-    // ---- 4. row scales: lane t (< T) of every wavefront combines the 8
-    // partial maxima of row t; the scales then go to scalar registers
-    float srow = 0.0f;
-    if (lane < T) {
-      uint32_t m = 0u;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) m = max(m, (rowred[w * 8 + (lane >> 1)] >> ((lane & 1) * 16)) & 0xffffu);
-      const float ax = A16::to_f32(m);
-      srow = m ? 127.0f / ax : 0.0f;
-      if (wave == 0) arow[lane] = ax;
-    }
-    float st[TB];
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-      st[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, srow), t));
-    // int8 codes of this thread's chunks
-    for (int c = tid; c < KC; c += 512) {
-      const uint32_t skip = (bm[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-      const uint32_t m0 = expand4(~skip & 0xfu), m1 = expand4((~skip >> 4) & 0xfu);
-      uint4 v[TB];
-#pragma unroll
-      for (int t = 0; t < TB; ++t)
-        if (t < T) v[t] = *reinterpret_cast<const uint4*>(xs + t * K + c * 8);
-#pragma unroll
-      for (int t = 0; t < TB; ++t)
-        if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(v[t], st[t], m0, m1);
-    }
-    // wavefront 0: compact the outlier indices (ascending), then gather the
-    // weight bytes of the first 32 outlier columns for the epilogue
-    if (wave == 0) {
-      const int per = (KW + 63) / 64;
-      const int w0i = min(KW, lane * per), w1i = min(KW, w0i + per);
-      int local = 0;
-      for (int w = w0i; w < w1i; ++w) local += __popc(bm[w]);
-      const int incl = wave_incl_sum(local);
-      const int count = __builtin_amdgcn_readlane(incl, 63);
-      if (count) {
-        int j = incl - local;
-        for (int w = w0i; w < w1i; ++w) {
-          uint32_t bits = bm[w];
-          while (bits) {
-            idxl[j++] = (uint16_t)(w * 32 + __builtin_ctz(bits));
-            bits &= bits - 1u;
-          }
-        }
-      }
-      if (lane == 0) *cnt = count;
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // the wavefront's index writes precede its reads
-      const uint4 iv = *reinterpret_cast<const uint4*>(idxl + fg * 8);
-      const uint32_t iw[4] = {iv.x, iv.y, iv.z, iv.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (iw[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        g[e] = load_word_of(rW, fg * 8 + e < count ? rowoff + h : kOobOffset);
-      }
-    }
-  }
-  lds_barrier();  // C: int8 rows of X, row statistics and outlier indices ready
+  lds_barrier();  // C: int8 rows of X and the row statistics are ready
 
   if (!xwave) {
     // ---- 5. int8 product of this wavefront's K range; partial sums to LDS.
     // B operand lanes of rows past T read row T-1: they only feed output
     // columns t >= T, which are never stored. Steps past the range read
     // in-bounds X; their weights were loaded as zeros.
-    v4i acc = {0, 0, 0, 0};
+    v4i acc4[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};  // independent chains
     const int8_t* xrow = xq + min(fi, T - 1) * L.kp;
     auto compute_batch = [&](const v4i* w, int b) {
       v4i xf[kGemvBatch];
@@ -311,7 +377,8 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       }
       __builtin_amdgcn_sched_barrier(0);  // all reads in flight before the first product
 #pragma unroll
-      for (int s = 0; s < kGemvBatch; ++s) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[s], xf[s], acc, 0, 0, 0);
+      for (int s = 0; s < kGemvBatch; ++s)
+        acc4[s & 3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[s], xf[s], acc4[s & 3], 0, 0, 0);
     };
     for (int b = 0; b < nbatch; b += 2) {
       if (b + 1 < nbatch) load_batch(w1, b + 1);
@@ -321,15 +388,16 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
         compute_batch(w1, b + 1);
       }
     }
-    red[ww * 64 + lane] = acc;
+    red[ww * 64 + lane] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   }
-  // X wavefront 0, while the stream wavefronts multiply: the 16-bit outlier
-  // product, which needs only X and the gathered weight bytes. Lane holds
-  // rows (n) n0 + 4*fg + v of column (t) fi.
-  const int count = *cnt;
+  // X wavefront 0, while the stream wavefronts multiply: the outlier indices,
+  // then the 16-bit outlier product, which needs only X and the gathered
+  // weight bytes. Lane holds rows (n) n0 + 4*fg + v of column (t) fi.
   const int t = fi;
   v4f yo = {0.f, 0.f, 0.f, 0.f};
-  if (wave == 0 && count) {
+  const int count0 = wave == 0 ? compact() : 0;
+  if (count0) {
+    const int count = count0;
     const uint16_t* xr = xs + min(t, T - 1) * K;
     for (int c = 0; c < count; c += kOutChunk) {
       // 8 indices in one read (past `count` they are masked below), then the
@@ -347,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool ok = c + fg * 8 + e < count;
-        const uint32_t word = c == 0 ? g[e] : load_word_of(rW, ok ? rowoff + (uint32_t)h[e] : kOobOffset);
+        const uint32_t word = load_word_of(rW, ok ? rowoff + (uint32_t)h[e] : kOobOffset);
         wf[e] = A16::from_f32(((float)byte_of(word, h[e]) * brow) / 127.0f);
         xf[e] = (ok && t < T) ? xv[e] : (uint16_t)0;
       }
@@ -358,9 +426,10 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       yo = A16::mma16(wf4, xf4, yo);
     }
   }
-  lds_barrier();  // D: the 4 partial products are in LDS
+  lds_barrier();  // D: the 4 partial products and the outlier indices are in LDS
 
   // intermediate stages for inspection (first block only, off the timed path)
+  const int count = __builtin_amdgcn_readfirstlane(*cnt);
   if (blockIdx.x == 0) {
     for (int w = tid; w < KW; w += 512)
       if (a.dbg_bitmap) a.dbg_bitmap[w] = bm[w];

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // alone, so that work waits neither for the stream wavefronts to finish
   // issuing nor for their loads.
   constexpr bool kXScan = TB == 1;
-  constexpr int kScanWaves = kXScan ? 4 : 8;
+  constexpr int kScanWaves = kXScan ? 4 : 8;  // wavefronts that leave partial row maxima
 
   // stream wavefronts: their K range and the first batch of weight loads
   const int ww = wave & 3;
@@ -163,12 +163,19 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   const int kend = min(K, kbeg + kq);
   const int steps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   const int nbatch = (steps + kGemvBatch - 1) / kGemvBatch;
+  // Whole 128-byte lines per load instruction: for the step pair (2p, 2p+1)
+  // load w[2p] covers rows 0-7 and w[2p+1] rows 8-15, each row's 128 bytes
+  // by 8 lanes. Lane (fg, fi) takes row fi & 7 (+ 8), bytes 16 * (fg + 4 *
+  // (fi >> 3)) of the pair: lanes fi < 8 hold the first 64 bytes of their
+  // row, lanes fi >= 8 the second 64 bytes of row fi - 8 (+ 8).
   auto load_batch = [&](v4i* w, int b) {
+    const uint32_t r0 = (uint32_t)((fi & 7) * K), r1 = (uint32_t)((8 + (fi & 7)) * K);
 #pragma unroll
-    for (int s = 0; s < kGemvBatch; ++s) {
-      const int k = kbeg + (b * kGemvBatch + s) * 64 + fg * 16;
-      const uint32_t off = k < kend ? rowoff + (uint32_t)k : kOobOffset;
-      w[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
+    for (int p = 0; p < kGemvBatch / 2; ++p) {
+      const int k = kbeg + (b * kGemvBatch + 2 * p) * 64 + fg * 16 + (fi >> 3) * 64;
+      const bool in = k < kend;
+      w[2 * p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, in ? r0 + (uint32_t)k : kOobOffset, 0, 0));
+      w[2 * p + 1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, in ? r1 + (uint32_t)k : kOobOffset, 0, 0));
     }
   };
   // ---- 3. the scan: a thread takes 8-column chunks across all rows: column
@@ -363,22 +370,38 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
 
   if (!xwave) {
     // ---- 5. int8 product of this wavefront's K range; partial sums to LDS.
-    // B operand lanes of rows past T read row T-1: they only feed output
-    // columns t >= T, which are never stored. Steps past the range read
-    // in-bounds X; their weights were loaded as zeros.
+    // B operand lanes of rows past T hold zeros and read nothing: they only
+    // feed output columns t >= T, which are never stored, and at small T the
+    // LDS reads of the live lanes alone are a fraction of a full fragment's.
+    // Steps past the range read in-bounds X; their weights were loaded as zeros.
     v4i acc4[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};  // independent chains
     const int8_t* xrow = xq + min(fi, T - 1) * L.kp;
+    const bool live = fi < T;
     auto compute_batch = [&](const v4i* w, int b) {
       v4i xf[kGemvBatch];
 #pragma unroll
-      for (int s = 0; s < kGemvBatch; ++s) {
-        const int k = min(kbeg + (b * kGemvBatch + s) * 64 + fg * 16, K - 16);
-        xf[s] = *reinterpret_cast<const v4i*>(xrow + k);
+      for (int s = 0; s < kGemvBatch; ++s) xf[s] = v4i{0, 0, 0, 0};
+      if (live) {
+#pragma unroll
+        for (int s = 0; s < kGemvBatch; ++s) {
+          const int k = min(kbeg + (b * kGemvBatch + s) * 64 + fg * 16, K - 16);
+          xf[s] = *reinterpret_cast<const v4i*>(xrow + k);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);  // all reads in flight before the first product
+      // Each whole-line fragment meets both halves of the X pair. Product
+      // rows where the fragment's k range matches the X half are the valid
+      // ones: acc4[0] rows 0-7 (weight rows 0-7, first halves), acc4[1]
+      // rows 8-15 (weight rows 0-7, second halves), acc4[2] rows 0-7 (weight
+      // rows 8-15, first halves), acc4[3] rows 8-15 (weight rows 8-15,
+      // second halves); the other rows are discarded.
 #pragma unroll
-      for (int s = 0; s < kGemvBatch; ++s)
-        acc4[s & 3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[s], xf[s], acc4[s & 3], 0, 0, 0);
+      for (int p = 0; p < kGemvBatch / 2; ++p) {
+        acc4[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p], xf[2 * p], acc4[0], 0, 0, 0);
+        acc4[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p], xf[2 * p + 1], acc4[1], 0, 0, 0);
+        acc4[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p + 1], xf[2 * p], acc4[2], 0, 0, 0);
+        acc4[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p + 1], xf[2 * p + 1], acc4[3], 0, 0, 0);
+      }
     };
     for (int b = 0; b < nbatch; b += 2) {
       if (b + 1 < nbatch) load_batch(w1, b + 1);
@@ -388,7 +411,14 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
         compute_batch(w1, b + 1);
       }
     }
-    red[ww * 64 + lane] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    // Output lane (fg, fi) holds rows 4 fg .. 4 fg + 3: lanes fg < 2 (rows
+    // 0-7) add acc4[1] of the lane 32 above, lanes fg >= 2 (rows 8-15)
+    // acc4[2] of the lane 32 below. Exact int32 sums.
+    const v4i own = fg < 2 ? acc4[0] : acc4[3], give = fg < 2 ? acc4[2] : acc4[1];
+    v4i other;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) other[v] = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, give[v]);
+    red[ww * 64 + lane] = own + other;
   }
   // X wavefront 0, while the stream wavefronts multiply: the outlier indices,
   // then the 16-bit outlier product, which needs only X and the gathered

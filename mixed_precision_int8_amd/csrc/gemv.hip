@@ -277,14 +277,22 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   auto compact = [&]() -> int {
     const int per = (KW + 63) / 64;
     const int w0i = min(KW, lane * per), w1i = min(KW, w0i + per);
+    // up to 4 words per lane (K <= 8192) are read once and kept in registers
+    constexpr int kHeld = 4;
+    uint32_t held[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) held[i] = w0i + i < w1i ? bm[w0i + i] : 0u;
     int local = 0;
-    for (int w = w0i; w < w1i; ++w) local += __popc(bm[w]);
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) local += __popc(held[i]);
+    for (int w = w0i + kHeld; w < w1i; ++w) local += __popc(bm[w]);
     const int incl = wave_incl_sum(local);
     const int count = __builtin_amdgcn_readlane(incl, 63);
     if (count) {
       int j = incl - local;
       for (int w = w0i; w < w1i; ++w) {
-        uint32_t bits = bm[w];
+        const int i = w - w0i;
+        uint32_t bits = i == 0 ? held[0] : i == 1 ? held[1] : i == 2 ? held[2] : i == 3 ? held[3] : bm[w];
         while (bits) {
           idxl[j++] = (uint16_t)(w * 32 + __builtin_ctz(bits));
           bits &= bits - 1u;
@@ -425,6 +433,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // weight bytes. Lane holds rows (n) n0 + 4*fg + v of column (t) fi.
   const int t = fi;
   v4f yo = {0.f, 0.f, 0.f, 0.f};
+  const float at = wave == 0 && t < T ? arow[t] : 0.0f;  // row statistic for the epilogue, read early
   const int count0 = wave == 0 ? compact() : 0;
   if (count0) {
     const int count = count0;
@@ -459,8 +468,8 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   lds_barrier();  // D: the 4 partial products and the outlier indices are in LDS
 
   // intermediate stages for inspection (first block only, off the timed path)
-  const int count = __builtin_amdgcn_readfirstlane(*cnt);
   if (blockIdx.x == 0) {
+    const int count = __builtin_amdgcn_readfirstlane(*cnt);
     for (int w = tid; w < KW; w += 512)
       if (a.dbg_bitmap) a.dbg_bitmap[w] = bm[w];
     for (int j = tid; j < count; j += 512)
@@ -486,7 +495,6 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     for (int v = 0; v < 4; ++v)
       if (n + v < N) a.dbg_C[(size_t)t * N + n + v] = acc[v];
   }
-  const float at = t < T ? arow[t] : 0.0f;
   v4f y;
 #pragma unroll
   for (int v = 0; v < 4; ++v) y[v] = (float)acc[v] * (at * (bs4[v] * (1.0f / 16129.0f))) + yo[v];

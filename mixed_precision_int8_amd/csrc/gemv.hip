@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t outlier_bits(const uint32_t keep[4]) {
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
 __device__ __forceinline__ uint32_t as_u32(v2u16 x) { return __builtin_bit_cast(uint32_t, x); }
 
-template <int TB, bool BF16>
+template <int TB, bool BF16, bool XS>
 __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, int kq) {
   using A16 = Act16<BF16>;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -151,10 +151,12 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.Wq + (size_t)n0 * K, (uint32_t)(rows_n * K));
   const uint32_t rowoff = (uint32_t)(fi * K);
   constexpr int NP = (TB + 1) / 2;  // row pairs packed as u16x2
-  // At T = 1 the X wavefronts scan (each its own copies of X) and quantize
+  // With XS the X wavefronts scan (each its own copies of X) and quantize
   // alone, so that work waits neither for the stream wavefronts to finish
-  // issuing nor for their loads.
-  constexpr bool kXScan = TB == 1;
+  // issuing nor for their loads. X wavefront w copies the 1 KB pieces w,
+  // w + 4, ... of X, which hold the chunks 64w + 256i of every row when
+  // there is one row or K is a multiple of 2048 (the host picks XS then).
+  constexpr bool kXScan = XS;
   constexpr int kScanWaves = kXScan ? 4 : 8;  // wavefronts that leave partial row maxima
 
   // stream wavefronts: their K range and the first batch of weight loads
@@ -516,12 +518,12 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   }
 }
 
-template <int TB, bool BF16>
+template <int TB, bool BF16, bool XS>
 static hipError_t launch_gemv_tb(const LinearArgs& a, hipStream_t stream) {
   const GemvLds L = gemv_lds(a.T, a.K);
   static std::atomic<int> attr_max{64 * 1024};  // dynamic LDS this instance is allowed so far
   if (L.total > attr_max.load()) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kd_gemv<TB, BF16>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kd_gemv<TB, BF16, XS>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     int cur = attr_max.load();
@@ -530,18 +532,20 @@ static hipError_t launch_gemv_tb(const LinearArgs& a, hipStream_t stream) {
   }
   const int kq = (int)(ceil_div(ceil_div(a.K, 4), 64) * 64);
   const int blocks = (int)ceil_div(a.N, kGemvRowsN);
-  hipLaunchKernelGGL((kd_gemv<TB, BF16>), dim3(blocks), dim3(512), L.total, stream, a,
+  hipLaunchKernelGGL((kd_gemv<TB, BF16, XS>), dim3(blocks), dim3(512), L.total, stream, a,
                      threshold_code(a.thr, BF16), kq);
   return hipGetLastError();
 }
 
 template <bool BF16>
 static hipError_t launch_gemv_dt(const LinearArgs& a, hipStream_t stream) {
-  if (a.T <= 1) return launch_gemv_tb<1, BF16>(a, stream);
-  if (a.T <= 2) return launch_gemv_tb<2, BF16>(a, stream);
-  if (a.T <= 4) return launch_gemv_tb<4, BF16>(a, stream);
-  if (a.T <= 8) return launch_gemv_tb<8, BF16>(a, stream);
-  return launch_gemv_tb<16, BF16>(a, stream);
+  // the X wavefronts scan alone when their copies hold whole chunk columns
+  const bool xs = a.K % 2048 == 0;
+  if (a.T <= 1) return launch_gemv_tb<1, BF16, true>(a, stream);
+  if (a.T <= 2) return xs ? launch_gemv_tb<2, BF16, true>(a, stream) : launch_gemv_tb<2, BF16, false>(a, stream);
+  if (a.T <= 4) return xs ? launch_gemv_tb<4, BF16, true>(a, stream) : launch_gemv_tb<4, BF16, false>(a, stream);
+  if (a.T <= 8) return xs ? launch_gemv_tb<8, BF16, true>(a, stream) : launch_gemv_tb<8, BF16, false>(a, stream);
+  return xs ? launch_gemv_tb<16, BF16, true>(a, stream) : launch_gemv_tb<16, BF16, false>(a, stream);
 }
 
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream) {

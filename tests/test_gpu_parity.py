@@ -216,13 +216,14 @@ def test_many_outlier_chunks():
     run_case("100 outliers gemv", W, X[:9], 6.0, GEMV)
 
 
-@pytest.mark.parametrize("T,K,n_out", [(3, 8192, 45), (8, 4096, 32), (1, 14336, 33)])
+@pytest.mark.parametrize("T,K,n_out", [(3, 8192, 45), (8, 4096, 32), (1, 14336, 33), (12, 4096, 40),
+                                       (16, 2048, 20), (6, 2064, 9)])
 def test_gemv_outlier_bytes_across_k_ranges(T, K, n_out):
-    """Decode kernel: the weight bytes of the first 32 outlier columns come
-    out of the registers that streamed the weight, from each of the four K
-    quarters and from every register batch (two at K = 8192, four at 14336);
-    columns past the first 32 are read from memory. Ragged N; bit-exact
-    stages and Y within the bar."""
+    """Decode kernel: outlier columns spread over each of the four K
+    quarters and every register batch (two at K = 8192, four at 14336), more
+    than one 32-column chunk of them, ragged N; rows up to 16, with K a
+    multiple of 2048 (the X wavefronts scan and quantize alone) and not
+    (2064). Bit-exact stages and Y within the bar."""
     W, X = _small(T, K, 300, seed=K + n_out, n_out=n_out)
     _, c = run_case(f"gemv outliers over K ranges K={K}", W, X, 6.0, GEMV)
     assert c >= n_out

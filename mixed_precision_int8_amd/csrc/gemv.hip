@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t outlier_bits(const uint32_t keep[4]) {
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
 __device__ __forceinline__ uint32_t as_u32(v2u16 x) { return __builtin_bit_cast(uint32_t, x); }
 
-template <int TB, bool BF16, bool XS>
+template <int TB, bool BF16, int XM>
 __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, int kq) {
   using A16 = Act16<BF16>;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -156,7 +156,14 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // issuing nor for their loads. X wavefront w copies the 1 KB pieces w,
   // w + 4, ... of X, which hold the chunks 64w + 256i of every row when
   // there is one row or K is a multiple of 2048 (the host picks XS then).
-  constexpr bool kXScan = XS;
+  constexpr bool kXScan = XM != 0;   // the X wavefronts scan alone
+  constexpr bool kXQuant = XM == 1;  // ... and quantize alone (else all 8 wavefronts do, after barrier B)
+  // XM == 2: X is loaded into the X wavefronts' registers, each thread the
+  // kCpt chunks it scans, and written to LDS by them; the kernel then has no
+  // copy into LDS in flight that the stream wavefronts' LDS reads would wait on
+  constexpr int kCpt = XM == 2 ? (TB <= 2 ? 4 : 4096 / (TB * 256)) : 1;
+  static_assert(XM != 2 || kCpt >= 1, "register-loaded X needs TB <= 16");
+  uint4 xr[kCpt][TB];
   constexpr int kScanWaves = kXScan ? 4 : 8;  // wavefronts that leave partial row maxima
 
   // stream wavefronts: their K range and the first batch of weight loads
@@ -184,40 +191,38 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // absmax -> outlier flags -> keep masks -> row maxima over the kept columns.
   // All values are 16-bit codes with the sign cleared, compared as packed u16.
   // Each scanning wavefront leaves its partial row maxima in rowred.
-  auto scan_chunks = [&](int first, int stride) {
+  // one chunk: its column maxima over the rows -> outlier bits into the
+  // bitmap; the rows' maxima over its kept columns into rmax
+  auto scan_chunk = [&](int c, const uint4* v, v2u16* rmax) {
     const v2u16 hthr2 = {(uint16_t)hthr, (uint16_t)hthr};
-    v2u16 rmax[TB];
+    v2u16 ab[TB][4];
 #pragma unroll
-    for (int t = 0; t < TB; ++t) rmax[t] = v2u16{0, 0};
-    for (int c = first; c < KC; c += stride) {
-      v2u16 ab[TB][4];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        const uint4 v = t < T ? *reinterpret_cast<const uint4*>(xs + t * K + c * 8) : uint4{0, 0, 0, 0};
-        ab[t][0] = as_u16x2(v.x & 0x7fff7fffu);
-        ab[t][1] = as_u16x2(v.y & 0x7fff7fffu);
-        ab[t][2] = as_u16x2(v.z & 0x7fff7fffu);
-        ab[t][3] = as_u16x2(v.w & 0x7fff7fffu);
-      }
-      uint32_t keep[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v2u16 cm = ab[0][i];
-#pragma unroll
-        for (int t = 1; t < TB; ++t) cm = pk_max(cm, ab[t][i]);
-        keep[i] = keep_mask(cm, hthr2);
-      }
-      if ((keep[0] & keep[1] & keep[2] & keep[3]) != 0xffffffffu)
-        atomicOr(&bm[c >> 2], outlier_bits(keep) << ((c & 3) * 8));
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        v2u16 m = rmax[t];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = pk_max(m, as_u16x2(as_u32(ab[t][i]) & keep[i]));
-        rmax[t] = m;
-      }
+    for (int t = 0; t < TB; ++t) {
+      ab[t][0] = as_u16x2(v[t].x & 0x7fff7fffu);
+      ab[t][1] = as_u16x2(v[t].y & 0x7fff7fffu);
+      ab[t][2] = as_u16x2(v[t].z & 0x7fff7fffu);
+      ab[t][3] = as_u16x2(v[t].w & 0x7fff7fffu);
     }
-    // fold the two halves, pack row pairs, reduce over the wavefront
+    uint32_t keep[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v2u16 cm = ab[0][i];
+#pragma unroll
+      for (int t = 1; t < TB; ++t) cm = pk_max(cm, ab[t][i]);
+      keep[i] = keep_mask(cm, hthr2);
+    }
+    if ((keep[0] & keep[1] & keep[2] & keep[3]) != 0xffffffffu)
+      atomicOr(&bm[c >> 2], outlier_bits(keep) << ((c & 3) * 8));
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      v2u16 m = rmax[t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = pk_max(m, as_u16x2(as_u32(ab[t][i]) & keep[i]));
+      rmax[t] = m;
+    }
+  };
+  // fold the two halves, pack row pairs, reduce over the wavefront
+  auto scan_finish = [&](const v2u16* rmax) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       if (2 * p < T) {
@@ -227,6 +232,19 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
         if (lane == 0) rowred[wave * 8 + p] = r;
       }
     }
+  };
+  auto scan_chunks = [&](int first, int stride) {
+    v2u16 rmax[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) rmax[t] = v2u16{0, 0};
+    for (int c = first; c < KC; c += stride) {
+      uint4 v[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        v[t] = t < T ? *reinterpret_cast<const uint4*>(xs + t * K + c * 8) : uint4{0, 0, 0, 0};
+      scan_chunk(c, v, rmax);
+    }
+    scan_finish(rmax);
   };
 
   // ---- 4. row scales from the scanning wavefronts' partial maxima, and the
@@ -328,8 +346,22 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     // the scales of the 16 weight rows (rows past N read as zero)
     const int xbytes = T * K * 2;
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X, (uint32_t)xbytes);
-    for (int blk = wave; blk * 1024 < xbytes; blk += 4)
-      lds_copy16(rX, lds + L.xs + blk * 1024, (uint32_t)(blk * 1024 + lane * 16));
+    if constexpr (XM == 2) {
+      // into registers, each thread the chunks it scans (rows past T and
+      // chunks past the row read as zero); written to LDS below
+#pragma unroll
+      for (int i = 0; i < kCpt; ++i) {
+        const int c = xt + 256 * i;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const uint32_t off = c < KC && t < T ? (uint32_t)((t * K + c * 8) * 2) : kOobOffset;
+          xr[i][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+        }
+      }
+    } else {
+      for (int blk = wave; blk * 1024 < xbytes; blk += 4)
+        lds_copy16(rX, lds + L.xs + blk * 1024, (uint32_t)(blk * 1024 + lane * 16));
+    }
     if (wave == 0) {
       const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.sW + n0, (uint32_t)(rows_n * 4));
       brow = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)(fi * 4), 0, 0));
@@ -355,9 +387,28 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       for (int c = xt; c < KC; c += 256)
         if ((c & 3) == 0) bm[c >> 2] = 0u;
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's part of X has landed
-      scan_chunks(xt, 256);
-      x_sync();  // the 4 partial maxima and the whole bitmap are in LDS
-      quantize_chunks(xt, 256);
+      if constexpr (XM == 2) {
+        v2u16 rmax[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) rmax[t] = v2u16{0, 0};
+#pragma unroll
+        for (int i = 0; i < kCpt; ++i) {
+          const int c = xt + 256 * i;
+          if (c < KC) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+              if (t < T) *reinterpret_cast<uint4*>(lds + L.xs + (t * K + c * 8) * 2) = xr[i][t];
+            scan_chunk(c, xr[i], rmax);
+          }
+        }
+        scan_finish(rmax);
+      } else {
+        scan_chunks(xt, 256);
+      }
+      if constexpr (kXQuant) {
+        x_sync();  // the 4 partial maxima and the whole bitmap are in LDS
+        quantize_chunks(xt, 256);
+      }
     } else {
       for (int w = xt; w < KW; w += 256) bm[w] = 0u;
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's part of X has landed
@@ -373,6 +424,8 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     // all 8 wavefronts scan and quantize (the stream wavefronts have issued
     // their loads by now)
     scan_chunks(tid, 512);
+  }
+  if constexpr (!kXQuant) {
     lds_barrier();  // B: bitmap and partial row maxima complete
     quantize_chunks(tid, 512);
   }
@@ -518,12 +571,12 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   }
 }
 
-template <int TB, bool BF16, bool XS>
+template <int TB, bool BF16, int XM>
 static hipError_t launch_gemv_tb(const LinearArgs& a, hipStream_t stream) {
   const GemvLds L = gemv_lds(a.T, a.K);
   static std::atomic<int> attr_max{64 * 1024};  // dynamic LDS this instance is allowed so far
   if (L.total > attr_max.load()) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kd_gemv<TB, BF16, XS>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kd_gemv<TB, BF16, XM>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     int cur = attr_max.load();
@@ -532,20 +585,30 @@ static hipError_t launch_gemv_tb(const LinearArgs& a, hipStream_t stream) {
   }
   const int kq = (int)(ceil_div(ceil_div(a.K, 4), 64) * 64);
   const int blocks = (int)ceil_div(a.N, kGemvRowsN);
-  hipLaunchKernelGGL((kd_gemv<TB, BF16, XS>), dim3(blocks), dim3(512), L.total, stream, a,
+  hipLaunchKernelGGL((kd_gemv<TB, BF16, XM>), dim3(blocks), dim3(512), L.total, stream, a,
                      threshold_code(a.thr, BF16), kq);
   return hipGetLastError();
 }
 
 template <bool BF16>
 static hipError_t launch_gemv_dt(const LinearArgs& a, hipStream_t stream) {
-  // the X wavefronts scan alone when their copies hold whole chunk columns
+  // XM 1: the X wavefronts scan and quantize alone, when their copies hold
+  // whole chunk columns (measured best up to 4 rows); XM 2: X in their
+  // registers (a thread holds kCpt chunks of TB rows), they scan alone and all
+  // 8 wavefronts quantize (best at 8 rows); XM 0: all 8 scan and quantize
   const bool xs = a.K % 2048 == 0;
-  if (a.T <= 1) return launch_gemv_tb<1, BF16, true>(a, stream);
-  if (a.T <= 2) return xs ? launch_gemv_tb<2, BF16, true>(a, stream) : launch_gemv_tb<2, BF16, false>(a, stream);
-  if (a.T <= 4) return xs ? launch_gemv_tb<4, BF16, true>(a, stream) : launch_gemv_tb<4, BF16, false>(a, stream);
-  if (a.T <= 8) return xs ? launch_gemv_tb<8, BF16, true>(a, stream) : launch_gemv_tb<8, BF16, false>(a, stream);
-  return xs ? launch_gemv_tb<16, BF16, true>(a, stream) : launch_gemv_tb<16, BF16, false>(a, stream);
+  if (a.T <= 1) return launch_gemv_tb<1, BF16, 1>(a, stream);
+  if (a.T <= 2)
+    return xs ? launch_gemv_tb<2, BF16, 1>(a, stream)
+              : a.K <= 8192 ? launch_gemv_tb<2, BF16, 2>(a, stream) : launch_gemv_tb<2, BF16, 0>(a, stream);
+  if (a.T <= 4)
+    return xs ? launch_gemv_tb<4, BF16, 1>(a, stream)
+              : a.K <= 8192 ? launch_gemv_tb<4, BF16, 2>(a, stream) : launch_gemv_tb<4, BF16, 0>(a, stream);
+  if (a.T <= 8)
+    return a.K <= 4096 ? launch_gemv_tb<8, BF16, 2>(a, stream)
+                       : xs ? launch_gemv_tb<8, BF16, 1>(a, stream) : launch_gemv_tb<8, BF16, 0>(a, stream);
+  return a.K <= 2048 ? launch_gemv_tb<16, BF16, 2>(a, stream)
+                     : xs ? launch_gemv_tb<16, BF16, 1>(a, stream) : launch_gemv_tb<16, BF16, 0>(a, stream);
 }
 
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream) {

@@ -211,16 +211,46 @@ __device__ __forceinline__ void load_row_regs(const LinearArgs& a, int t, int la
     if (u < cpl) v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, (uint32_t)((lane + 64 * u) * 16), 0, 0));
 }
 
+// The outlier flags of a lane's chunks c = lane + 64 u, the same for every
+// row: read from the bitmap once (all reads in flight together) and packed
+// four chunks' 8-bit masks to a register. Read for every chunk from LDS, the
+// masks had cost the 8-chunk kernel eight LDS round trips per row in
+// sequence.
+template <int CPL>
+__device__ __forceinline__ void load_skip_masks(const uint32_t* bm, int lane, int KC,
+                                                uint32_t (&sk)[(CPL + 3) / 4]) {
+  uint32_t w[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) w[u] = lane + 64 * u < KC ? bm[(lane >> 2) + 16 * u] : 0u;
+#pragma unroll
+  for (int j = 0; j < (CPL + 3) / 4; ++j) {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * j + i < CPL) x |= ((w[4 * j + i] >> ((lane & 3) * 8)) & 0xffu) << (8 * i);
+    sk[j] = x;
+  }
+}
+// the mask of chunk u: from the packed registers (8 chunks per lane), else
+// from the bitmap in LDS (longer rows: registers for their masks would cost
+// the rows' register buffers occupancy)
+template <int CPL>
+__device__ __forceinline__ uint32_t skip_of(const uint32_t (&sk)[(CPL + 3) / 4], const uint32_t* bm, int lane,
+                                            int u) {
+  if constexpr (CPL <= 8) return (sk[u >> 2] >> ((u & 3) * 8)) & 0xffu;
+  else return chunk_skip_mask(bm, lane + 64 * u);
+}
+
 // absmax over the kept columns, quantization and the stores of row t (held in v)
 template <bool BF16, int CPL>
-__device__ __forceinline__ void quantize_row_regs(const LinearArgs& a, const uint32_t* bm, int t, int lane,
-                                                  const uint4 (&v)[CPL]) {
+__device__ __forceinline__ void quantize_row_regs(const LinearArgs& a, const uint32_t (&sk)[(CPL + 3) / 4],
+                                                  const uint32_t* bm, int t, int lane, const uint4 (&v)[CPL]) {
   const int K = a.K, KC = K >> 3, cpl = (KC + 63) >> 6;
   uint32_t m = 0u;
 #pragma unroll
   for (int u = 0; u < CPL; ++u) {
     const int c = lane + 64 * u;
-    if (u < cpl && c < KC) m = max(m, chunk_kept_max(v[u], chunk_skip_mask(bm, c)));
+    if (u < cpl && c < KC) m = max(m, chunk_kept_max(v[u], skip_of<CPL>(sk, bm, lane, u)));
   }
   m = wave_max_u16x2(m) & 0xffffu;
   const float ax = Act16<BF16>::to_f32(m);
@@ -238,7 +268,7 @@ __device__ __forceinline__ void quantize_row_regs(const LinearArgs& a, const uin
     for (int i = 0; i < G; ++i) {
       const int u = u0 + i, c = lane + 64 * u;
       if (u < cpl && c < KC) {
-        const uint32_t skip = chunk_skip_mask(bm, c);
+        const uint32_t skip = skip_of<CPL>(sk, bm, lane, u);
         q[i] = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
       }
     }
@@ -307,21 +337,23 @@ __global__ __launch_bounds__(kPrepThreads) void ka_prepare(LinearArgs a, int gro
   __syncthreads();
 
   if (quant) {
+    uint32_t sk[(CB + 3) / 4];
+    if constexpr (CPL > 0 && CPL <= 8) load_skip_masks<CB>(bm, lane, K >> 3, sk);
     // ---- activations: rows row0, row0 + W, ...; two register buffers alternate
     if constexpr (CPL > 0 && ONE) {
       // one register buffer: any next row's loads follow the current row's stores
       for (int t = row0; t < T; t += W) {
         if (t != row0) load_row_regs<CB>(a, t, lane, v0);
-        quantize_row_regs<BF16, CB>(a, bm, t, lane, v0);
+        quantize_row_regs<BF16, CB>(a, sk, bm, t, lane, v0);
       }
     } else if constexpr (CPL > 0) {
       for (int t = row0; t < T; t += 2 * W) {
         const int t1 = t + W;
         if (t1 < T) load_row_regs<CB>(a, t1, lane, v1);
-        quantize_row_regs<BF16, CB>(a, bm, t, lane, v0);
+        quantize_row_regs<BF16, CB>(a, sk, bm, t, lane, v0);
         if (t1 >= T) break;
         if (t1 + W < T) load_row_regs<CB>(a, t1 + W, lane, v0);
-        quantize_row_regs<BF16, CB>(a, bm, t1, lane, v1);
+        quantize_row_regs<BF16, CB>(a, sk, bm, t1, lane, v1);
       }
     } else {
       for (int t = row0; t < T; t += W) quantize_row_mem<BF16>(a, bm, t, lane);

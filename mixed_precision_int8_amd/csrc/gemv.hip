@@ -156,14 +156,16 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // issuing nor for their loads. X wavefront w copies the 1 KB pieces w,
   // w + 4, ... of X, which hold the chunks 64w + 256i of every row when
   // there is one row or K is a multiple of 2048 (the host picks XS then).
-  constexpr bool kXScan = XM != 0;   // the X wavefronts scan alone
-  constexpr bool kXQuant = XM == 1;  // ... and quantize alone (else all 8 wavefronts do, after barrier B)
-  // XM == 2: X is loaded into the X wavefronts' registers, each thread the
+  constexpr bool kXScan = XM != 0;               // the X wavefronts scan alone
+  constexpr bool kXQuant = XM == 1 || XM == 3;   // ... and quantize alone (else all 8 wavefronts do, after barrier B)
+  constexpr bool kXRegs = XM == 2 || XM == 3;    // X loaded into the X wavefronts' registers
+  // XM 2 and 3: X is loaded into the X wavefronts' registers, each thread the
   // kCpt chunks it scans, and written to LDS by them; the kernel then has no
   // copy into LDS in flight that the stream wavefronts' LDS reads would wait on
-  constexpr int kCpt = XM == 2 ? (TB <= 2 ? 4 : 4096 / (TB * 256)) : 1;
-  static_assert(XM != 2 || kCpt >= 1, "register-loaded X needs TB <= 16");
+  constexpr int kCpt = kXRegs ? (TB <= 2 ? 4 : 4096 / (TB * 256)) : 1;
+  static_assert(!kXRegs || kCpt >= 1, "register-loaded X needs TB <= 16");
   uint4 xr[kCpt][TB];
+  uint32_t xskip[kCpt];  // outlier flags of the thread's chunks (register-loaded X)
   constexpr int kScanWaves = kXScan ? 4 : 8;  // wavefronts that leave partial row maxima
 
   // stream wavefronts: their K range and the first batch of weight loads
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // Each scanning wavefront leaves its partial row maxima in rowred.
   // one chunk: its column maxima over the rows -> outlier bits into the
   // bitmap; the rows' maxima over its kept columns into rmax
-  auto scan_chunk = [&](int c, const uint4* v, v2u16* rmax) {
+  auto scan_chunk = [&](int c, const uint4* v, v2u16* rmax) -> uint32_t {
     const v2u16 hthr2 = {(uint16_t)hthr, (uint16_t)hthr};
     v2u16 ab[TB][4];
 #pragma unroll
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       for (int t = 1; t < TB; ++t) cm = pk_max(cm, ab[t][i]);
       keep[i] = keep_mask(cm, hthr2);
     }
-    if ((keep[0] & keep[1] & keep[2] & keep[3]) != 0xffffffffu)
-      atomicOr(&bm[c >> 2], outlier_bits(keep) << ((c & 3) * 8));
+    const uint32_t bits = outlier_bits(keep);
+    if (bits) atomicOr(&bm[c >> 2], bits << ((c & 3) * 8));
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       v2u16 m = rmax[t];
@@ -220,6 +222,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       for (int i = 0; i < 4; ++i) m = pk_max(m, as_u16x2(as_u32(ab[t][i]) & keep[i]));
       rmax[t] = m;
     }
+    return bits;
   };
   // fold the two halves, pack row pairs, reduce over the wavefront
   auto scan_finish = [&](const v2u16* rmax) {
@@ -249,9 +252,9 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
 
   // ---- 4. row scales from the scanning wavefronts' partial maxima, and the
   // int8 codes of the chunks first, first + stride, ...
-  auto quantize_chunks = [&](int first, int stride) {
-    // lane t (< T) of every calling wavefront combines the partial maxima of
-    // row t; the scales then go to scalar registers
+  // lane t (< T) of every calling wavefront combines the partial maxima of
+  // row t; the scales then go to scalar registers
+  auto row_scales = [&](float (&st)[TB]) {
     float srow = 0.0f;
     if (lane < T) {
       uint32_t m = 0u;
@@ -261,10 +264,13 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       srow = m ? 127.0f / ax : 0.0f;
       if (wave == 0) arow[lane] = ax;
     }
-    float st[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t)
       st[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, srow), t));
+  };
+  auto quantize_chunks = [&](int first, int stride) {
+    float st[TB];
+    row_scales(st);
     // int8 codes of this thread's chunks
     for (int c = first; c < KC; c += stride) {
       uint4 v[TB];
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     // the scales of the 16 weight rows (rows past N read as zero)
     const int xbytes = T * K * 2;
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X, (uint32_t)xbytes);
-    if constexpr (XM == 2) {
+    if constexpr (kXRegs) {
       // into registers, each thread the chunks it scans (rows past T and
       // chunks past the row read as zero); written to LDS below
 #pragma unroll
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       for (int c = xt; c < KC; c += 256)
         if ((c & 3) == 0) bm[c >> 2] = 0u;
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's part of X has landed
-      if constexpr (XM == 2) {
+      if constexpr (kXRegs) {
         v2u16 rmax[TB];
 #pragma unroll
         for (int t = 0; t < TB; ++t) rmax[t] = v2u16{0, 0};
@@ -398,16 +404,33 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
 #pragma unroll
             for (int t = 0; t < TB; ++t)
               if (t < T) *reinterpret_cast<uint4*>(lds + L.xs + (t * K + c * 8) * 2) = xr[i][t];
-            scan_chunk(c, xr[i], rmax);
+            xskip[i] = scan_chunk(c, xr[i], rmax);
           }
         }
         scan_finish(rmax);
       } else {
         scan_chunks(xt, 256);
       }
-      if constexpr (kXQuant) {
+      if constexpr (XM == 1) {
         x_sync();  // the 4 partial maxima and the whole bitmap are in LDS
         quantize_chunks(xt, 256);
+      }
+      if constexpr (XM == 3) {
+        // codes straight from the registers; a chunk's outlier flags are the
+        // scan's own (it saw every row of its columns)
+        x_sync();  // the 4 partial maxima are in LDS
+        float st[TB];
+        row_scales(st);
+#pragma unroll
+        for (int i = 0; i < kCpt; ++i) {
+          const int c = xt + 256 * i;
+          if (c < KC) {
+            const uint32_t m0 = expand4(~xskip[i] & 0xfu), m1 = expand4((~xskip[i] >> 4) & 0xfu);
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+              if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(xr[i][t], st[t], m0, m1);
+          }
+        }
       }
     } else {
       for (int w = xt; w < KW; w += 256) bm[w] = 0u;
@@ -592,20 +615,21 @@ static hipError_t launch_gemv_tb(const LinearArgs& a, hipStream_t stream) {
 
 template <bool BF16>
 static hipError_t launch_gemv_dt(const LinearArgs& a, hipStream_t stream) {
-  // XM 1: the X wavefronts scan and quantize alone, when their copies hold
-  // whole chunk columns (measured best up to 4 rows); XM 2: X in their
-  // registers (a thread holds kCpt chunks of TB rows), they scan alone and all
-  // 8 wavefronts quantize (best at 8 rows); XM 0: all 8 scan and quantize
+  // XM 3: X in the X wavefronts' registers (a thread holds kCpt chunks of TB
+  // rows), they scan and quantize alone from the registers (up to 8 rows);
+  // XM 2: the same loads, the X wavefronts scan and all 8 quantize (16 rows);
+  // XM 1: X copied into LDS, the X wavefronts scan and quantize alone, when
+  // their copies hold whole chunk columns; XM 0: all 8 scan and quantize
   const bool xs = a.K % 2048 == 0;
-  if (a.T <= 1) return launch_gemv_tb<1, BF16, 1>(a, stream);
+  if (a.T <= 1) return a.K <= 8192 ? launch_gemv_tb<1, BF16, 3>(a, stream) : launch_gemv_tb<1, BF16, 1>(a, stream);
   if (a.T <= 2)
-    return xs ? launch_gemv_tb<2, BF16, 1>(a, stream)
-              : a.K <= 8192 ? launch_gemv_tb<2, BF16, 2>(a, stream) : launch_gemv_tb<2, BF16, 0>(a, stream);
+    return a.K <= 8192 ? launch_gemv_tb<2, BF16, 3>(a, stream)
+                       : xs ? launch_gemv_tb<2, BF16, 1>(a, stream) : launch_gemv_tb<2, BF16, 0>(a, stream);
   if (a.T <= 4)
-    return xs ? launch_gemv_tb<4, BF16, 1>(a, stream)
-              : a.K <= 8192 ? launch_gemv_tb<4, BF16, 2>(a, stream) : launch_gemv_tb<4, BF16, 0>(a, stream);
+    return a.K <= 8192 ? launch_gemv_tb<4, BF16, 3>(a, stream)
+                       : xs ? launch_gemv_tb<4, BF16, 1>(a, stream) : launch_gemv_tb<4, BF16, 0>(a, stream);
   if (a.T <= 8)
-    return a.K <= 4096 ? launch_gemv_tb<8, BF16, 2>(a, stream)
+    return a.K <= 4096 ? launch_gemv_tb<8, BF16, 3>(a, stream)
                        : xs ? launch_gemv_tb<8, BF16, 1>(a, stream) : launch_gemv_tb<8, BF16, 0>(a, stream);
   return a.K <= 2048 ? launch_gemv_tb<16, BF16, 2>(a, stream)
                      : xs ? launch_gemv_tb<16, BF16, 1>(a, stream) : launch_gemv_tb<16, BF16, 0>(a, stream);

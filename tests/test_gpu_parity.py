@@ -217,13 +217,16 @@ def test_many_outlier_chunks():
 
 
 @pytest.mark.parametrize("T,K,n_out", [(3, 8192, 45), (8, 4096, 32), (1, 14336, 33), (12, 4096, 40),
-                                       (16, 2048, 20), (6, 2064, 9)])
+                                       (16, 2048, 20), (6, 2064, 9), (11, 3056, 14), (2, 10000, 36),
+                                       (4, 10016, 7)])
 def test_gemv_outlier_bytes_across_k_ranges(T, K, n_out):
     """Decode kernel: outlier columns spread over each of the four K
     quarters and every register batch (two at K = 8192, four at 14336), more
-    than one 32-column chunk of them, ragged N; rows up to 16, with K a
-    multiple of 2048 (the X wavefronts scan and quantize alone) and not
-    (2064). Bit-exact stages and Y within the bar."""
+    than one 32-column chunk of them, ragged N; every form of the X work:
+    X held in registers (up to 8 rows and K <= 8192, 4096 at 8 rows; 16 rows
+    with K <= 2048), X copied to LDS and worked by the X wavefronts alone
+    (K a multiple of 2048 past those sizes), and by all 8 wavefronts (3056,
+    10000, 10016). Bit-exact stages and Y within the bar."""
     W, X = _small(T, K, 300, seed=K + n_out, n_out=n_out)
     _, c = run_case(f"gemv outliers over K ranges K={K}", W, X, 6.0, GEMV)
     assert c >= n_out

@@ -246,11 +246,29 @@ template <bool BF16, int CPL>
 __device__ __forceinline__ void quantize_row_regs(const LinearArgs& a, const uint32_t (&sk)[(CPL + 3) / 4],
                                                   const uint32_t* bm, int t, int lane, const uint4 (&v)[CPL]) {
   const int K = a.K, KC = K >> 3, cpl = (KC + 63) >> 6;
+  // past 8 chunks the masks come from LDS, four chunks' words per round trip
+  constexpr int GM = CPL <= 8 ? 1 : 4;
+  auto masks = [&](int u0, uint32_t (&mk)[GM]) {
+    if constexpr (CPL <= 8) {
+      mk[0] = skip_of<CPL>(sk, bm, lane, u0);
+    } else {
+      uint32_t w[GM];
+#pragma unroll
+      for (int i = 0; i < GM; ++i) w[i] = lane + 64 * (u0 + i) < KC ? bm[(lane >> 2) + 16 * (u0 + i)] : 0u;
+#pragma unroll
+      for (int i = 0; i < GM; ++i) mk[i] = (w[i] >> ((lane & 3) * 8)) & 0xffu;
+    }
+  };
   uint32_t m = 0u;
 #pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    const int c = lane + 64 * u;
-    if (u < cpl && c < KC) m = max(m, chunk_kept_max(v[u], skip_of<CPL>(sk, bm, lane, u)));
+  for (int u0 = 0; u0 < CPL; u0 += GM) {
+    uint32_t mk[GM];
+    masks(u0, mk);
+#pragma unroll
+    for (int i = 0; i < GM; ++i) {
+      const int u = u0 + i, c = lane + 64 * u;
+      if (u < cpl && c < KC) m = max(m, chunk_kept_max(v[u], mk[i]));
+    }
   }
   m = wave_max_u16x2(m) & 0xffffu;
   const float ax = Act16<BF16>::to_f32(m);
@@ -265,11 +283,16 @@ __device__ __forceinline__ void quantize_row_regs(const LinearArgs& a, const uin
   for (int u0 = 0; u0 < CPL; u0 += G) {
     uint2 q[G];
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int u = u0 + i, c = lane + 64 * u;
-      if (u < cpl && c < KC) {
-        const uint32_t skip = skip_of<CPL>(sk, bm, lane, u);
-        q[i] = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+    for (int i0 = 0; i0 < G; i0 += GM) {
+      uint32_t mk[GM];
+      masks(u0 + i0, mk);
+#pragma unroll
+      for (int i = i0; i < i0 + GM; ++i) {
+        const int u = u0 + i, c = lane + 64 * u;
+        if (u < cpl && c < KC) {
+          const uint32_t skip = mk[i - i0];
+          q[i] = Act16<BF16>::quantize8(v[u], s, expand4(~skip & 0xfu), expand4((~skip >> 4) & 0xfu));
+        }
       }
     }
 #pragma unroll

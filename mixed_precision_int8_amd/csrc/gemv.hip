@@ -174,19 +174,34 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   const int kend = min(K, kbeg + kq);
   const int steps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   const int nbatch = (steps + kGemvBatch - 1) / kGemvBatch;
-  // Whole 128-byte lines per load instruction: for the step pair (2p, 2p+1)
+  // Whole lines (TB <= 2): 128 contiguous bytes per row per load; for the step pair (2p, 2p+1)
   // load w[2p] covers rows 0-7 and w[2p+1] rows 8-15, each row's 128 bytes
   // by 8 lanes. Lane (fg, fi) takes row fi & 7 (+ 8), bytes 16 * (fg + 4 *
   // (fi >> 3)) of the pair: lanes fi < 8 hold the first 64 bytes of their
   // row, lanes fi >= 8 the second 64 bytes of row fi - 8 (+ 8).
+  // Up to 2 rows, where the weights landing is the critical path, a load covers
+  // whole lines and each fragment takes two MFMAs (above). From 4 rows on the
+  // product starts after the X work, when the weights have landed, and the
+  // doubled MFMAs would be on the critical path (about 2000 instead of 1000
+  // cycles per wavefront): lane (fg, fi) then loads row fi, bytes 16 fg of
+  // the 64-byte step, one MFMA per fragment.
+  constexpr bool kWholeLine = TB <= 2;
   auto load_batch = [&](v4i* w, int b) {
-    const uint32_t r0 = (uint32_t)((fi & 7) * K), r1 = (uint32_t)((8 + (fi & 7)) * K);
+    if constexpr (kWholeLine) {
+      const uint32_t r0 = (uint32_t)((fi & 7) * K), r1 = (uint32_t)((8 + (fi & 7)) * K);
 #pragma unroll
-    for (int p = 0; p < kGemvBatch / 2; ++p) {
-      const int k = kbeg + (b * kGemvBatch + 2 * p) * 64 + fg * 16 + (fi >> 3) * 64;
-      const bool in = k < kend;
-      w[2 * p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, in ? r0 + (uint32_t)k : kOobOffset, 0, 0));
-      w[2 * p + 1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, in ? r1 + (uint32_t)k : kOobOffset, 0, 0));
+      for (int p = 0; p < kGemvBatch / 2; ++p) {
+        const int k = kbeg + (b * kGemvBatch + 2 * p) * 64 + fg * 16 + (fi >> 3) * 64;
+        const bool in = k < kend;
+        w[2 * p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, in ? r0 + (uint32_t)k : kOobOffset, 0, 0));
+        w[2 * p + 1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, in ? r1 + (uint32_t)k : kOobOffset, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kGemvBatch; ++s) {
+        const int k = kbeg + (b * kGemvBatch + s) * 64 + fg * 16;
+        w[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rW, k < kend ? rowoff + (uint32_t)k : kOobOffset, 0, 0));
+      }
     }
   };
   // ---- 3. the scan: a thread takes 8-column chunks across all rows: column
@@ -481,12 +496,18 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       // rows 8-15 (weight rows 0-7, second halves), acc4[2] rows 0-7 (weight
       // rows 8-15, first halves), acc4[3] rows 8-15 (weight rows 8-15,
       // second halves); the other rows are discarded.
+      if constexpr (kWholeLine) {
 #pragma unroll
-      for (int p = 0; p < kGemvBatch / 2; ++p) {
-        acc4[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p], xf[2 * p], acc4[0], 0, 0, 0);
-        acc4[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p], xf[2 * p + 1], acc4[1], 0, 0, 0);
-        acc4[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p + 1], xf[2 * p], acc4[2], 0, 0, 0);
-        acc4[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p + 1], xf[2 * p + 1], acc4[3], 0, 0, 0);
+        for (int p = 0; p < kGemvBatch / 2; ++p) {
+          acc4[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p], xf[2 * p], acc4[0], 0, 0, 0);
+          acc4[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p], xf[2 * p + 1], acc4[1], 0, 0, 0);
+          acc4[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p + 1], xf[2 * p], acc4[2], 0, 0, 0);
+          acc4[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[2 * p + 1], xf[2 * p + 1], acc4[3], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kGemvBatch; ++s)
+          acc4[s & 3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[s], xf[s], acc4[s & 3], 0, 0, 0);
       }
     };
     for (int b = 0; b < nbatch; b += 2) {
@@ -500,11 +521,15 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     // Output lane (fg, fi) holds rows 4 fg .. 4 fg + 3: lanes fg < 2 (rows
     // 0-7) add acc4[1] of the lane 32 above, lanes fg >= 2 (rows 8-15)
     // acc4[2] of the lane 32 below. Exact int32 sums.
-    const v4i own = fg < 2 ? acc4[0] : acc4[3], give = fg < 2 ? acc4[2] : acc4[1];
-    v4i other;
+    if constexpr (kWholeLine) {
+      const v4i own = fg < 2 ? acc4[0] : acc4[3], give = fg < 2 ? acc4[2] : acc4[1];
+      v4i other;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) other[v] = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, give[v]);
-    red[ww * 64 + lane] = own + other;
+      for (int v = 0; v < 4; ++v) other[v] = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, give[v]);
+      red[ww * 64 + lane] = own + other;
+    } else {
+      red[ww * 64 + lane] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    }
   }
   // X wavefront 0, while the stream wavefronts multiply: the outlier indices,
   // then the 16-bit outlier product, which needs only X and the gathered

@@ -121,6 +121,27 @@ __device__ __forceinline__ uint32_t outlier_bits(const uint32_t keep[4]) {
   return bits;
 }
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
+// Packed-u16 maxima over the wavefront of NV independent values, one DPP step
+// for all of them before the next, so that the chains overlap instead of
+// waiting out each other's latencies; the totals end in lane 63.
+template <int NV>
+__device__ __forceinline__ void wave_max_u16x2_n(uint32_t (&v)[NV]) {
+  auto step = [&](auto ctrl, auto row_mask) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v[i], (int)v[i], decltype(ctrl)::value,
+                                                               decltype(row_mask)::value, 0xF, false);
+      v[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, v[i]),
+                                                                    __builtin_bit_cast(v2u16, o)));
+    }
+  };
+  step(std::integral_constant<int, 0xB1>{}, std::integral_constant<int, 0xF>{});   // quad_perm [1,0,3,2]
+  step(std::integral_constant<int, 0x4E>{}, std::integral_constant<int, 0xF>{});   // quad_perm [2,3,0,1]
+  step(std::integral_constant<int, 0x141>{}, std::integral_constant<int, 0xF>{});  // row_half_mirror
+  step(std::integral_constant<int, 0x140>{}, std::integral_constant<int, 0xF>{});  // row_mirror
+  step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast:15
+  step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});  // row_bcast:31
+}
 __device__ __forceinline__ uint32_t as_u32(v2u16 x) { return __builtin_bit_cast(uint32_t, x); }
 
 template <int TB, bool BF16, int XM>
@@ -240,16 +261,19 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     return bits;
   };
   // fold the two halves, pack row pairs, reduce over the wavefront
+  // (rows past T hold zeros, so every pair is reduced and only live ones stored)
   auto scan_finish = [&](const v2u16* rmax) {
+    uint32_t r[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      if (2 * p < T) {
-        const uint32_t lo = max(rmax[2 * p].x, rmax[2 * p].y);
-        const uint32_t hi = 2 * p + 1 < TB ? max(rmax[2 * p + 1].x, rmax[2 * p + 1].y) : 0u;
-        const uint32_t r = wave_max_u16x2(lo | (hi << 16));
-        if (lane == 0) rowred[wave * 8 + p] = r;
-      }
+      const uint32_t lo = max(rmax[2 * p].x, rmax[2 * p].y);
+      const uint32_t hi = 2 * p + 1 < TB ? max(rmax[2 * p + 1].x, rmax[2 * p + 1].y) : 0u;
+      r[p] = lo | (hi << 16);
     }
+    wave_max_u16x2_n<NP>(r);
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (2 * p < T && lane == 63) rowred[wave * 8 + p] = r[p];
   };
   auto scan_chunks = [&](int first, int stride) {
     v2u16 rmax[TB];
@@ -309,6 +333,32 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
 #pragma unroll
       for (int t = 0; t < TB; ++t)
         if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(v[t], st[t], m0, m1);
+    }
+  };
+
+  // The same codes, one (row, chunk) item per thread and step, for the form
+  // where every row is quantized by all 8 wavefronts: with few chunks per row,
+  // splitting by chunk alone would leave most threads without work and the
+  // rest with all rows. Each thread takes its row's scale from the partial
+  // maxima itself (the same expression as row_scales, so the same value).
+  auto quantize_items = [&](int first, int stride) {
+    for (int i = first; i < T * KC; i += stride) {
+      const int t = i / KC, c = i - t * KC;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int w = 0; w < kScanWaves; ++w) m = max(m, (rowred[w * 8 + (t >> 1)] >> ((t & 1) * 16)) & 0xffffu);
+      const float ax = A16::to_f32(m);
+      const float st = m ? 127.0f / ax : 0.0f;
+      const uint4 v = *reinterpret_cast<const uint4*>(xs + t * K + c * 8);
+      const uint32_t skip = (bm[c >> 2] >> ((c & 3) * 8)) & 0xffu;
+      const uint32_t m0 = expand4(~skip & 0xfu), m1 = expand4((~skip >> 4) & 0xfu);
+      *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(v, st, m0, m1);
+    }
+    if (wave == 0 && lane < T) {  // the row statistic for the epilogue
+      uint32_t m = 0u;
+#pragma unroll
+      for (int w = 0; w < kScanWaves; ++w) m = max(m, (rowred[w * 8 + (lane >> 1)] >> ((lane & 1) * 16)) & 0xffffu);
+      arow[lane] = A16::to_f32(m);
     }
   };
 
@@ -465,7 +515,8 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   }
   if constexpr (!kXQuant) {
     lds_barrier();  // B: bitmap and partial row maxima complete
-    quantize_chunks(tid, 512);
+    if constexpr (XM == 2) quantize_items(tid, 512);
+    else quantize_chunks(tid, 512);
   }
   lds_barrier();  // C: int8 rows of X and the row statistics are ready
 

@@ -121,19 +121,19 @@ __device__ __forceinline__ uint32_t outlier_bits(const uint32_t keep[4]) {
   return bits;
 }
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
-// Packed-u16 maxima over the wavefront of NV independent values, one DPP step
+__device__ __forceinline__ uint32_t as_u32(v2u16 x) { return __builtin_bit_cast(uint32_t, x); }
+// Maxima over the wavefront of NV independent unsigned values, one DPP step
 // for all of them before the next, so that the chains overlap instead of
-// waiting out each other's latencies; the totals end in lane 63.
+// waiting out each other's latencies; the totals end in lane 63. Lanes that a
+// step leaves without a source take 0, the identity of the maximum, so each
+// step can be one v_max_u32 with a DPP operand.
 template <int NV>
-__device__ __forceinline__ void wave_max_u16x2_n(uint32_t (&v)[NV]) {
+__device__ __forceinline__ void wave_max_u32_n(uint32_t (&v)[NV]) {
   auto step = [&](auto ctrl, auto row_mask) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v[i], (int)v[i], decltype(ctrl)::value,
-                                                               decltype(row_mask)::value, 0xF, false);
-      v[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, v[i]),
-                                                                    __builtin_bit_cast(v2u16, o)));
-    }
+    for (int i = 0; i < NV; ++i)
+      v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], decltype(ctrl)::value,
+                                                              decltype(row_mask)::value, 0xF, false));
   };
   step(std::integral_constant<int, 0xB1>{}, std::integral_constant<int, 0xF>{});   // quad_perm [1,0,3,2]
   step(std::integral_constant<int, 0x4E>{}, std::integral_constant<int, 0xF>{});   // quad_perm [2,3,0,1]
@@ -142,7 +142,6 @@ __device__ __forceinline__ void wave_max_u16x2_n(uint32_t (&v)[NV]) {
   step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast:15
   step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});  // row_bcast:31
 }
-__device__ __forceinline__ uint32_t as_u32(v2u16 x) { return __builtin_bit_cast(uint32_t, x); }
 
 template <int TB, bool BF16, int XM>
 __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, int kq) {
@@ -263,17 +262,13 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // fold the two halves, pack row pairs, reduce over the wavefront
   // (rows past T hold zeros, so every pair is reduced and only live ones stored)
   auto scan_finish = [&](const v2u16* rmax) {
-    uint32_t r[NP];
+    uint32_t r[TB];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const uint32_t lo = max(rmax[2 * p].x, rmax[2 * p].y);
-      const uint32_t hi = 2 * p + 1 < TB ? max(rmax[2 * p + 1].x, rmax[2 * p + 1].y) : 0u;
-      r[p] = lo | (hi << 16);
-    }
-    wave_max_u16x2_n<NP>(r);
+    for (int t = 0; t < TB; ++t) r[t] = max(rmax[t].x, rmax[t].y);
+    wave_max_u32_n<TB>(r);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      if (2 * p < T && lane == 63) rowred[wave * 8 + p] = r[p];
+      if (2 * p < T && lane == 63) rowred[wave * 8 + p] = r[2 * p] | (2 * p + 1 < TB ? r[2 * p + 1] << 16 : 0u);
   };
   auto scan_chunks = [&](int first, int stride) {
     v2u16 rmax[TB];

@@ -114,6 +114,15 @@ def test_ragged_rows(T):
         run_case(f"ragged T={T}", W, X, 6.0, path, check_auto=True)
 
 
+@pytest.mark.parametrize("T,K,N", [(11, 1040, 70), (16, 2032, 33), (13, 16, 9), (15, 528, 100), (9, 2048, 48)])
+def test_sixteen_row_form_ragged(T, K, N):
+    """The fused kernel's 16-row form (K up to 2048) hands out one (row,
+    chunk) item per thread: row counts and chunk counts that do not divide
+    the 512 threads, and one row group of 16 rows."""
+    W, X = _small(T, K, N, seed=7 * T + K, n_out=4)
+    run_case(f"16-row form T={T} K={K} N={N}", W, X, 6.0, GEMV)
+
+
 @pytest.mark.parametrize("K,N", [(16, 1), (48, 3), (1040, 17), (4112, 250), (272, 1000), (8192, 64)])
 def test_ragged_k_and_n(K, N):
     W, X = _small(37, K, N, seed=K + N)

@@ -206,6 +206,11 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // cycles per wavefront): lane (fg, fi) then loads row fi, bytes 16 fg of
   // the 64-byte step, one MFMA per fragment.
   constexpr bool kWholeLine = TB <= 2;
+  // the outlier indices compacted by a stream wavefront before barrier C (the
+  // form whose X wavefronts meet at the LDS counter and quantize alone), from
+  // 4 rows on: with fewer rows the X work ends early and the compaction would
+  // hold barrier C back instead
+  constexpr bool kEarlyIdx = XM == 3 && TB >= 4;
   auto load_batch = [&](v4i* w, int b) {
     if constexpr (kWholeLine) {
       const uint32_t r0 = (uint32_t)((fi & 7) * K), r1 = (uint32_t)((8 + (fi & 7)) * K);
@@ -501,6 +506,23 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     // the X wavefronts work (issuing them stalls only these wavefronts)
     if constexpr (kXScan) lds_barrier();  // E
     load_batch(w0, 0);  // out-of-range steps read as zero
+    if constexpr (kEarlyIdx) {
+      // The first stream wavefront, idle until its weights land, compacts the
+      // outlier indices once the X wavefronts' scan is complete (the counter
+      // reaches 4 after their bitmap updates), so that after barrier C
+      // wavefront 0 starts straight at the gather. The wait reads the LDS
+      // counter without ordering against memory: the wavefront's weight loads
+      // stay in flight. It is bounded, so it always ends.
+      if (wave == 4) {
+        const __attribute__((address_space(3))) int* ctr = (const __attribute__((address_space(3))) int*)xctr;
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        compact();
+      }
+    }
   }
   if constexpr (!kXScan) {
     lds_barrier();  // A: X is in LDS, the bitmap is clear
@@ -583,7 +605,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   const int t = fi;
   v4f yo = {0.f, 0.f, 0.f, 0.f};
   const float at = wave == 0 && t < T ? arow[t] : 0.0f;  // row statistic for the epilogue, read early
-  const int count0 = wave == 0 ? compact() : 0;
+  const int count0 = wave != 0 ? 0 : kEarlyIdx ? __builtin_amdgcn_readfirstlane(*cnt) : compact();
   if (count0) {
     const int count = count0;
     const uint16_t* xr = xs + min(t, T - 1) * K;

@@ -210,7 +210,11 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   // form whose X wavefronts meet at the LDS counter and quantize alone), from
   // 4 rows on: with fewer rows the X work ends early and the compaction would
   // hold barrier C back instead
-  constexpr bool kEarlyIdx = XM == 3 && TB >= 4;
+  constexpr bool kIdxByStream = XM == 3 && TB >= 4;
+  // in the 16-row form X wavefront 3 compacts them after barrier B, before its
+  // share of the quantization (it has the least scanning to do)
+  constexpr bool kIdxByX3 = XM == 2;
+  constexpr bool kEarlyIdx = kIdxByStream || kIdxByX3;
   auto load_batch = [&](v4i* w, int b) {
     if constexpr (kWholeLine) {
       const uint32_t r0 = (uint32_t)((fi & 7) * K), r1 = (uint32_t)((8 + (fi & 7)) * K);
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     // the X wavefronts work (issuing them stalls only these wavefronts)
     if constexpr (kXScan) lds_barrier();  // E
     load_batch(w0, 0);  // out-of-range steps read as zero
-    if constexpr (kEarlyIdx) {
+    if constexpr (kIdxByStream) {
       // The first stream wavefront, idle until its weights land, compacts the
       // outlier indices once the X wavefronts' scan is complete (the counter
       // reaches 4 after their bitmap updates), so that after barrier C
@@ -532,8 +536,12 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   }
   if constexpr (!kXQuant) {
     lds_barrier();  // B: bitmap and partial row maxima complete
-    if constexpr (XM == 2) quantize_items(tid, 512);
-    else quantize_chunks(tid, 512);
+    if constexpr (XM == 2) {
+      if (wave == 3) compact();  // the bitmap is complete at B
+      quantize_items(tid, 512);
+    } else {
+      quantize_chunks(tid, 512);
+    }
   }
   lds_barrier();  // C: int8 rows of X and the row statistics are ready
 

@@ -366,9 +366,10 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
     }
   };
 
-  // ---- 5b. wavefront 0: the outlier indices, ascending, compacted from the
-  // bitmap (the int8 product does not need them, so this runs after barrier
-  // C, beside the stream wavefronts' products); returns their count
+  // ---- 5b. the outlier indices, ascending, compacted from the bitmap by one
+  // wavefront; returns their count. The int8 product does not need them:
+  // wavefront 0 compacts them after barrier C, beside the stream wavefronts'
+  // products, unless a wavefront with slack has done so before C (kEarlyIdx).
   auto compact = [&]() -> int {
     const int per = (KW + 63) / 64;
     const int w0i = min(KW, lane * per), w1i = min(KW, w0i + per);
@@ -514,9 +515,12 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       // The first stream wavefront, idle until its weights land, compacts the
       // outlier indices once the X wavefronts' scan is complete (the counter
       // reaches 4 after their bitmap updates), so that after barrier C
-      // wavefront 0 starts straight at the gather. The wait reads the LDS
-      // counter without ordering against memory: the wavefront's weight loads
-      // stay in flight. It is bounded, so it always ends.
+      // wavefront 0 starts straight at the gather. The wait is a relaxed read
+      // of the LDS counter, with no ordering against memory, so the
+      // wavefront's weight loads stay in flight. That suffices here: the X
+      // wavefronts raise the counter only once their bitmap updates have
+      // completed, and this wavefront's LDS reads of the bitmap issue after
+      // the counter read has returned. The wait is bounded, so it always ends.
       if (wave == 4) {
         const __attribute__((address_space(3))) int* ctr = (const __attribute__((address_space(3))) int*)xctr;
         for (int spin = 0; spin < (1 << 22); ++spin) {

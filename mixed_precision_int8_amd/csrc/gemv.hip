@@ -336,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
       const uint32_t m0 = expand4(~skip & 0xfu), m1 = expand4((~skip >> 4) & 0xfu);
 #pragma unroll
       for (int t = 0; t < TB; ++t)
-        if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(v[t], st[t], m0, m1);
+        if (__builtin_expect(t < T, 1)) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(v[t], st[t], m0, m1);
     }
   };
 
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
           if (c < KC) {
 #pragma unroll
             for (int t = 0; t < TB; ++t)
-              if (t < T) *reinterpret_cast<uint4*>(lds + L.xs + (t * K + c * 8) * 2) = xr[i][t];
+              if (__builtin_expect(t < T, 1)) *reinterpret_cast<uint4*>(lds + L.xs + (t * K + c * 8) * 2) = xr[i][t];
             xskip[i] = scan_chunk(c, xr[i], rmax);
           }
         }
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
             const uint32_t m0 = expand4(~xskip[i] & 0xfu), m1 = expand4((~xskip[i] >> 4) & 0xfu);
 #pragma unroll
             for (int t = 0; t < TB; ++t)
-              if (t < T) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(xr[i][t], st[t], m0, m1);
+              if (__builtin_expect(t < T, 1)) *reinterpret_cast<uint2*>(xq + t * L.kp + c * 8) = A16::quantize8(xr[i][t], st[t], m0, m1);
           }
         }
       }

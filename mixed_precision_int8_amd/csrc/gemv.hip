@@ -683,7 +683,14 @@ __global__ __launch_bounds__(512, 1) void kd_gemv(LinearArgs a, uint32_t hthr, i
   for (int v = 0; v < 4; ++v) y[v] = (float)acc[v] * (at * (bs4[v] * (1.0f / 16129.0f))) + yo[v];
   if (a.bias) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) y[v] += A16::to_f32(bias4[v]);
+    for (int v = 0; v < 4; ++v) {
+      // An empty asm that may change the bias bits keeps their conversion
+      // here. Moved up to the loads, it would wait there, and with the copies
+      // of X issued before the bias, that wait holds the entry barrier.
+      uint32_t b = bias4[v];
+      asm volatile("" : "+v"(b));
+      y[v] += A16::to_f32(b);
+    }
   }
   if (t < T) {
     uint16_t* dst = a.Y + (size_t)t * N + n;
